@@ -1,0 +1,87 @@
+"""The P-cast pages' qualitative results, reproduced by the oracle on synthetic inputs.
+
+Setting: the Sweep shape (causal, d = 128, Q/K/V i.i.d. N(0,1) in bf16, sink
+bias Delta on keys 0..3), with fewer heads so the CPU finishes in seconds.
+"pages" mode keeps V exact and casts only P, which is the summary's
+kernel-faithful simulation.  MSE is the mean over all output elements of
+(O2 - O1)^2 against exact attention.
+
+What is checked is the direction and ordering the pages report.  The size of
+the fwd S=1 penalty on this zero-mean-V workload (about 2x at N = 4096,
+growing with N) is below the pages' 3-10x; the pages do not state the
+simulation's head size, value distribution or MSE normalisation, so absolute
+ratios stay unpinned.
+"""
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import core
+
+N, D, H = 4096, 128, 2
+
+
+@pytest.fixture(scope="module")
+def sweep_inputs():
+    return synthetic.qkv_bf16(1, H, H, N, D, 2)
+
+
+def _run(inp, delta, S, order, mode="pages", n=N):
+    q, k, v = inp
+    r = core.rows(q, k, v, synthetic.sink_bias(n, delta), True, S, order, mode)
+    r["mse"] = float(np.mean((r["o2"] - r["o1"]) ** 2))
+    r["underflow"] = r["zero"].sum() / r["total"].sum()
+    return r
+
+
+@pytest.mark.slow
+def test_forward_s1_is_worst_at_delta7(sweep_inputs):
+    base = _run(sweep_inputs, 7.0, 1.0, 0)
+    for S, order in ((1.0, 1), (256.0, 0), (256.0, 1)):
+        other = _run(sweep_inputs, 7.0, S, order)
+        assert base["mse"] / other["mse"] > 1.5
+
+
+@pytest.mark.slow
+def test_s256_beats_s448_forward(sweep_inputs):
+    for delta in (5.0, 7.0):
+        a = _run(sweep_inputs, delta, 256.0, 0)["mse"]
+        b = _run(sweep_inputs, delta, 448.0, 0)["mse"]
+        assert a < b
+
+
+@pytest.mark.slow
+def test_reverse_and_s256_together_add_nothing(sweep_inputs):
+    a = _run(sweep_inputs, 7.0, 256.0, 0)["mse"]
+    b = _run(sweep_inputs, 7.0, 256.0, 1)["mse"]
+    assert abs(a - b) / a < 0.02
+
+
+@pytest.mark.slow
+def test_gain_grows_with_sequence_length():
+    ratios = []
+    for n in (1024, 2048, 4096):
+        inp = synthetic.qkv_bf16(1, 1, 1, n, D, 2)
+        r1 = _run(inp, 7.0, 1.0, 0, n=n)["mse"]
+        r2 = _run(inp, 7.0, 256.0, 1, n=n)["mse"]
+        ratios.append(r1 / r2)
+    assert ratios[0] < ratios[1] < ratios[2]
+
+
+@pytest.mark.slow
+def test_collapse_crosses_half_between_5_and_6(sweep_inputs):
+    assert _run(sweep_inputs, 5.0, 1.0, 0)["underflow"] < 0.5 < _run(sweep_inputs, 6.0, 1.0, 0)["underflow"]
+
+
+@pytest.mark.slow
+def test_scale_512_saturates(sweep_inputs):
+    assert _run(sweep_inputs, 7.0, 512.0, 0)["mse"] > 5 * _run(sweep_inputs, 7.0, 256.0, 0)["mse"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("delta", [5.0, 7.0, 9.0])
+def test_reverse_256_no_underflow_beyond_sink_block(sweep_inputs, delta):
+    r = _run(sweep_inputs, delta, 256.0, 1, mode="kernel")
+    assert r["zero_beyond_block0"].sum() == 0
+    f = _run(sweep_inputs, delta, 1.0, 0, mode="kernel")
+    assert f["zero_beyond_block0"].sum() > 0
