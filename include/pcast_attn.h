@@ -1,0 +1,108 @@
+/*
+ * pcast_attn.h -- C ABI of the FP8 "P-cast" attention forward for AMD MI355X (gfx950).
+ *
+ * The operation (FlashAttention blog by marketmaker.cc, sections "Perché
+ * l'attenzione è legata alla memoria", "L'algoritmo Flash Attention" and
+ * "La ricorrenza softmax online"; P-cast summaries on gist.science, sections
+ * 1 and 2):
+ *
+ *   O = softmax(Q K^T / sqrt(d) + bias) V
+ *
+ * computed tile by tile with online softmax over key blocks of
+ * PCAST_KV_BLOCK keys.  For each query row, a running max m (including the
+ * current block) and a running sum l of the un-cast probabilities are kept;
+ * the probability tile P is multiplied by the static scale S, rounded to FP8
+ * E4M3 (OCP e4m3fn, round to nearest even, saturating at 448) and multiplied
+ * with V rounded to E4M3 on the FP8 matrix cores; the accumulator is divided
+ * by S*l at the end.  Key blocks are visited 0 -> last (forward) or last -> 0
+ * (reverse), the two iteration orders the P-cast summary compares
+ * ("Ottimizzazione 1").  S = 0 selects the reference path with P and V in
+ * bf16 instead of E4M3 (no P-cast).
+ *
+ * All entry points are plain C, take device pointers, never allocate memory
+ * that outlives the call, never fall back to another implementation, and
+ * report errors through their return code.
+ */
+#ifndef PCAST_ATTN_H
+#define PCAST_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PCAST_ABI_VERSION 1
+
+/* Keys per KV block.  The block size is part of the numerics (the running
+ * max is updated once per block), so it is fixed. */
+#define PCAST_KV_BLOCK 64
+
+#define PCAST_ORDER_FORWARD 0
+#define PCAST_ORDER_REVERSE 1
+
+/* Return codes. */
+#define PCAST_OK 0
+#define PCAST_EINVAL 1  /* bad pointer, shape, scalar or alignment; nothing was enqueued */
+#define PCAST_ENOTSUP 2 /* device is not gfx950, or d / N outside the supported set    */
+#define PCAST_EHIP 3    /* HIP runtime or launch error; see pcast_strerror(code)        */
+
+/*
+ * attn_fwd_pcast -- enqueue one attention forward on `stream`.
+ *
+ * Q      device, bf16 bits, [B][Hq][N][d] row-major, contiguous, 16-byte aligned.
+ * K, V   device, bf16 bits, [B][Hkv][N][d] row-major, contiguous, 16-byte aligned.
+ * bias   device, float32 [N], additive logit bias per key (natural-log units),
+ *        or NULL for none.  Keys with bias != 0 are "sink" keys; every other
+ *        key is "non-sink" (all keys when bias is NULL).
+ * B, Hq, Hkv  batch and head counts, Hq % Hkv == 0; query head h reads key/value
+ *        head h / (Hq / Hkv).
+ * N      sequence length (queries and keys), N >= 1 and N % 64 == 0.
+ * d      head size, 64 or 128.
+ * causal 0 = every key visible; 1 = key j visible to query i iff j <= i.
+ * S      > 0 and finite: P-cast scale (powers of two are exact in fp32; values
+ *        above 448 saturate the largest probabilities).  0: bf16 reference path.
+ * order  PCAST_ORDER_FORWARD or PCAST_ORDER_REVERSE.
+ * out    device, float32 [B][Hq][N][d], written completely.
+ * stats  device, uint64 [pcast_stats_words(B, Hq, N)], or NULL for no
+ *        counting.  For query rows [64r, 64r + 64) of (batch b, head h), word
+ *        2*((b*Hq + h)*(N/64) + r) receives the number of unmasked non-sink
+ *        (query, key) pairs evaluated, and the next word the number of those
+ *        whose E4M3 code of P*S is zero (underflow).  Words are overwritten,
+ *        not accumulated.  In the bf16 path the second word counts P values
+ *        that round to zero in bf16.
+ * stream hipStream_t, or NULL for the default stream.
+ *
+ * Ownership: the caller owns every buffer; the library keeps no pointer after
+ * returning.  Temporary device memory -- a copy of V in E4M3 (or bf16 for
+ * S = 0) laid out in the matrix-core operand order, B*Hkv*N*d bytes (twice
+ * that for bf16), plus one flag per key block -- is taken from HIP's
+ * stream-ordered allocator on `stream` and released on the same stream;
+ * pcast_workspace_bytes() gives its size.
+ * Synchronisation: the call returns once the work is enqueued; results are
+ * valid after `stream` completes.  Calls on different streams may overlap.
+ * Errors: returns PCAST_OK or one of the codes above; no C++ exception crosses
+ * this boundary.
+ */
+int attn_fwd_pcast(const void* Q, const void* K, const void* V, const float* bias, int B, int Hq,
+                   int Hkv, int N, int d, int causal, float S, int order, float* out,
+                   unsigned long long* stats, void* stream);
+
+/* Number of uint64 words the stats buffer needs: B * Hq * ceil(N / 64) * 2. */
+size_t pcast_stats_words(int B, int Hq, int N);
+
+/* Bytes of stream-ordered temporary memory one attn_fwd_pcast call takes. */
+size_t pcast_workspace_bytes(int B, int Hkv, int N, int d, float S);
+
+/* Human-readable text for a return code, with the detail of the last error
+ * raised on the calling thread when there is one. */
+const char* pcast_strerror(int code);
+
+/* PCAST_ABI_VERSION of the built library. */
+int pcast_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PCAST_ATTN_H */

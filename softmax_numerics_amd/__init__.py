@@ -1,0 +1,110 @@
+"""FP8 P-cast attention forward for AMD MI355X -- Python binding of libpcast_attn.so.
+
+Argument marshalling only: every step of the attention runs in the HIP
+kernels behind the C ABI declared in include/pcast_attn.h.  PyTorch provides
+device memory and the stream.  There is no fallback: if the library is not
+built, or the device is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpcast_attn.so")
+
+PCAST_OK, PCAST_EINVAL, PCAST_ENOTSUP, PCAST_EHIP = 0, 1, 2, 3
+KV_BLOCK = 64
+ORDERS = {"forward": 0, "reverse": 1, 0: 0, 1: 1}
+
+# Every symbol include/pcast_attn.h declares.
+EXPORTS = ("attn_fwd_pcast", "pcast_stats_words", "pcast_workspace_bytes", "pcast_strerror",
+           "pcast_abi_version")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class PcastError(RuntimeError):
+    def __init__(self, code: int, text: str):
+        super().__init__(f"attn_fwd_pcast failed ({code}): {text}")
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the built library (raises if it is missing)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError(f"{path} is not built; run __graft_entry__.build() or "
+                                   "python -m softmax_numerics_amd.build")
+            lib = ctypes.CDLL(path)
+            P, I = ctypes.c_void_p, ctypes.c_int
+            lib.attn_fwd_pcast.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P]
+            lib.attn_fwd_pcast.restype = I
+            lib.pcast_stats_words.argtypes = [I, I, I]
+            lib.pcast_stats_words.restype = ctypes.c_size_t
+            lib.pcast_workspace_bytes.argtypes = [I, I, I, I, ctypes.c_float]
+            lib.pcast_workspace_bytes.restype = ctypes.c_size_t
+            lib.pcast_strerror.argtypes = [I]
+            lib.pcast_strerror.restype = ctypes.c_char_p
+            lib.pcast_abi_version.argtypes = []
+            lib.pcast_abi_version.restype = I
+            _lib = lib
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return load_library().pcast_strerror(code).decode()
+
+
+def attn_fwd_pcast(Q, K, V, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats, stream) -> int:
+    """Raw call with integer device addresses (0 for NULL); returns the C return code."""
+    return int(load_library().attn_fwd_pcast(Q, K, V, bias or None, B, Hq, Hkv, N, d, int(causal),
+                                             float(S), int(order), out, stats or None, stream or None))
+
+
+def stats_words(B: int, Hq: int, N: int) -> int:
+    return int(load_library().pcast_stats_words(B, Hq, N))
+
+
+def workspace_bytes(B: int, Hkv: int, N: int, d: int, S: float) -> int:
+    return int(load_library().pcast_workspace_bytes(B, Hkv, N, d, float(S)))
+
+
+def forward(q, k, v, bias=None, causal: bool = True, S: float = 256.0, order="reverse",
+            stats: bool = False, out=None):
+    """O = softmax(q k^T / sqrt(d) + bias) v with the P-cast, on the current stream.
+
+    q: bf16 [B, Hq, N, d]; k, v: bf16 [B, Hkv, N, d]; bias: fp32 [N] or None.
+    S > 0: P*S cast to E4M3; S = 0: the bf16 reference path.  Returns
+    (out fp32 [B, Hq, N, d], stats int64 [B, Hq, N/64, 2] or None).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D bfloat16 tensor on the GPU")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, N, d] matching q")
+    if bias is not None and (bias.dtype != torch.float32 or not bias.is_cuda or bias.shape != (N,)
+                             or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 [N] tensor on the GPU")
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+    st = None
+    if stats:
+        st = torch.empty(stats_words(B, Hq, N), dtype=torch.int64, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = attn_fwd_pcast(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                        0 if bias is None else bias.data_ptr(), B, Hq, Hkv, N, d, causal, S,
+                        ORDERS[order], out.data_ptr(), 0 if st is None else st.data_ptr(), stream)
+    if rc != PCAST_OK:
+        raise PcastError(rc, strerror(rc))
+    if st is not None:
+        st = st.view(B, Hq, -1, 2)
+    return out, st

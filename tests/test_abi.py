@@ -1,0 +1,91 @@
+"""CPU-side checks of the C ABI: the library loads, exports what the header
+declares, and rejects bad arguments before touching a device."""
+import os
+import re
+
+import pytest
+
+import softmax_numerics_amd as sna
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # an aligned non-null address; never dereferenced by the checks below
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sna.LIB_PATH):
+        from softmax_numerics_amd import build
+        build.build()
+    return sna.load_library()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pcast_attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    decl = r"^(?:const\s+)?(?:unsigned\s+)?[A-Za-z_][A-Za-z_0-9]*\s*\*?\s+\*?([a-z_0-9]+)\("
+    return set(re.findall(decl, text, flags=re.M))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert declared == set(sna.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_version_and_sizes(lib):
+    assert lib.pcast_abi_version() == 1
+    assert sna.stats_words(4, 32, 8192) == 4 * 32 * 128 * 2
+    assert sna.stats_words(1, 1, 100) == 4
+    assert sna.workspace_bytes(4, 32, 8192, 128, 256.0) == 4 * 32 * 8192 * 128 + 4 * 128
+    assert sna.workspace_bytes(4, 32, 8192, 128, 0.0) == 2 * 4 * 32 * 8192 * 128 + 4 * 128
+
+
+def _call(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128, causal=1, S=256.0,
+             order=1, out=FAKE, stats=0, stream=0)
+    a.update(kw)
+    return sna.attn_fwd_pcast(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=0), sna.PCAST_EINVAL),
+    (dict(out=0), sna.PCAST_EINVAL),
+    (dict(B=0), sna.PCAST_EINVAL),
+    (dict(Hq=3, Hkv=2), sna.PCAST_EINVAL),
+    (dict(causal=2), sna.PCAST_EINVAL),
+    (dict(order=2), sna.PCAST_EINVAL),
+    (dict(S=-1.0), sna.PCAST_EINVAL),
+    (dict(S=float("nan")), sna.PCAST_EINVAL),
+    (dict(S=float("inf")), sna.PCAST_EINVAL),
+    (dict(Q=FAKE + 8), sna.PCAST_EINVAL),
+    (dict(stats=FAKE + 4), sna.PCAST_EINVAL),
+    (dict(d=96), sna.PCAST_ENOTSUP),
+    (dict(N=100), sna.PCAST_ENOTSUP),
+])
+def test_argument_errors(lib, kw, code):
+    assert _call(**kw) == code
+    assert sna.strerror(code) != "success"
+
+
+def test_strerror_texts(lib):
+    assert sna.strerror(0) == "success"
+    _call(d=96)
+    assert "d = 96" in sna.strerror(sna.PCAST_ENOTSUP)
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "softmax_numerics_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", text, flags=re.M), f
+                assert "pcast_oracle" not in text, f
+
+
+def test_forward_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sna.forward(q, q, q)
