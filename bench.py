@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 P-cast attention forward on one MI355X.
+
+One step is one pass of the whole hot path over the workload's input, which
+is already resident in HBM: the V pre-pass (pcast_prepare_v) and the attention
+kernel (attn_fwd_pcast_prepared) with the underflow counters on.  The default
+workload is B=4, H=32, N=8192, d=128, causal, sink bias 7 on keys 0..3,
+S = 256, reverse order.
+
+Printed (one JSON line): throughput in TFLOP/s (algorithmic flops,
+FlashAttention convention 2*B*H*N^2*d for causal), the attention kernel's own
+time from HIP events on the launch stream, its fraction of the FP8 dense MFMA
+peak, the CPU oracle timed on a bounded sample of the same workload, and the
+output MSE against fp64 attention on that sample for S=256 reverse and S=1
+forward.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 P-cast attn fwd TFLOP/s + % MFMA peak; output MSE vs fp64 at Δ=7"
+PEAK_FP8 = 5000.0    # TFLOP/s, MI355X dense FP8 MFMA
+PEAK_BF16 = 2500.0   # TFLOP/s, MI355X dense bf16 MFMA
+KERNEL_SRC = os.path.join(ROOT, "softmax_numerics_amd", "csrc", "attn_fwd_pcast.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_throughput.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def causal_row_flops(rows, N: int, d: int, causal: bool):
+    import numpy as np
+    i = np.asarray(rows) % N
+    keys = (i + 1) if causal else np.full(i.shape, N)
+    return float(np.sum(4.0 * d * keys))
+
+
+def cpu_baseline(w, qb, kb, vb, bias, out_rev, out_fwd1, target_s: float, seed: int = 0):
+    """Time the oracle (kernel-mode block pipeline + exact attention, fp64, all
+    host threads) on random 64-row blocks of the same workload, and use its
+    exact result for the output-MSE comparison of the two GPU runs."""
+    import numpy as np
+    from oracle import core
+
+    nthreads = os.cpu_count() or 1
+    rng = np.random.default_rng(seed)
+    nb = w.N // 64
+    all_blocks = [(b, h, r) for b in range(w.B) for h in range(w.Hq) for r in range(nb)]
+
+    def rows_of(blocks):
+        return np.concatenate([np.arange(((b * w.Hq + h) * w.N + r * 64),
+                                         ((b * w.Hq + h) * w.N + r * 64) + 64) for b, h, r in blocks])
+
+    # calibrate on two blocks, then size the sample to about target_s seconds
+    calib = [all_blocks[i] for i in rng.choice(len(all_blocks), 2, replace=False)]
+    t0 = time.perf_counter()
+    core.rows(qb, kb, vb, bias, w.causal, 256.0, 1, "kernel", row_ids=rows_of(calib), nthreads=nthreads)
+    rate = causal_row_flops(rows_of(calib), w.N, w.d, w.causal) / max(time.perf_counter() - t0, 1e-3)
+    per_block = w.flops / len(all_blocks)
+    n = int(min(len(all_blocks), max(4, target_s * rate / per_block)))
+    blocks = [all_blocks[i] for i in sorted(rng.choice(len(all_blocks), n, replace=False))]
+    ids = rows_of(blocks)
+    t0 = time.perf_counter()
+    ref = core.rows(qb, kb, vb, bias, w.causal, 256.0, 1, "kernel", row_ids=ids, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    flops = causal_row_flops(ids, w.N, w.d, w.causal)
+    o1 = ref["o1"]
+    mse = {}
+    for name, out in (("S256_reverse", out_rev), ("S1_forward", out_fwd1)):
+        got = out.reshape(-1, w.d)[ids].astype(np.float64)
+        mse[name] = float(np.mean((got - o1) ** 2))
+    mse["oracle_S256_reverse"] = float(np.mean((ref["o2"] - o1) ** 2))
+    mse["ratio_S1fwd_over_S256rev"] = mse["S1_forward"] / mse["S256_reverse"]
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{n} random 64-row query blocks of {len(all_blocks)} ({ids.size} rows, "
+                      f"{flops / w.flops * 100:.2f}% of the flops), kernel-mode P-cast emulation plus "
+                      f"exact attention in fp64, {dt:.1f} s"}
+    return base, mse
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="throughput", choices=["tiny", "sweep", "throughput", "gqa", "long"])
+    ap.add_argument("--no-stats", action="store_true", help="time without the underflow counters")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the P-cast forward needs no collective, and multi-GPU runs are not part of this build",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import softmax_numerics_amd as sna
+    import synthetic
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    sna.load_library()
+    w = synthetic.WORKLOADS[args.workload]
+    delta, S, order = 7.0, 256.0, (0 if w.name == "tiny" else 1)   # tiny is non-causal, forward
+    dev = torch.device("cuda:0")
+    print(f"[bench] workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} causal={w.causal} "
+          f"delta={delta} S={S} order={order}", file=sys.stderr, flush=True)
+    qb, kb, vb = synthetic.qkv_bf16(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed)
+    bias = synthetic.sink_bias(w.N, delta)
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    q, k, v = to(qb), to(kb), to(vb)
+    bias_t = torch.from_numpy(bias).to(dev)
+    out = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device=dev)
+    stats = None if args.no_stats else torch.empty(sna.stats_words(w.B, w.Hq, w.N), dtype=torch.int64, device=dev)
+    ws = torch.empty(sna.workspace_bytes(w.B, w.Hkv, w.N, w.d, S), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def step(S_=S, order_=order, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        rc = sna.prepare_v(v.data_ptr(), w.B, w.Hkv, w.N, w.d, S_, ws.data_ptr(), sh)
+        if ev is not None:
+            ev[1].record(stream)
+        rc = rc or sna.attn_fwd_pcast_prepared(
+            q.data_ptr(), k.data_ptr(), ws.data_ptr(), bias_t.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d,
+            int(w.causal), S_, order_, out.data_ptr(), 0 if stats is None else stats.data_ptr(), sh)
+        if ev is not None:
+            ev[2].record(stream)
+        if rc != sna.PCAST_OK:
+            raise sna.PcastError(rc, sna.strerror(rc))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev=events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prep_ms = [e[0].elapsed_time(e[1]) for e in events]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in events]
+    ms_per_step = wall * 1e3 / args.steps
+    print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (wall), attention kernel "
+          f"{np.mean(attn_ms):.4f} ms, V pre-pass {np.mean(prep_ms):.4f} ms", file=sys.stderr, flush=True)
+
+    flops = w.flops
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (float(np.mean(attn_ms)) * 1e-3) / 1e12
+    mixed_roof = 1.0 / (0.5 / PEAK_BF16 + 0.5 / PEAK_FP8)
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3(P.V)+bf16(QK^T), fp32 softmax", "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} "
+                               f"{'causal' if w.causal else 'non-causal'}, sink bias {delta} on keys 0..3, "
+                               f"S={S:g}, {'reverse' if order else 'forward'} order, "
+                               f"underflow counters {'off' if stats is None else 'on'}",
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8, 4),
+                     "traffic": measured_traffic(w.name)},
+        "attention_kernel_ms": round(float(np.mean(attn_ms)), 5),
+        "v_prepass_ms": round(float(np.mean(prep_ms)), 5),
+        "frac_bf16_peak": round(achieved / PEAK_BF16, 4),
+        "frac_mixed_roof": round(achieved / mixed_roof, 4),
+    }
+
+    if not args.no_cpu_baseline:
+        out_rev = out.cpu().numpy()
+        step(S_=1.0, order_=0)                      # S = 1 forward, for the error contrast
+        torch.cuda.synchronize()
+        out_fwd1 = out.cpu().numpy()
+        base, mse = cpu_baseline(w, qb, kb, vb, bias, out_rev, out_fwd1, args.cpu_seconds)
+        result["cpu_baseline"] = base
+        result["mse_vs_fp64_sampled"] = mse
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -74,24 +74,51 @@ extern "C" {
  * stream hipStream_t, or NULL for the default stream.
  *
  * Ownership: the caller owns every buffer; the library keeps no pointer after
- * returning.  Temporary device memory -- a copy of V in E4M3 (or bf16 for
- * S = 0) laid out in the matrix-core operand order, B*Hkv*N*d bytes (twice
- * that for bf16), plus one flag per key block -- is taken from HIP's
- * stream-ordered allocator on `stream` and released on the same stream;
- * pcast_workspace_bytes() gives its size.
+ * returning.  The call takes pcast_workspace_bytes() of temporary device
+ * memory from HIP's stream-ordered allocator on `stream` and releases it on
+ * the same stream; pcast_prepare_v + attn_fwd_pcast_prepared do the same work
+ * without allocating.
  * Synchronisation: the call returns once the work is enqueued; results are
  * valid after `stream` completes.  Calls on different streams may overlap.
- * Errors: returns PCAST_OK or one of the codes above; no C++ exception crosses
- * this boundary.
+ * Errors: returns PCAST_OK or one of the codes above; argument errors are
+ * detected before anything is enqueued; no C++ exception crosses this
+ * boundary.
  */
 int attn_fwd_pcast(const void* Q, const void* K, const void* V, const float* bias, int B, int Hq,
                    int Hkv, int N, int d, int causal, float S, int order, float* out,
                    unsigned long long* stats, void* stream);
 
+/*
+ * The same forward in two stages, for callers that bring their own temporary
+ * memory (and for timing the attention kernel on its own).
+ *
+ * pcast_prepare_v -- enqueue the copy of V that the matrix cores read: for
+ * each (b, kv head, key block) a [d][64] tile of E4M3(V) (S > 0: round to
+ * nearest even, saturating at +/-448) or of V itself (S = 0, bf16), with the
+ * 64 keys in the order in which the attention kernel holds its probabilities.
+ *   V          device, bf16 [B][Hkv][N][d], 16-byte aligned.
+ *   workspace  device, pcast_workspace_bytes(B, Hkv, N, d, S) bytes, 16-byte
+ *              aligned, owned by the caller; overwritten.
+ *   B, Hkv, N, d, S as for attn_fwd_pcast (only S == 0 versus S > 0 matters).
+ * Returns as attn_fwd_pcast.
+ *
+ * attn_fwd_pcast_prepared -- enqueue the attention kernel reading V from a
+ * workspace filled by pcast_prepare_v with the same V, B, Hkv, N, d and the
+ * same choice of S == 0 or S > 0 (stream order, or any other synchronisation,
+ * must make the pre-pass complete first).  Other arguments, results and errors
+ * as for attn_fwd_pcast.  Allocates nothing.
+ */
+int pcast_prepare_v(const void* V, int B, int Hkv, int N, int d, float S, void* workspace,
+                    void* stream);
+
+int attn_fwd_pcast_prepared(const void* Q, const void* K, const void* workspace, const float* bias,
+                            int B, int Hq, int Hkv, int N, int d, int causal, float S, int order,
+                            float* out, unsigned long long* stats, void* stream);
+
 /* Number of uint64 words the stats buffer needs: B * Hq * ceil(N / 64) * 2. */
 size_t pcast_stats_words(int B, int Hq, int N);
 
-/* Bytes of stream-ordered temporary memory one attn_fwd_pcast call takes. */
+/* Bytes of the V operand copy: B * Hkv * N * d for S > 0, twice that for S = 0. */
 size_t pcast_workspace_bytes(int B, int Hkv, int N, int d, float S);
 
 /* Human-readable text for a return code, with the detail of the last error

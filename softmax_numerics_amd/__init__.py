@@ -19,8 +19,8 @@ KV_BLOCK = 64
 ORDERS = {"forward": 0, "reverse": 1, 0: 0, 1: 1}
 
 # Every symbol include/pcast_attn.h declares.
-EXPORTS = ("attn_fwd_pcast", "pcast_stats_words", "pcast_workspace_bytes", "pcast_strerror",
-           "pcast_abi_version")
+EXPORTS = ("attn_fwd_pcast", "pcast_prepare_v", "attn_fwd_pcast_prepared", "pcast_stats_words",
+           "pcast_workspace_bytes", "pcast_strerror", "pcast_abi_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -44,6 +44,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             P, I = ctypes.c_void_p, ctypes.c_int
             lib.attn_fwd_pcast.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P]
             lib.attn_fwd_pcast.restype = I
+            lib.pcast_prepare_v.argtypes = [P, I, I, I, I, ctypes.c_float, P, P]
+            lib.pcast_prepare_v.restype = I
+            lib.attn_fwd_pcast_prepared.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I,
+                                                    P, P, P]
+            lib.attn_fwd_pcast_prepared.restype = I
             lib.pcast_stats_words.argtypes = [I, I, I]
             lib.pcast_stats_words.restype = ctypes.c_size_t
             lib.pcast_workspace_bytes.argtypes = [I, I, I, I, ctypes.c_float]
@@ -64,6 +69,19 @@ def attn_fwd_pcast(Q, K, V, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats
     """Raw call with integer device addresses (0 for NULL); returns the C return code."""
     return int(load_library().attn_fwd_pcast(Q, K, V, bias or None, B, Hq, Hkv, N, d, int(causal),
                                              float(S), int(order), out, stats or None, stream or None))
+
+
+def prepare_v(V, B, Hkv, N, d, S, workspace, stream) -> int:
+    """Raw pcast_prepare_v with integer device addresses; returns the C return code."""
+    return int(load_library().pcast_prepare_v(V, B, Hkv, N, d, float(S), workspace, stream or None))
+
+
+def attn_fwd_pcast_prepared(Q, K, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
+                            stream) -> int:
+    """Raw attn_fwd_pcast_prepared with integer device addresses; returns the C return code."""
+    return int(load_library().attn_fwd_pcast_prepared(
+        Q, K, workspace, bias or None, B, Hq, Hkv, N, d, int(causal), float(S), int(order), out,
+        stats or None, stream or None))
 
 
 def stats_words(B: int, Hq: int, N: int) -> int:

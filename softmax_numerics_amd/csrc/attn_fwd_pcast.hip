@@ -71,14 +71,11 @@ struct Geometry {
 
 // ---------------------------------------------------------------------------
 // Pre-pass: V (bf16, [B][Hkv][N][D]) -> operand copy [B][Hkv][N/64][D][64]
-// in slot order, E4M3 (RNE, saturating) or bf16.  Also one flag per key block
-// telling whether any key in it has a non-zero bias.
+// in slot order, E4M3 (RNE, saturating) or bf16.
 // ---------------------------------------------------------------------------
 template <int D, bool kFp8>
 __global__ __launch_bounds__(256) void pcast_prep_v(const uint16_t* __restrict__ V,
-                                                     void* __restrict__ vop,
-                                                     const float* __restrict__ bias,
-                                                     int* __restrict__ bias_flags, int n_tiles) {
+                                                     void* __restrict__ vop) {
   __shared__ uint16_t tile[kKvBlock][D + 2];
   const int tid = threadIdx.x;
   const int64_t blk = blockIdx.x;  // flat (b, hkv, key block)
@@ -119,11 +116,6 @@ __global__ __launch_bounds__(256) void pcast_prep_v(const uint16_t* __restrict__
       dst[col * 32 + pair] = (uint32_t)tile[k0][col] | ((uint32_t)tile[k0 + 1][col] << 16);
     }
   }
-  if (bias != nullptr && blk < n_tiles && tid < 64) {
-    const bool nz = bias[blk * kKvBlock + tid] != 0.0f;
-    const uint64_t any = __ballot(nz);
-    if (tid == 0) bias_flags[blk] = any != 0 ? 1 : 0;
-  }
 }
 
 struct Params {
@@ -131,7 +123,6 @@ struct Params {
   const uint16_t* k;
   const void* vop;
   const float* bias;
-  const int* bias_flags;
   float* out;
   unsigned long long* stats;
   int B, Hq, Hkv, N;
@@ -189,6 +180,8 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kKBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][kVBytes];
+  __shared__ float lds_bias[2][kKvBlock];  // bias * log2(e) of the staged key block
+  __shared__ int lds_bflag[2];              // any non-zero bias in the staged block
   __shared__ unsigned int lds_cnt[2][2];
 
   const int tid = threadIdx.x;
@@ -222,6 +215,8 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
                          ((int64_t)b * p.Hkv + hk) * (int64_t)n_tiles * kKvBlock * D * kEsize;
 
   i32x4_t kreg[kKPer], vreg[kVPer];
+  float breg = 0.0f;
+  const bool with_bias = p.bias != nullptr;
   auto tile_of = [&](int it) { return p.order ? (t_last - it) : it; };
   auto load_regs = [&](int t) {
     const uint8_t* ks = kbase + (int64_t)t * kKvBlock * D * 2;
@@ -230,6 +225,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
     for (int i = 0; i < kKPer; ++i) kreg[i] = *reinterpret_cast<const i32x4_t*>(ks + (int64_t)(i * kThreads + tid) * 16);
 #pragma unroll
     for (int i = 0; i < kVPer; ++i) vreg[i] = *reinterpret_cast<const i32x4_t*>(vs + (int64_t)(i * kThreads + tid) * 16);
+    if (with_bias && wave == 0) breg = p.bias[t * kKvBlock + lane];
   };
   auto store_lds = [&](int buf) {
 #pragma unroll
@@ -243,6 +239,11 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
       const int c = i * kThreads + tid;
       const int row = c / (kKvBlock * kEsize / 16), part = c % (kKvBlock * kEsize / 16);
       *reinterpret_cast<i32x4_t*>(&lds_v[buf][row * kVStride + part * 16]) = vreg[i];
+    }
+    if (with_bias && wave == 0) {
+      lds_bias[buf][lane] = breg * kLog2e;
+      const bool any = __ballot(breg != 0.0f) != 0;
+      if (lane == 0) lds_bflag[buf] = any ? 1 : 0;
     }
   };
 
@@ -267,7 +268,8 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
     const bool visible = wave_active && (!p.causal || key0 <= wrow0 + kRowsPerWave - 1);
     if (visible) {
       const bool diag = p.causal && (key0 + kKvBlock - 1 > wrow0);
-      const bool has_bias = p.bias != nullptr && p.bias_flags[t] != 0;
+      const bool has_bias = with_bias && lds_bflag[cur] != 0;
+      const float* bl = lds_bias[cur];
 
       // ---- S^T = K Q^T (two 32-key halves) ----
       f32x16_t sacc[2];
@@ -293,8 +295,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
         for (int r = 0; r < 16; ++r) x[kb * 16 + r] = sacc[kb][r] * p.logit_scale;
       if (has_bias) {
 #pragma unroll
-        for (int j = 0; j < 32; ++j)
-          x[j] = fmaf(p.bias[key0 + slot_key(g, j)], kLog2e, x[j]);
+        for (int j = 0; j < 32; ++j) x[j] += bl[slot_key(g, j)];
       }
       if (diag) {
 #pragma unroll
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
             for (int j = 0; j < 32; ++j) {
               const int key = key0 + slot_key(g, j);
               const bool vis = !p.causal || key <= myrow;
-              const bool nonsink = !has_bias || p.bias[key] == 0.0f;
+              const bool nonsink = !has_bias || bl[key - key0] == 0.0f;
               const bool z = ((pw[j / 4] >> (8 * (j % 4))) & 0xFFu) == 0;
               cnt_tot += (vis && nonsink);
               cnt_zero += (vis && nonsink && z);
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
           for (int j = 0; j < 32; ++j) {
             const int key = key0 + slot_key(g, j);
             const bool vis = !p.causal || key <= myrow;
-            const bool nonsink = !has_bias || p.bias[key] == 0.0f;
+            const bool nonsink = !has_bias || bl[key - key0] == 0.0f;
             const bool z = ((pw[j / 2] >> (16 * (j % 2))) & 0xFFFFu) == 0;
             cnt_tot += (vis && nonsink);
             cnt_zero += (vis && nonsink && z);
@@ -482,22 +483,17 @@ bool is_pow2(float S) {
 }
 
 template <int D, bool kFp8>
-int launch(const Params& base, const uint16_t* V, void* ws, size_t vop_bytes, hipStream_t stream) {
-  Params p = base;
-  const int n_tiles = p.N / kKvBlock;
-  int* flags = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + vop_bytes);
-  p.vop = ws;
-  p.bias_flags = flags;
-  const int64_t nblk = (int64_t)p.B * p.Hkv * n_tiles;
-  hipLaunchKernelGGL((pcast_prep_v<D, kFp8>), dim3((unsigned)nblk), dim3(256), 0, stream, V, ws, p.bias,
-                     flags, n_tiles);
+void launch_prep(const uint16_t* V, void* ws, int64_t n_blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((pcast_prep_v<D, kFp8>), dim3((unsigned)n_blocks), dim3(256), 0, stream, V, ws);
+}
+
+template <int D, bool kFp8>
+void launch_attn(const Params& p, hipStream_t stream) {
   const dim3 grid((p.N + kBlockRows - 1) / kBlockRows, p.Hq, p.B);
   if (p.stats)
     hipLaunchKernelGGL((pcast_attn_fwd<D, kFp8, true>), grid, dim3(kThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((pcast_attn_fwd<D, kFp8, false>), grid, dim3(kThreads), 0, stream, p);
-  const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? PCAST_OK : hip_fail(e, "kernel launch");
 }
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
@@ -513,9 +509,7 @@ size_t pcast_stats_words(int B, int Hq, int N) {
 
 size_t pcast_workspace_bytes(int B, int Hkv, int N, int d, float S) {
   if (B <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return 0;
-  const size_t esize = (S == 0.0f) ? 2 : 1;
-  const size_t vop = (size_t)B * Hkv * N * d * esize;
-  return vop + sizeof(int) * (size_t)((N + kKvBlock - 1) / kKvBlock);
+  return (size_t)B * Hkv * N * d * ((S == 0.0f) ? 2 : 1);
 }
 
 int pcast_abi_version(void) { return PCAST_ABI_VERSION; }
@@ -534,39 +528,67 @@ const char* pcast_strerror(int code) {
   return buf;
 }
 
-int attn_fwd_pcast(const void* Q, const void* K, const void* V, const float* bias, int B, int Hq,
-                   int Hkv, int N, int d, int causal, float S, int order, float* out,
-                   unsigned long long* stats, void* stream) {
-  g_last_error[0] = '\0';
-  // ---- argument checks: nothing touches the device before they pass ----
-  if (!Q || !K || !V || !out) return fail(PCAST_EINVAL, "Q, K, V and out must be non-null");
+}  // extern "C"
+
+namespace {
+
+// Shape and scalar checks shared by the entry points.  Nothing here touches the device.
+int check_shape(int B, int Hq, int Hkv, int N, int d, float S) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0)
     return fail(PCAST_EINVAL, "B, Hq, Hkv, N, d must be positive");
   if (Hq % Hkv != 0) return fail(PCAST_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (!std::isfinite(S) || S < 0.0f) return fail(PCAST_EINVAL, "S must be finite and >= 0");
+  if (d != 64 && d != 128) return fail(PCAST_ENOTSUP, "d = %d: supported head sizes are 64 and 128", d);
+  if (N % kKvBlock != 0) return fail(PCAST_ENOTSUP, "N = %d: must be a multiple of %d", N, kKvBlock);
+  if ((int64_t)B * Hkv * (N / kKvBlock) > (int64_t)INT32_MAX || Hq > 65535 || B > 65535)
+    return fail(PCAST_ENOTSUP, "grid too large");
+  return PCAST_OK;
+}
+
+int check_attn_args(const void* Q, const void* K, const float* bias, int causal, int order,
+                    const float* out, const unsigned long long* stats) {
+  if (!Q || !K || !out) return fail(PCAST_EINVAL, "Q, K and out must be non-null");
   if (causal != 0 && causal != 1) return fail(PCAST_EINVAL, "causal must be 0 or 1");
   if (order != PCAST_ORDER_FORWARD && order != PCAST_ORDER_REVERSE)
     return fail(PCAST_EINVAL, "order must be 0 (forward) or 1 (reverse)");
-  if (!std::isfinite(S) || S < 0.0f) return fail(PCAST_EINVAL, "S must be finite and >= 0");
-  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16))
-    return fail(PCAST_EINVAL, "Q, K, V and out must be 16-byte aligned");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(out, 16))
+    return fail(PCAST_EINVAL, "Q, K and out must be 16-byte aligned");
   if (bias && !aligned(bias, 4)) return fail(PCAST_EINVAL, "bias must be 4-byte aligned");
   if (stats && !aligned(stats, 8)) return fail(PCAST_EINVAL, "stats must be 8-byte aligned");
-  if (d != 64 && d != 128) return fail(PCAST_ENOTSUP, "d = %d: supported head sizes are 64 and 128", d);
-  if (N % kKvBlock != 0) return fail(PCAST_ENOTSUP, "N = %d: must be a multiple of %d", N, kKvBlock);
-  if ((int64_t)Hq * ((N + kBlockRows - 1) / kBlockRows) > (int64_t)INT32_MAX || Hq > 65535 || B > 65535)
-    return fail(PCAST_ENOTSUP, "grid too large");
+  return PCAST_OK;
+}
 
+int check_device() {
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  const hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   const int arch = arch_check(dev);
   if (arch < 0) return fail(PCAST_EHIP, "cannot query device %d", dev);
   if (arch > 0) return fail(PCAST_ENOTSUP, "device %d is not gfx950", dev);
+  return PCAST_OK;
+}
 
+int enqueue_prep(const void* V, int B, int Hkv, int N, int d, float S, void* ws, hipStream_t st) {
+  const bool fp8 = S != 0.0f;
+  const int64_t n_blocks = (int64_t)B * Hkv * (N / kKvBlock);
+  const uint16_t* Vb = static_cast<const uint16_t*>(V);
+  if (d == 64) {
+    if (fp8) launch_prep<64, true>(Vb, ws, n_blocks, st); else launch_prep<64, false>(Vb, ws, n_blocks, st);
+  } else {
+    if (fp8) launch_prep<128, true>(Vb, ws, n_blocks, st); else launch_prep<128, false>(Vb, ws, n_blocks, st);
+  }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PCAST_OK : hip_fail(e, "V pre-pass launch");
+}
+
+int enqueue_attn(const void* Q, const void* K, const void* ws, const float* bias, int B, int Hq,
+                 int Hkv, int N, int d, int causal, float S, int order, float* out,
+                 unsigned long long* stats, hipStream_t st) {
   const bool fp8 = S != 0.0f;
   Params p{};
   p.q = static_cast<const uint16_t*>(Q);
   p.k = static_cast<const uint16_t*>(K);
+  p.vop = ws;
   p.bias = bias;
   p.out = out;
   p.stats = stats;
@@ -579,20 +601,63 @@ int attn_fwd_pcast(const void* Q, const void* K, const void* V, const float* bia
   // otherwise S*fl(448/S) may exceed 448 by an ulp, which still rounds to 448).
   p.p_clamp = fp8 ? 448.0f / S : 1.0f;
   p.scale_mode = fp8 ? ((is_pow2(S) ? 0 : 2) | (S > 448.0f ? 1 : 0)) : 0;
+  if (d == 64) {
+    if (fp8) launch_attn<64, true>(p, st); else launch_attn<64, false>(p, st);
+  } else {
+    if (fp8) launch_attn<128, true>(p, st); else launch_attn<128, false>(p, st);
+  }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PCAST_OK : hip_fail(e, "attention kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int pcast_prepare_v(const void* V, int B, int Hkv, int N, int d, float S, void* workspace,
+                    void* stream) {
+  g_last_error[0] = '\0';
+  if (!V || !workspace) return fail(PCAST_EINVAL, "V and workspace must be non-null");
+  if (!aligned(V, 16) || !aligned(workspace, 16))
+    return fail(PCAST_EINVAL, "V and workspace must be 16-byte aligned");
+  int rc = check_shape(B, Hkv, Hkv, N, d, S);
+  if (rc != PCAST_OK) return rc;
+  if ((rc = check_device()) != PCAST_OK) return rc;
+  return enqueue_prep(V, B, Hkv, N, d, S, workspace, static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_pcast_prepared(const void* Q, const void* K, const void* workspace, const float* bias,
+                            int B, int Hq, int Hkv, int N, int d, int causal, float S, int order,
+                            float* out, unsigned long long* stats, void* stream) {
+  g_last_error[0] = '\0';
+  if (!workspace) return fail(PCAST_EINVAL, "workspace must be non-null");
+  if (!aligned(workspace, 16)) return fail(PCAST_EINVAL, "workspace must be 16-byte aligned");
+  int rc = check_attn_args(Q, K, bias, causal, order, out, stats);
+  if (rc != PCAST_OK) return rc;
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  if ((rc = check_device()) != PCAST_OK) return rc;
+  return enqueue_attn(Q, K, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
+                      static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_pcast(const void* Q, const void* K, const void* V, const float* bias, int B, int Hq,
+                   int Hkv, int N, int d, int causal, float S, int order, float* out,
+                   unsigned long long* stats, void* stream) {
+  g_last_error[0] = '\0';
+  // ---- argument checks: nothing touches the device before they pass ----
+  int rc = check_attn_args(Q, K, bias, causal, order, out, stats);
+  if (rc != PCAST_OK) return rc;
+  if (!V) return fail(PCAST_EINVAL, "V must be non-null");
+  if (!aligned(V, 16)) return fail(PCAST_EINVAL, "V must be 16-byte aligned");
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  if ((rc = check_device()) != PCAST_OK) return rc;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const size_t vop_bytes = (size_t)B * Hkv * N * d * (fp8 ? 1 : 2);
-  const size_t ws_bytes = pcast_workspace_bytes(B, Hkv, N, d, S);
   void* ws = nullptr;
-  e = hipMallocAsync(&ws, ws_bytes, st);
+  hipError_t e = hipMallocAsync(&ws, pcast_workspace_bytes(B, Hkv, N, d, S), st);
   if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
-
-  int rc;
-  const uint16_t* Vb = static_cast<const uint16_t*>(V);
-  if (d == 64)
-    rc = fp8 ? launch<64, true>(p, Vb, ws, vop_bytes, st) : launch<64, false>(p, Vb, ws, vop_bytes, st);
-  else
-    rc = fp8 ? launch<128, true>(p, Vb, ws, vop_bytes, st) : launch<128, false>(p, Vb, ws, vop_bytes, st);
+  rc = enqueue_prep(V, B, Hkv, N, d, S, ws, st);
+  if (rc == PCAST_OK) rc = enqueue_attn(Q, K, ws, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats, st);
   e = hipFreeAsync(ws, st);
   if (rc != PCAST_OK) return rc;
   if (e != hipSuccess) return hip_fail(e, "hipFreeAsync(workspace)");

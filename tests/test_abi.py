@@ -37,8 +37,8 @@ def test_version_and_sizes(lib):
     assert lib.pcast_abi_version() == 1
     assert sna.stats_words(4, 32, 8192) == 4 * 32 * 128 * 2
     assert sna.stats_words(1, 1, 100) == 4
-    assert sna.workspace_bytes(4, 32, 8192, 128, 256.0) == 4 * 32 * 8192 * 128 + 4 * 128
-    assert sna.workspace_bytes(4, 32, 8192, 128, 0.0) == 2 * 4 * 32 * 8192 * 128 + 4 * 128
+    assert sna.workspace_bytes(4, 32, 8192, 128, 256.0) == 4 * 32 * 8192 * 128
+    assert sna.workspace_bytes(4, 32, 8192, 128, 0.0) == 2 * 4 * 32 * 8192 * 128
 
 
 def _call(**kw):
@@ -66,6 +66,32 @@ def _call(**kw):
 def test_argument_errors(lib, kw, code):
     assert _call(**kw) == code
     assert sna.strerror(code) != "success"
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(workspace=0), sna.PCAST_EINVAL),
+    (dict(workspace=FAKE + 4), sna.PCAST_EINVAL),
+    (dict(Q=0), sna.PCAST_EINVAL),
+    (dict(order=5), sna.PCAST_EINVAL),
+    (dict(N=96), sna.PCAST_ENOTSUP),
+])
+def test_prepared_argument_errors(lib, kw, code):
+    a = dict(Q=FAKE, K=FAKE, workspace=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128, causal=1,
+             S=256.0, order=1, out=FAKE, stats=0, stream=0)
+    a.update(kw)
+    assert sna.attn_fwd_pcast_prepared(**a) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(V=0), sna.PCAST_EINVAL),
+    (dict(workspace=0), sna.PCAST_EINVAL),
+    (dict(S=-2.0), sna.PCAST_EINVAL),
+    (dict(d=32), sna.PCAST_ENOTSUP),
+])
+def test_prepare_argument_errors(lib, kw, code):
+    a = dict(V=FAKE, B=1, Hkv=1, N=128, d=128, S=256.0, workspace=FAKE, stream=0)
+    a.update(kw)
+    assert sna.prepare_v(**a) == code
 
 
 def test_strerror_texts(lib):
