@@ -64,9 +64,20 @@ __host__ __device__ constexpr int slot_key(int g, int b) {
 
 template <int D>
 struct Geometry {
-  static constexpr int kKStride = D * 2 + 16;  // bytes per K row in LDS (padded)
   static constexpr int kQSteps = D / 16;       // bf16 MFMA k-steps over d
   static constexpr int kDTiles = D / 32;       // 32-column output tiles
+};
+
+// An LDS tile of rows of kRowBytes, stored without padding: the 16-byte chunk c of
+// row r sits at chunk position c ^ key(r), key(r) = (r / rows per 256 bytes) % chunks
+// per row.  The 16 lanes of one ds_read_b128 phase that read the same logical chunk
+// of 16 consecutive rows then cover all 64 banks.
+template <int kRowBytes>
+struct Swizzle {
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kRowsPerWindow = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
+  __device__ static int key(int row) { return (row / kRowsPerWindow) % kChunks; }
+  __device__ static int offset(int row, int chunk) { return row * kRowBytes + ((chunk ^ key(row)) << 4); }
 };
 
 // ---------------------------------------------------------------------------
@@ -126,38 +137,46 @@ struct Params {
   float* out;
   unsigned long long* stats;
   int B, Hq, Hkv, N;
-  int causal, order;
+  int order;
   float logit_scale;  // log2(e) / sqrt(d)
   float S;            // P-cast scale (1 in the bf16 path)
-  float inv_S;        // 1/S, the conversion scale when S is a power of two
-  float p_clamp;      // largest P kept before conversion (448/S when S > 448)
-  int scale_mode;     // 0: S = 2^k <= 448, 1: S = 2^k > 448, 2: other S <= 448, 3: other S > 448
+  float inv_S;        // 1/S: the conversion scale when S is a power of two
+  float p_clamp;      // largest P kept before conversion when S > 448 (448/S)
 };
 
-__device__ inline uint32_t zero_bytes(uint32_t w) {
-  const uint32_t t = (w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu;
-  return __builtin_popcount(~(t | w | 0x7F7F7F7Fu));
-}
+// How P becomes an MFMA operand.
+enum PMode : int {
+  kPow2 = 0,       // E4M3, S = 2^k <= 448: scaling inside the conversion (exact)
+  kPow2Clamp = 1,  // E4M3, S = 2^k > 448: P clamped to 448/S first
+  kMul = 2,        // E4M3, other S <= 448: fp32 multiply, then conversion
+  kMulClamp = 3,   // E4M3, other S > 448: clamp, multiply, convert
+  kBf16 = 4,       // no P-cast: P and V in bf16
+};
 
-__device__ inline uint32_t zero_halves(uint32_t w) {
-  return ((w & 0xFFFFu) == 0) + ((w >> 16) == 0);
+// Non-zero E4M3 codes among the 4 bytes of w.  Codes of P*S >= 0 lie in
+// [0x00, 0x7E], so adding 0x7F sets bit 7 of a byte exactly when it is non-zero
+// and never carries into the next byte.
+__device__ inline uint32_t nonzero_codes(uint32_t w, uint32_t acc) {
+  return __builtin_popcount((w + 0x7F7F7F7Fu) & 0x80808080u) + acc;
 }
 
 // Convert 4 probabilities to 4 E4M3 codes in one word.
-__device__ inline uint32_t cast4_fp8(const Params& p, float a, float b, float c, float d) {
-  if (p.scale_mode & 1) {  // S > 448: keep S*P <= 448
+template <int kMode>
+__device__ inline uint32_t cast4(const Params& p, float a, float b, float c, float d) {
+  if constexpr (kMode == kPow2Clamp || kMode == kMulClamp) {
     const float lim = p.p_clamp;
     a = fminf(a, lim); b = fminf(b, lim); c = fminf(c, lim); d = fminf(d, lim);
   }
-  if (p.scale_mode < 2) {  // power of two: exact scaling inside the conversion
+  if constexpr (kMode == kPow2 || kMode == kPow2Clamp) {
     s16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2_t{0, 0}, a, b, p.inv_S, false);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, p.inv_S, true);
     return __builtin_bit_cast(uint32_t, r);
+  } else {
+    const float S = p.S;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a * S, b * S, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c * S, d * S, w, true);
+    return (uint32_t)w;
   }
-  const float S = p.S;
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a * S, b * S, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c * S, d * S, w, true);
-  return (uint32_t)w;
 }
 
 __device__ inline uint32_t cast2_bf16(float a, float b) {
@@ -165,40 +184,78 @@ __device__ inline uint32_t cast2_bf16(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-template <int D, bool kFp8, bool kStats>
+typedef __attribute__((address_space(1))) const void global_cvoid;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS: lane i writes
+// lds + 16*i (global_load_lds_dwordx4; `lds` must be the same in every lane).
+__device__ inline void load_to_lds16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)lds, 16, 0, 0);
+}
+
+// max over the two 32-lane halves (lane l and lane l ^ 32 hold the same query row)
+__device__ inline float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+
+__device__ inline float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+// Workgroup -> (batch, head, 128-row block).  The hardware hands workgroup i
+// to XCD i % 8; the remap gives each XCD a contiguous range of heads so that
+// the K/V of a head are read into one XCD's L2, and within a head the
+// longest (causal) row blocks start first.
+__device__ inline void decode_block(int lin, int total, int n_rb, int Hq, bool causal, int& b, int& h,
+                                    int& rb) {
+  const int q = total / 8, r = total % 8;
+  const int xcd = lin % 8, slot = lin / 8;
+  const int v = (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+  const int hh = v / n_rb, rbi = v % n_rb;
+  rb = causal ? n_rb - 1 - rbi : rbi;
+  b = hh / Hq;
+  h = hh % Hq;
+}
+
+template <int D, int kMode, bool kCausal, bool kStats>
 __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
   using G = Geometry<D>;
+  constexpr bool kFp8 = kMode != kBf16;
   constexpr int kEsize = kFp8 ? 1 : 2;                      // bytes per V operand element
-  constexpr int kVStride = kKvBlock * kEsize + 16;          // bytes per V^T row in LDS (padded)
-  constexpr int kKBytes = kKvBlock * G::kKStride;
-  constexpr int kVBytes = D * kVStride;
-  constexpr int kKChunks = kKvBlock * D * 2 / 16;           // 16-byte chunks per K block
-  constexpr int kVChunks = D * kKvBlock * kEsize / 16;      // 16-byte chunks per V block
-  constexpr int kKPer = kKChunks / kThreads;
-  constexpr int kVPer = kVChunks / kThreads;
-  static_assert(kKChunks % kThreads == 0 && kVChunks % kThreads == 0, "staging split");
+  constexpr int kKRow = D * 2;                              // bytes per K row
+  constexpr int kVRow = kKvBlock * kEsize;                  // bytes per V^T row (64 keys)
+  constexpr int kKTile = kKvBlock * kKRow;                  // bytes of one K block
+  constexpr int kVTile = D * kVRow;                         // bytes of one V operand block
+  using SK = Swizzle<kKRow>;
+  using SV = Swizzle<kVRow>;
+  // direct global -> LDS loads (64 lanes x 16 bytes = 1 KB each) per wave and block
+  constexpr int kKLoads = kKTile / (1024 * kWaves);
+  constexpr int kVLoads = kVTile / (1024 * kWaves);
+  static_assert(kKTile % (1024 * kWaves) == 0 && kVTile % (1024 * kWaves) == 0, "staging split");
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kKBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][kVBytes];
-  __shared__ float lds_bias[2][kKvBlock];  // bias * log2(e) of the staged key block
-  __shared__ int lds_bflag[2];              // any non-zero bias in the staged block
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kKTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][kVTile];
   __shared__ unsigned int lds_cnt[2][2];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
   const int g = lane / 32, li = lane % 32;
   const int n_rb = (p.N + kBlockRows - 1) / kBlockRows;
-  // causal: heaviest row blocks first
-  const int rb = p.causal ? (n_rb - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  int b, h, rb;
+  decode_block(blockIdx.x, n_rb * p.Hq * p.B, n_rb, p.Hq, kCausal, b, h, rb);
   const int hk = h / (p.Hq / p.Hkv);
   const int n_tiles = p.N / kKvBlock;
   const int row0 = rb * kBlockRows;
   const int wrow0 = row0 + wave * kRowsPerWave;  // first row of this wave
   const int myrow = wrow0 + li;
   const bool wave_active = wrow0 < p.N;
-  const int t_last = p.causal ? min((row0 + kBlockRows - 1) / kKvBlock, n_tiles - 1) : n_tiles - 1;
+  const int t_last = kCausal ? min((row0 + kBlockRows - 1) / kKvBlock, n_tiles - 1) : n_tiles - 1;
   const int n_it = t_last + 1;
+  const float c = p.logit_scale;
 
   if (kStats && tid < 4) lds_cnt[tid / 2][tid % 2] = 0;
 
@@ -211,39 +268,55 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
   }
 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k + ((int64_t)b * p.Hkv + hk) * p.N * D);
-  const uint8_t* vbase = static_cast<const uint8_t*>(p.vop) +
-                         ((int64_t)b * p.Hkv + hk) * (int64_t)n_tiles * kKvBlock * D * kEsize;
+  const uint8_t* vbase = static_cast<const uint8_t*>(p.vop) + ((int64_t)b * p.Hkv + hk) * (int64_t)n_tiles * kVTile;
 
-  i32x4_t kreg[kKPer], vreg[kVPer];
-  float breg = 0.0f;
+  // Each lane's source offsets for the direct loads: lane i of load j of wave w fills
+  // LDS chunk position (w * loads + j) * 64 + i, which holds logical chunk
+  // position ^ key(row) of that row.
+  int ksrc[kKLoads], vsrc[kVLoads];
+#pragma unroll
+  for (int i = 0; i < kKLoads; ++i) {
+    const int pos = (wave * kKLoads + i) * 64 + lane, r = pos / SK::kChunks;
+    ksrc[i] = r * kKRow + (((pos % SK::kChunks) ^ SK::key(r)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < kVLoads; ++i) {
+    const int pos = (wave * kVLoads + i) * 64 + lane, r = pos / SV::kChunks;
+    vsrc[i] = r * kVRow + (((pos % SV::kChunks) ^ SV::key(r)) << 4);
+  }
   const bool with_bias = p.bias != nullptr;
+  float bpend = 0.0f;  // bias of key (block start + lane) for the next step's block
   auto tile_of = [&](int it) { return p.order ? (t_last - it) : it; };
-  auto load_regs = [&](int t) {
-    const uint8_t* ks = kbase + (int64_t)t * kKvBlock * D * 2;
-    const uint8_t* vs = vbase + (int64_t)t * kKvBlock * D * kEsize;
-#pragma unroll
-    for (int i = 0; i < kKPer; ++i) kreg[i] = *reinterpret_cast<const i32x4_t*>(ks + (int64_t)(i * kThreads + tid) * 16);
-#pragma unroll
-    for (int i = 0; i < kVPer; ++i) vreg[i] = *reinterpret_cast<const i32x4_t*>(vs + (int64_t)(i * kThreads + tid) * 16);
-    if (with_bias && wave == 0) breg = p.bias[t * kKvBlock + lane];
+  auto visible = [&](int t) {
+    return wave_active && (!kCausal || t * kKvBlock <= wrow0 + kRowsPerWave - 1);
   };
-  auto store_lds = [&](int buf) {
+  auto load_k = [&](int t, int buf) {
+    const uint8_t* ks = kbase + t * kKTile;
 #pragma unroll
-    for (int i = 0; i < kKPer; ++i) {
-      const int c = i * kThreads + tid;
-      const int row = c / (D * 2 / 16), part = c % (D * 2 / 16);
-      *reinterpret_cast<i32x4_t*>(&lds_k[buf][row * G::kKStride + part * 16]) = kreg[i];
-    }
+    for (int i = 0; i < kKLoads; ++i)
+      load_to_lds16(ks + ksrc[i], &lds_k[buf][(wave * kKLoads + i) * 1024]);
+  };
+  auto load_v = [&](int t, int buf) {
+    const uint8_t* vs = vbase + t * kVTile;
 #pragma unroll
-    for (int i = 0; i < kVPer; ++i) {
-      const int c = i * kThreads + tid;
-      const int row = c / (kKvBlock * kEsize / 16), part = c % (kKvBlock * kEsize / 16);
-      *reinterpret_cast<i32x4_t*>(&lds_v[buf][row * kVStride + part * 16]) = vreg[i];
-    }
-    if (with_bias && wave == 0) {
-      lds_bias[buf][lane] = breg * kLog2e;
-      const bool any = __ballot(breg != 0.0f) != 0;
-      if (lane == 0) lds_bflag[buf] = any ? 1 : 0;
+    for (int i = 0; i < kVLoads; ++i)
+      load_to_lds16(vs + vsrc[i], &lds_v[buf][(wave * kVLoads + i) * 1024]);
+  };
+  auto load_bias = [&](int t) {
+    if (with_bias) bpend = p.bias[t * kKvBlock + lane];
+  };
+  auto wait_loads = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // S^T = K Q^T for the key block staged in K buffer `buf` (two 32-key halves, fp32 accumulation)
+  const int xk = SK::key(li);  // rows li and li + 32 share the swizzle key
+  auto issue_s = [&](int buf, f32x16_t(&sa)[2]) {
+    const uint8_t* kl = lds_k[buf] + li * kKRow;
+#pragma unroll
+    for (int s = 0; s < G::kQSteps; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + kb * 32 * kKRow + (((2 * s + g) ^ xk) << 4));
+        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16_t{} : sa[kb], 0, 0, 0);
+      }
     }
   };
 
@@ -252,158 +325,208 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
   for (int dt = 0; dt < G::kDTiles; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+  f32x16_t sacc[2];  // logits (then probabilities) of the block being processed
   float m_run = -INFINITY, l_run = 0.0f;
-  unsigned int cnt_tot = 0, cnt_zero = 0;
+  unsigned int cnt_tot = 0, cnt_zero = 0, cnt_nz_fast = 0, n_fast = 0;
 
-  load_regs(tile_of(0));
-  store_lds(0);
-  __syncthreads();
+  // Softmax of a block with no mask and no sink: the max of the raw logits gives
+  // the max of s*c (c > 0), and exp2(s*c - m') is one fma and one exp2.
+  auto softmax_fast = [&](f32x16_t(&sa)[2]) -> float {
+    float mx = fmaxf(sa[0][0], sa[0][1]);
+#pragma unroll
+    for (int j = 2; j < 32; j += 2) mx = fmaxf(fmaxf(mx, sa[j / 16][j % 16]), sa[j / 16][(j + 1) % 16]);
+    mx = halves_max(mx);
+    const float m_new = fmaxf(m_run, mx * c);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float neg = -m_new;
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float pj = __builtin_amdgcn_exp2f(fmaf(sa[j / 16][j % 16], c, neg));
+      sa[j / 16][j % 16] = pj;
+      psum += pj;
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    return alpha;
+  };
+  // Softmax of a block with a causal mask or a sink bias, in place.  `bl_lane` holds the
+  // bias of key (block start + lane); each lane fetches its keys' values by shuffle.
+  auto softmax_general = [&](f32x16_t(&sa)[2], int key0, bool diag, bool has_bias, float bl_lane) -> float {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int kj = slot_key(g, j);
+      float xj = sa[j / 16][j % 16] * c;
+      if (has_bias) xj = fmaf(sa[j / 16][j % 16], c, __shfl(bl_lane, kj) * kLog2e);
+      if (diag && key0 + kj > myrow) xj = -INFINITY;
+      sa[j / 16][j % 16] = xj;
+    }
+    float mx = sa[0][0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) mx = fmaxf(mx, sa[j / 16][j % 16]);
+    mx = halves_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float pj = __builtin_amdgcn_exp2f(sa[j / 16][j % 16] - m_use);
+      sa[j / 16][j % 16] = pj;
+      psum += pj;
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    return alpha;
+  };
+  // P-cast of the 32 probabilities into the FP8 operand (slot order)
+  auto cast_p = [&](f32x16_t(&sa)[2]) {
+    i32x8_t pb;
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+      pb[w] = (int)cast4<kMode>(p, sa[w / 4][4 * (w % 4)], sa[w / 4][4 * (w % 4) + 1],
+                                sa[w / 4][4 * (w % 4) + 2], sa[w / 4][4 * (w % 4) + 3]);
+    return pb;
+  };
+  // underflow counters of a block with a mask or a sink: per key
+  auto count_general = [&](const i32x8_t& pb, int key0, bool has_bias, float bl_lane) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int kj = slot_key(g, j);
+      const bool vis = !kCausal || key0 + kj <= myrow;
+      const bool nonsink = !has_bias || __shfl(bl_lane, kj) == 0.0f;
+      const bool z = (((uint32_t)pb[j / 4] >> (8 * (j % 4))) & 0xFFu) == 0;
+      cnt_tot += (vis && nonsink);
+      cnt_zero += (vis && nonsink && z);
+    }
+  };
+  // non-zero codes of a block where every pair is visible and non-sink: v_msad_u8
+  // sums |(w | 0x80808080) - w| = 0x80 over the bytes where w is non-zero, so the
+  // accumulator holds 128 times the count
+  auto count_fast = [&](const i32x8_t& pb) {
+    ++n_fast;
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+      cnt_nz_fast = __builtin_amdgcn_msad_u8((uint32_t)pb[w] | 0x80808080u, (uint32_t)pb[w], cnt_nz_fast);
+  };
+  // O^T = alpha O^T (alpha == 1 in every lane: exact no-op, skipped), overlapped
+  // with the 16 logit MFMAs of the next block when there is one.
+  auto rescale_and_next = [&](float alpha, bool next, int nbuf) {
+    const bool rs = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
+    if (next && rs) {
+      issue_s(nbuf, sacc);
+#pragma unroll
+      for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * G::kQSteps; ++i) {
+        if (i + 2 < 2 * G::kQSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16 * G::kDTiles / (2 * G::kQSteps), 0);
+      }
+    } else if (next) {
+      issue_s(nbuf, sacc);
+    } else if (rs) {
+#pragma unroll
+      for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+  };
+  // O^T += V8^T P8^T
+  auto accumulate_fp8 = [&](int buf, const i32x8_t& pb) {
+    const uint8_t* vl = lds_v[buf] + li * kVRow;
+    const int xv = SV::key(li);  // rows dt*32 + li share the swizzle key
+    const int vlo = ((2 * g) ^ xv) << 4, vhi = ((2 * g + 1) ^ xv) << 4;
+#pragma unroll
+    for (int dt = 0; dt < G::kDTiles; ++dt) {
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vlo);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vhi);
+      const i32x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, oacc[dt], 0, 0, 0, 0, 0, 0);
+    }
+  };
 
-  for (int it = 0; it < n_it; ++it) {
+  // One step: softmax, P-cast and P.V of block `it` (its logits are in sacc); the
+  // logits of block it+1 are formed into sacc once the P-cast has consumed it.
+  auto step = [&](int it) {
     const int t = tile_of(it);
-    const int cur = it & 1;
-    if (it + 1 < n_it) load_regs(tile_of(it + 1));
-
-    const int key0 = t * kKvBlock;
-    const bool visible = wave_active && (!p.causal || key0 <= wrow0 + kRowsPerWave - 1);
-    if (visible) {
-      const bool diag = p.causal && (key0 + kKvBlock - 1 > wrow0);
-      const bool has_bias = with_bias && lds_bflag[cur] != 0;
-      const float* bl = lds_bias[cur];
-
-      // ---- S^T = K Q^T (two 32-key halves) ----
-      f32x16_t sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-      const uint8_t* kl = lds_k[cur];
-#pragma unroll
-      for (int s = 0; s < G::kQSteps; ++s) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + (kb * 32 + li) * G::kKStride + (s * 16 + g * 8) * 2);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
-        }
-      }
-
-      // ---- logits in log2 units, bias, causal mask ----
-      float x[32];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[kb * 16 + r] = sacc[kb][r] * p.logit_scale;
-      if (has_bias) {
-#pragma unroll
-        for (int j = 0; j < 32; ++j) x[j] += bl[slot_key(g, j)];
-      }
-      if (diag) {
-#pragma unroll
-        for (int j = 0; j < 32; ++j)
-          if (key0 + slot_key(g, j) > myrow) x[j] = -INFINITY;
-      }
-
-      // ---- running max (this block included) ----
-      float mu = x[0];
-#pragma unroll
-      for (int j = 1; j < 32; ++j) mu = fmaxf(mu, x[j]);
-      mu = fmaxf(mu, __shfl_xor(mu, 32));
-      const float m_new = fmaxf(m_run, mu);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-
-      // ---- P = exp2(x - m'), row sum from the un-cast P ----
-      float psum = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        x[j] = __builtin_amdgcn_exp2f(x[j] - m_use);
-        psum += x[j];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-
-      // ---- rescale O when any row's max grew (alpha == 1 is an exact no-op) ----
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int dt = 0; dt < G::kDTiles; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      }
-
+    const int cur = it & 1, nxt = cur ^ 1;
+    const bool more1 = it + 1 < n_it, more2 = it + 2 < n_it;
+    // K of block it+2 replaces K of block it (last read during step it-1); V of
+    // block it+1 replaces V of block it-1.  Both land while this step computes.
+    if (more2) load_k(tile_of(it + 2), cur);
+    if (more1) load_v(tile_of(it + 1), nxt);
+    const float bl_lane = bpend;  // bias of key key0 + lane
+    if (more1) load_bias(tile_of(it + 1));
+    const bool vis = visible(t);
+    const bool vis1 = more1 && visible(tile_of(it + 1));
+    if (vis) {
+      const int key0 = t * kKvBlock;
+      const bool diag = kCausal && (key0 + kKvBlock - 1 > wrow0);
+      const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bl_lane != 0.0f) != 0;
+      const bool fast = !diag && !has_bias;
+      const float alpha = fast ? softmax_fast(sacc) : softmax_general(sacc, key0, diag, has_bias, bl_lane);
       if constexpr (kFp8) {
-        // ---- P-cast: 32 codes = 8 words, slot order ----
-        uint32_t pw[8];
-#pragma unroll
-        for (int w = 0; w < 8; ++w)
-          pw[w] = cast4_fp8(p, x[4 * w], x[4 * w + 1], x[4 * w + 2], x[4 * w + 3]);
+        const i32x8_t pb = cast_p(sacc);
         if constexpr (kStats) {
-          if (!has_bias && !diag) {
-            cnt_tot += 32;
-#pragma unroll
-            for (int w = 0; w < 8; ++w) cnt_zero += zero_bytes(pw[w]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 32; ++j) {
-              const int key = key0 + slot_key(g, j);
-              const bool vis = !p.causal || key <= myrow;
-              const bool nonsink = !has_bias || bl[key - key0] == 0.0f;
-              const bool z = ((pw[j / 4] >> (8 * (j % 4))) & 0xFFu) == 0;
-              cnt_tot += (vis && nonsink);
-              cnt_zero += (vis && nonsink && z);
-            }
-          }
+          if (fast) count_fast(pb);
+          else count_general(pb, key0, has_bias, bl_lane);
         }
-        i32x8_t pb;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) pb[w] = (int)pw[w];
-        // ---- O^T += V8^T P8^T ----
-        const uint8_t* vl = lds_v[cur];
-#pragma unroll
-        for (int dt = 0; dt < G::kDTiles; ++dt) {
-          const uint8_t* src = vl + (dt * 32 + li) * kVStride + g * 32;
-          const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(src);
-          const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(src + 16);
-          const i32x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, oacc[dt], 0, 0, 0, 0, 0, 0);
-        }
+        rescale_and_next(alpha, vis1, nxt);
+        accumulate_fp8(cur, pb);
       } else {
-        // ---- bf16 path: P in bf16, 4 k-steps of 16 slots ----
         uint32_t pw[16];
 #pragma unroll
-        for (int w = 0; w < 16; ++w) pw[w] = cast2_bf16(x[2 * w], x[2 * w + 1]);
+        for (int w = 0; w < 16; ++w) pw[w] = cast2_bf16(sacc[w / 8][(2 * w) % 16], sacc[w / 8][(2 * w + 1) % 16]);
         if constexpr (kStats) {
 #pragma unroll
           for (int j = 0; j < 32; ++j) {
-            const int key = key0 + slot_key(g, j);
-            const bool vis = !p.causal || key <= myrow;
-            const bool nonsink = !has_bias || bl[key - key0] == 0.0f;
+            const int kj = slot_key(g, j);
+            const bool vis_j = !kCausal || key0 + kj <= myrow;
+            const bool nonsink = !has_bias || __shfl(bl_lane, kj) == 0.0f;
             const bool z = ((pw[j / 2] >> (16 * (j % 2))) & 0xFFFFu) == 0;
-            cnt_tot += (vis && nonsink);
-            cnt_zero += (vis && nonsink && z);
+            cnt_tot += (vis_j && nonsink);
+            cnt_zero += (vis_j && nonsink && z);
           }
         }
-        const uint8_t* vl = lds_v[cur];
+        rescale_and_next(alpha, vis1, nxt);
+        const uint8_t* vl = lds_v[cur] + li * kVRow;
+        const int xv = SV::key(li);
 #pragma unroll
         for (int dt = 0; dt < G::kDTiles; ++dt) {
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vl + (dt * 32 + li) * kVStride + (g * 32 + s * 8) * 2);
-            i32x4_t bw = {(int)pw[4 * s], (int)pw[4 * s + 1], (int)pw[4 * s + 2], (int)pw[4 * s + 3]};
-            const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, bw);
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, oacc[dt], 0, 0, 0);
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vl + dt * 32 * kVRow + (((4 * g + s) ^ xv) << 4));
+            const i32x4_t bw = {(int)pw[4 * s], (int)pw[4 * s + 1], (int)pw[4 * s + 2], (int)pw[4 * s + 3]};
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bw), oacc[dt], 0, 0, 0);
           }
         }
       }
+    } else if (vis1) {
+      issue_s(nxt, sacc);
     }
-
-    if (it + 1 < n_it) store_lds(cur ^ 1);
+    wait_loads();
     __syncthreads();
-  }
+  };
+
+  // prologue: K and V of the first block, K of the second; logits of the first block
+  load_k(tile_of(0), 0);
+  load_v(tile_of(0), 0);
+  load_bias(tile_of(0));
+  if (n_it > 1) load_k(tile_of(1), 1);
+  wait_loads();
+  __syncthreads();
+  if (visible(tile_of(0))) issue_s(0, sacc);
+  // step 0 reloads K buffer 0: every wave must have read block 0's K first
+  __syncthreads();
+  for (int it = 0; it < n_it; ++it) step(it);
 
   // ---- epilogue: O = A / (S l) ----
   if (wave_active) {
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.0f / (p.S * l_tot);
+    const float inv = 1.0f / (p.S * halves_sum(l_run));
     float* orow = p.out + (((int64_t)b * p.Hq + h) * p.N + myrow) * D;
 #pragma unroll
     for (int dt = 0; dt < G::kDTiles; ++dt)
@@ -418,7 +541,8 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
       }
   }
   if constexpr (kStats) {
-    unsigned int a = cnt_tot, z = cnt_zero;
+    // fast blocks: every one of the lane's 32 pairs is visible and non-sink
+    unsigned int a = cnt_tot + 32u * n_fast, z = cnt_zero + 32u * n_fast - (cnt_nz_fast >> 7);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       a += __shfl_xor(a, off);
@@ -487,13 +611,31 @@ void launch_prep(const uint16_t* V, void* ws, int64_t n_blocks, hipStream_t stre
   hipLaunchKernelGGL((pcast_prep_v<D, kFp8>), dim3((unsigned)n_blocks), dim3(256), 0, stream, V, ws);
 }
 
-template <int D, bool kFp8>
-void launch_attn(const Params& p, hipStream_t stream) {
-  const dim3 grid((p.N + kBlockRows - 1) / kBlockRows, p.Hq, p.B);
+template <int D, int kMode, bool kCausal>
+void launch_attn3(const Params& p, hipStream_t stream) {
+  const int n_rb = (p.N + kBlockRows - 1) / kBlockRows;
+  const dim3 grid((unsigned)(n_rb * p.Hq * p.B));
   if (p.stats)
-    hipLaunchKernelGGL((pcast_attn_fwd<D, kFp8, true>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((pcast_attn_fwd<D, kMode, kCausal, true>), grid, dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((pcast_attn_fwd<D, kFp8, false>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((pcast_attn_fwd<D, kMode, kCausal, false>), grid, dim3(kThreads), 0, stream, p);
+}
+
+template <int D, int kMode>
+void launch_attn2(const Params& p, int causal, hipStream_t stream) {
+  if (causal) launch_attn3<D, kMode, true>(p, stream);
+  else launch_attn3<D, kMode, false>(p, stream);
+}
+
+template <int D>
+void launch_attn(const Params& p, int mode, int causal, hipStream_t stream) {
+  switch (mode) {
+    case kPow2: launch_attn2<D, kPow2>(p, causal, stream); break;
+    case kPow2Clamp: launch_attn2<D, kPow2Clamp>(p, causal, stream); break;
+    case kMul: launch_attn2<D, kMul>(p, causal, stream); break;
+    case kMulClamp: launch_attn2<D, kMulClamp>(p, causal, stream); break;
+    default: launch_attn2<D, kBf16>(p, causal, stream); break;
+  }
 }
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
@@ -540,7 +682,8 @@ int check_shape(int B, int Hq, int Hkv, int N, int d, float S) {
   if (!std::isfinite(S) || S < 0.0f) return fail(PCAST_EINVAL, "S must be finite and >= 0");
   if (d != 64 && d != 128) return fail(PCAST_ENOTSUP, "d = %d: supported head sizes are 64 and 128", d);
   if (N % kKvBlock != 0) return fail(PCAST_ENOTSUP, "N = %d: must be a multiple of %d", N, kKvBlock);
-  if ((int64_t)B * Hkv * (N / kKvBlock) > (int64_t)INT32_MAX || Hq > 65535 || B > 65535)
+  if ((int64_t)B * Hkv * (N / kKvBlock) > (int64_t)INT32_MAX ||
+      (int64_t)B * Hq * ((N + kBlockRows - 1) / kBlockRows) > (int64_t)INT32_MAX)
     return fail(PCAST_ENOTSUP, "grid too large");
   return PCAST_OK;
 }
@@ -593,19 +736,16 @@ int enqueue_attn(const void* Q, const void* K, const void* ws, const float* bias
   p.out = out;
   p.stats = stats;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N;
-  p.causal = causal; p.order = order;
+  p.order = order;
   p.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)d));
   p.S = fp8 ? S : 1.0f;
   p.inv_S = fp8 ? 1.0f / S : 1.0f;
   // S > 448: P is clamped to 448/S so that S*P stays at or below 448 (exact for S = 2^k;
   // otherwise S*fl(448/S) may exceed 448 by an ulp, which still rounds to 448).
   p.p_clamp = fp8 ? 448.0f / S : 1.0f;
-  p.scale_mode = fp8 ? ((is_pow2(S) ? 0 : 2) | (S > 448.0f ? 1 : 0)) : 0;
-  if (d == 64) {
-    if (fp8) launch_attn<64, true>(p, st); else launch_attn<64, false>(p, st);
-  } else {
-    if (fp8) launch_attn<128, true>(p, st); else launch_attn<128, false>(p, st);
-  }
+  const int mode = !fp8 ? kBf16 : ((is_pow2(S) ? kPow2 : kMul) + (S > 448.0f ? 1 : 0));
+  if (d == 64) launch_attn<64>(p, mode, causal, st);
+  else launch_attn<128>(p, mode, causal, st);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? PCAST_OK : hip_fail(e, "attention kernel launch");
 }
