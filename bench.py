@@ -74,18 +74,18 @@ def cpu_baseline(w, qb, kb, vb, bias, out_rev, out_fwd1, target_s: float, seed: 
         return np.concatenate([np.arange(((b * w.Hq + h) * w.N + r * 64),
                                          ((b * w.Hq + h) * w.N + r * 64) + 64) for b, h, r in blocks])
 
-    # calibrate on two blocks, then size the sample to about target_s seconds
-    calib = [all_blocks[i] for i in rng.choice(len(all_blocks), 2, replace=False)]
-    t0 = time.perf_counter()
-    core.rows(qb, kb, vb, bias, w.causal, 256.0, 1, "kernel", row_ids=rows_of(calib), nthreads=nthreads)
-    rate = causal_row_flops(rows_of(calib), w.N, w.d, w.causal) / max(time.perf_counter() - t0, 1e-3)
-    per_block = w.flops / len(all_blocks)
-    n = int(min(len(all_blocks), max(4, target_s * rate / per_block)))
-    blocks = [all_blocks[i] for i in sorted(rng.choice(len(all_blocks), n, replace=False))]
-    ids = rows_of(blocks)
-    t0 = time.perf_counter()
-    ref = core.rows(qb, kb, vb, bias, w.causal, 256.0, 1, "kernel", row_ids=ids, nthreads=nthreads)
-    dt = time.perf_counter() - t0
+    # grow a random block sample until one oracle call takes about target_s seconds
+    order_ = rng.permutation(len(all_blocks))
+    n = 8
+    while True:
+        blocks = [all_blocks[i] for i in sorted(order_[:n])]
+        ids = rows_of(blocks)
+        t0 = time.perf_counter()
+        ref = core.rows(qb, kb, vb, bias, w.causal, 256.0, 1, "kernel", row_ids=ids, nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * target_s or n >= len(all_blocks):
+            break
+        n = min(len(all_blocks), int(n * min(16.0, max(2.0, target_s / max(dt, 1e-3)))))
     flops = causal_row_flops(ids, w.N, w.d, w.causal)
     o1 = ref["o1"]
     mse = {}
@@ -110,7 +110,19 @@ def main() -> int:
     ap.add_argument("--no-stats", action="store_true", help="time without the underflow counters")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes, 3 times (scale for "
+                         "the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        x = torch.empty(args.calibrate_copy, dtype=torch.uint8, device="cuda:0").fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.calibrate_copy}))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
