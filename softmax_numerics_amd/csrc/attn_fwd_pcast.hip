@@ -77,7 +77,6 @@ struct Swizzle {
   static constexpr int kChunks = kRowBytes / 16;
   static constexpr int kRowsPerWindow = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
   __device__ static int key(int row) { return (row / kRowsPerWindow) % kChunks; }
-  __device__ static int offset(int row, int chunk) { return row * kRowBytes + ((chunk ^ key(row)) << 4); }
 };
 
 // ---------------------------------------------------------------------------
@@ -193,6 +192,11 @@ __device__ inline void load_to_lds16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)lds, 16, 0, 0);
 }
 
+// 4 bytes per lane from global memory straight into LDS (lane i writes lds + 4*i).
+__device__ inline void load_to_lds4(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)lds, 4, 0, 0);
+}
+
 // max over the two 32-lane halves (lane l and lane l ^ 32 hold the same query row)
 __device__ inline float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
   constexpr int kEsize = kFp8 ? 1 : 2;                      // bytes per V operand element
   constexpr int kKRow = D * 2;                              // bytes per K row
   constexpr int kVRow = kKvBlock * kEsize;                  // bytes per V^T row (64 keys)
-  constexpr int kKTile = kKvBlock * kKRow;                  // bytes of one K block
+  constexpr int kKTile = kKvBlock * kKRow;                  // bytes of one K block in HBM
   constexpr int kVTile = D * kVRow;                         // bytes of one V operand block
   using SK = Swizzle<kKRow>;
   using SV = Swizzle<kVRow>;
@@ -239,6 +243,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kKTile];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][kVTile];
+  __shared__ __attribute__((aligned(16))) float lds_bias[2][kKvBlock];  // bias of the staged key block
   __shared__ unsigned int lds_cnt[2][2];
 
   const int tid = threadIdx.x;
@@ -301,6 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i)
       load_to_lds16(vs + vsrc[i], &lds_v[buf][(wave * kVLoads + i) * 1024]);
+    if (with_bias && wave == 0) load_to_lds4(p.bias + t * kKvBlock + lane, &lds_bias[buf][0]);
   };
   auto load_bias = [&](int t) {
     if (with_bias) bpend = p.bias[t * kKvBlock + lane];
@@ -320,6 +326,16 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
     }
   };
 
+  // the 32-key half kb of the same product: 8 MFMAs into one accumulator
+  auto issue_s_half = [&](int buf, f32x16_t& out, int kb) {
+    const uint8_t* kl = lds_k[buf] + (kb * 32 + li) * kKRow;
+#pragma unroll
+    for (int s = 0; s < G::kQSteps; ++s) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + (((2 * s + g) ^ xk) << 4));
+      out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16_t{} : out, 0, 0, 0);
+    }
+  };
+
   f32x16_t oacc[G::kDTiles];
 #pragma unroll
   for (int dt = 0; dt < G::kDTiles; ++dt)
@@ -331,33 +347,50 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
 
   // Softmax of a block with no mask and no sink: the max of the raw logits gives
   // the max of s*c (c > 0), and exp2(s*c - m') is one fma and one exp2.
-  auto softmax_fast = [&](f32x16_t(&sa)[2]) -> float {
-    float mx = fmaxf(sa[0][0], sa[0][1]);
+  auto block_max = [&](f32x16_t(&sa)[2]) -> float {
+    // four independent max3 chains, then a tree
+    float m4[4];
 #pragma unroll
-    for (int j = 2; j < 32; j += 2) mx = fmaxf(fmaxf(mx, sa[j / 16][j % 16]), sa[j / 16][(j + 1) % 16]);
-    mx = halves_max(mx);
+    for (int q = 0; q < 4; ++q) {
+      m4[q] = fmaxf(sa[q / 2][(q % 2) * 8], sa[q / 2][(q % 2) * 8 + 1]);
+#pragma unroll
+      for (int r = 2; r < 8; r += 2)
+        m4[q] = fmaxf(fmaxf(m4[q], sa[q / 2][(q % 2) * 8 + r]), sa[q / 2][(q % 2) * 8 + r + 1]);
+    }
+    return halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+  };
+  auto softmax_fast = [&](f32x16_t(&sa)[2]) -> float {
+    const float mx = block_max(sa);
     const float m_new = fmaxf(m_run, mx * c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     const float neg = -m_new;
-    float psum = 0.0f;
+    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       const float pj = __builtin_amdgcn_exp2f(fmaf(sa[j / 16][j % 16], c, neg));
       sa[j / 16][j % 16] = pj;
-      psum += pj;
+      ps[j % 4] += pj;
     }
-    l_run = l_run * alpha + psum;
+    l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
     m_run = m_new;
     return alpha;
   };
-  // Softmax of a block with a causal mask or a sink bias, in place.  `bl_lane` holds the
-  // bias of key (block start + lane); each lane fetches its keys' values by shuffle.
-  auto softmax_general = [&](f32x16_t(&sa)[2], int key0, bool diag, bool has_bias, float bl_lane) -> float {
+  // bias of this lane's 32 keys from the staged block: slots 4q..4q+3 are 4 consecutive keys
+  auto lane_bias = [&](int buf, float (&bk)[32]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(&lds_bias[buf][slot_key(g, 4 * q)]);
+      bk[4 * q] = v.x; bk[4 * q + 1] = v.y; bk[4 * q + 2] = v.z; bk[4 * q + 3] = v.w;
+    }
+  };
+  // Softmax of a block with a causal mask or a sink bias, in place.
+  auto softmax_general = [&](f32x16_t(&sa)[2], int key0, bool diag, bool has_bias, int buf) -> float {
+    float bk[32];
+    if (has_bias) lane_bias(buf, bk);
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       const int kj = slot_key(g, j);
-      float xj = sa[j / 16][j % 16] * c;
-      if (has_bias) xj = fmaf(sa[j / 16][j % 16], c, __shfl(bl_lane, kj) * kLog2e);
+      float xj = has_bias ? fmaf(sa[j / 16][j % 16], c, bk[j] * kLog2e) : sa[j / 16][j % 16] * c;
       if (diag && key0 + kj > myrow) xj = -INFINITY;
       sa[j / 16][j % 16] = xj;
     }
@@ -368,14 +401,14 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float psum = 0.0f;
+    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       const float pj = __builtin_amdgcn_exp2f(sa[j / 16][j % 16] - m_use);
       sa[j / 16][j % 16] = pj;
-      psum += pj;
+      ps[j % 4] += pj;
     }
-    l_run = l_run * alpha + psum;
+    l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
     m_run = m_new;
     return alpha;
   };
@@ -389,12 +422,14 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
     return pb;
   };
   // underflow counters of a block with a mask or a sink: per key
-  auto count_general = [&](const i32x8_t& pb, int key0, bool has_bias, float bl_lane) {
+  auto count_general = [&](const i32x8_t& pb, int key0, bool has_bias, int buf) {
+    float bk[32];
+    if (has_bias) lane_bias(buf, bk);
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       const int kj = slot_key(g, j);
       const bool vis = !kCausal || key0 + kj <= myrow;
-      const bool nonsink = !has_bias || __shfl(bl_lane, kj) == 0.0f;
+      const bool nonsink = !has_bias || bk[j] == 0.0f;
       const bool z = (((uint32_t)pb[j / 4] >> (8 * (j % 4))) & 0xFFu) == 0;
       cnt_tot += (vis && nonsink);
       cnt_zero += (vis && nonsink && z);
@@ -468,12 +503,66 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
       const bool diag = kCausal && (key0 + kKvBlock - 1 > wrow0);
       const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bl_lane != 0.0f) != 0;
       const bool fast = !diag && !has_bias;
-      const float alpha = fast ? softmax_fast(sacc) : softmax_general(sacc, key0, diag, has_bias, bl_lane);
+      if (kFp8 && fast && vis1) {
+        // Pipelined by key halves, in place: once the first half's probabilities are
+        // cast, its registers take the next block's logits for keys 0..31 while the
+        // second half is exponentiated; then keys 32..63 of the next block while O is
+        // rescaled and the codes counted.
+        const float mx = block_max(sacc);
+        const float m_new = fmaxf(m_run, mx * c);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float neg = -m_new;
+        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        i32x8_t pb;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pj = __builtin_amdgcn_exp2f(fmaf(sacc[0][r], c, neg));
+          sacc[0][r] = pj;
+          ps[r % 4] += pj;
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          pb[w] = (int)cast4<kMode>(p, sacc[0][4 * w], sacc[0][4 * w + 1], sacc[0][4 * w + 2], sacc[0][4 * w + 3]);
+        issue_s_half(nxt, sacc[0], 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pj = __builtin_amdgcn_exp2f(fmaf(sacc[1][r], c, neg));
+          sacc[1][r] = pj;
+          ps[r % 4] += pj;
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          pb[4 + w] = (int)cast4<kMode>(p, sacc[1][4 * w], sacc[1][4 * w + 1], sacc[1][4 * w + 2], sacc[1][4 * w + 3]);
+        l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+        m_run = m_new;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < G::kQSteps; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i + 2 < G::kQSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 56 / G::kQSteps, 0);
+        }
+        issue_s_half(nxt, sacc[1], 1);
+#pragma unroll
+        for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;  // alpha == 1: exact no-op
+        if constexpr (kStats) count_fast(pb);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < G::kQSteps; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i + 2 < G::kQSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, (16 * G::kDTiles + (kStats ? 16 : 0)) / G::kQSteps, 0);
+        }
+        accumulate_fp8(cur, pb);
+      } else {
+      const float alpha = fast ? softmax_fast(sacc) : softmax_general(sacc, key0, diag, has_bias, cur);
       if constexpr (kFp8) {
         const i32x8_t pb = cast_p(sacc);
         if constexpr (kStats) {
           if (fast) count_fast(pb);
-          else count_general(pb, key0, has_bias, bl_lane);
+          else count_general(pb, key0, has_bias, cur);
         }
         rescale_and_next(alpha, vis1, nxt);
         accumulate_fp8(cur, pb);
@@ -486,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
           for (int j = 0; j < 32; ++j) {
             const int kj = slot_key(g, j);
             const bool vis_j = !kCausal || key0 + kj <= myrow;
-            const bool nonsink = !has_bias || __shfl(bl_lane, kj) == 0.0f;
+            const bool nonsink = !has_bias || lds_bias[cur][kj] == 0.0f;
             const bool z = ((pw[j / 2] >> (16 * (j % 2))) & 0xFFFFu) == 0;
             cnt_tot += (vis_j && nonsink);
             cnt_zero += (vis_j && nonsink && z);
@@ -504,6 +593,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
             oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bw), oacc[dt], 0, 0, 0);
           }
         }
+      }
       }
     } else if (vis1) {
       issue_s(nxt, sacc);
