@@ -152,13 +152,6 @@ enum PMode : int {
   kBf16 = 4,       // no P-cast: P and V in bf16
 };
 
-// Non-zero E4M3 codes among the 4 bytes of w.  Codes of P*S >= 0 lie in
-// [0x00, 0x7E], so adding 0x7F sets bit 7 of a byte exactly when it is non-zero
-// and never carries into the next byte.
-__device__ inline uint32_t nonzero_codes(uint32_t w, uint32_t acc) {
-  return __builtin_popcount((w + 0x7F7F7F7Fu) & 0x80808080u) + acc;
-}
-
 // Convert 4 probabilities to 4 E4M3 codes in one word.
 template <int kMode>
 __device__ inline uint32_t cast4(const Params& p, float a, float b, float c, float d) {
@@ -167,12 +160,13 @@ __device__ inline uint32_t cast4(const Params& p, float a, float b, float c, flo
     a = fminf(a, lim); b = fminf(b, lim); c = fminf(c, lim); d = fminf(d, lim);
   }
   if constexpr (kMode == kPow2 || kMode == kPow2Clamp) {
-    s16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2_t{0, 0}, a, b, p.inv_S, false);
+    // both halves of the word are written; its old contents (a's bits) are never read
+    s16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(s16x2_t, a), a, b, p.inv_S, false);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, p.inv_S, true);
     return __builtin_bit_cast(uint32_t, r);
   } else {
     const float S = p.S;
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a * S, b * S, 0, false);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a * S, b * S, __builtin_bit_cast(int, a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c * S, d * S, w, true);
     return (uint32_t)w;
   }
@@ -225,26 +219,302 @@ __device__ inline void decode_block(int lin, int total, int n_rb, int Hq, bool c
   h = hh % Hq;
 }
 
-template <int D, int kMode, bool kCausal, bool kStats>
-__global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
+template <int V>
+struct BufIndex {
+  static constexpr int value = V;
+};
+
+// ---------------------------------------------------------------------------
+// Attention kernel for the path without the P-cast (S = 0): P and V in bf16, P.V
+// on v_mfma_f32_32x32x16_bf16.  Same tiling and staging as the FP8 kernel below,
+// one step per block without its deferral.
+// ---------------------------------------------------------------------------
+template <int D, bool kCausal, bool kStats>
+__global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params p) {
   using G = Geometry<D>;
-  constexpr bool kFp8 = kMode != kBf16;
-  constexpr int kEsize = kFp8 ? 1 : 2;                      // bytes per V operand element
-  constexpr int kKRow = D * 2;                              // bytes per K row
-  constexpr int kVRow = kKvBlock * kEsize;                  // bytes per V^T row (64 keys)
-  constexpr int kKTile = kKvBlock * kKRow;                  // bytes of one K block in HBM
-  constexpr int kVTile = D * kVRow;                         // bytes of one V operand block
+  constexpr int kKRow = D * 2;                // bytes per K row
+  constexpr int kVRow = kKvBlock * 2;         // bytes per V^T row (64 bf16 values)
+  constexpr int kKTile = kKvBlock * kKRow;    // bytes of one K block
+  constexpr int kVTile = D * kVRow;           // bytes of one V operand block
   using SK = Swizzle<kKRow>;
   using SV = Swizzle<kVRow>;
-  // direct global -> LDS loads (64 lanes x 16 bytes = 1 KB each) per wave and block
-  constexpr int kKLoads = kKTile / (1024 * kWaves);
+  constexpr int kKLoads = kKTile / (1024 * kWaves);  // 1 KB direct loads per wave and block
   constexpr int kVLoads = kVTile / (1024 * kWaves);
   static_assert(kKTile % (1024 * kWaves) == 0 && kVTile % (1024 * kWaves) == 0, "staging split");
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kKTile];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][kVTile];
-  __shared__ __attribute__((aligned(16))) float lds_bias[2][kKvBlock];  // bias of the staged key block
+  // one LDS object per staging buffer (see the FP8 kernel)
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[kKTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[kKTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[kVTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[kVTile];
+  __shared__ __attribute__((aligned(16))) float lds_b0[kKvBlock];
+  __shared__ __attribute__((aligned(16))) float lds_b1[kKvBlock];
   __shared__ unsigned int lds_cnt[2][2];
+  auto kbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_k1 : lds_k0; };
+  auto vbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_v1 : lds_v0; };
+  auto bbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_b1 : lds_b0; };
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64;
+  const int g = lane / 32, li = lane % 32;
+  const int n_rb = (p.N + kBlockRows - 1) / kBlockRows;
+  int b, h, rb;
+  decode_block(blockIdx.x, n_rb * p.Hq * p.B, n_rb, p.Hq, kCausal, b, h, rb);
+  const int hk = h / (p.Hq / p.Hkv);
+  const int n_tiles = p.N / kKvBlock;
+  const int row0 = rb * kBlockRows;
+  const int wrow0 = row0 + wave * kRowsPerWave;  // first row of this wave
+  const int myrow = wrow0 + li;
+  const bool wave_active = wrow0 < p.N;
+  const int t_last = kCausal ? min((row0 + kBlockRows - 1) / kKvBlock, n_tiles - 1) : n_tiles - 1;
+  const int n_it = t_last + 1;
+  const float c = p.logit_scale;
+
+  if (kStats && tid < 4) lds_cnt[tid / 2][tid % 2] = 0;
+
+  // Q operand (B of S^T = K Q^T): lane holds Q[myrow][s*16 + g*8 .. +8) for each step s.
+  bf16x8_t qf[G::kQSteps];
+  if (wave_active) {
+    const uint16_t* qrow = p.q + (((int64_t)b * p.Hq + h) * p.N + myrow) * D + g * 8;
+#pragma unroll
+    for (int s = 0; s < G::kQSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + s * 16);
+  }
+
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k + ((int64_t)b * p.Hkv + hk) * p.N * D);
+  const uint8_t* vbase = static_cast<const uint8_t*>(p.vop) + ((int64_t)b * p.Hkv + hk) * (int64_t)n_tiles * kVTile;
+  int ksrc[kKLoads], vsrc[kVLoads];
+#pragma unroll
+  for (int i = 0; i < kKLoads; ++i) {
+    const int pos = (wave * kKLoads + i) * 64 + lane, r = pos / SK::kChunks;
+    ksrc[i] = r * kKRow + (((pos % SK::kChunks) ^ SK::key(r)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < kVLoads; ++i) {
+    const int pos = (wave * kVLoads + i) * 64 + lane, r = pos / SV::kChunks;
+    vsrc[i] = r * kVRow + (((pos % SV::kChunks) ^ SV::key(r)) << 4);
+  }
+  const bool with_bias = p.bias != nullptr;
+  auto tile_of = [&](int it) __attribute__((always_inline)) { return p.order ? (t_last - it) : it; };
+  auto visible = [&](int t) __attribute__((always_inline)) {
+    return wave_active && (!kCausal || t * kKvBlock <= wrow0 + kRowsPerWave - 1);
+  };
+  auto load_k = [&](int t, int buf) __attribute__((always_inline)) {
+    const uint8_t* ks = kbase + t * kKTile;
+#pragma unroll
+    for (int i = 0; i < kKLoads; ++i) load_to_lds16(ks + ksrc[i], kbuf(buf) + (wave * kKLoads + i) * 1024);
+  };
+  // V of a block and its bias travel together
+  auto load_v = [&](int t, int buf) __attribute__((always_inline)) {
+    const uint8_t* vs = vbase + t * kVTile;
+#pragma unroll
+    for (int i = 0; i < kVLoads; ++i) load_to_lds16(vs + vsrc[i], vbuf(buf) + (wave * kVLoads + i) * 1024);
+    if (with_bias && wave == 0) load_to_lds4(p.bias + t * kKvBlock + lane, bbuf(buf));
+  };
+  auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  const int xk = SK::key(li);  // rows li and li + 32 share the swizzle key
+  auto issue_s = [&](int buf, f32x16_t(&sa)[2]) __attribute__((always_inline)) {
+    const uint8_t* kl = kbuf(buf) + li * kKRow;
+#pragma unroll
+    for (int s = 0; s < G::kQSteps; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + kb * 32 * kKRow + (((2 * s + g) ^ xk) << 4));
+        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16_t{} : sa[kb], 0, 0, 0);
+      }
+    }
+  };
+  f32x16_t oacc[G::kDTiles];
+#pragma unroll
+  for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+  f32x16_t sacc[2];  // logits (then probabilities) of the block being processed
+  float m_run = -INFINITY, l_run = 0.0f;
+  unsigned int cnt_tot = 0, cnt_zero = 0;
+
+  // Softmax of a block, in place, with the causal mask and the bias where present.
+  auto softmax = [&](f32x16_t(&sa)[2], int key0, bool diag, bool has_bias, int buf)
+      __attribute__((always_inline)) -> float {
+    float bk[32];
+    if (has_bias) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(bbuf(buf) + slot_key(g, 4 * q));
+        bk[4 * q] = v.x; bk[4 * q + 1] = v.y; bk[4 * q + 2] = v.z; bk[4 * q + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int kj = slot_key(g, j);
+      float xj = has_bias ? fmaf(sa[j / 16][j % 16], c, bk[j] * kLog2e) : sa[j / 16][j % 16] * c;
+      if (diag && key0 + kj > myrow) xj = -INFINITY;
+      sa[j / 16][j % 16] = xj;
+    }
+    float mx = sa[0][0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) mx = fmaxf(mx, sa[j / 16][j % 16]);
+    mx = halves_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float pj = __builtin_amdgcn_exp2f(sa[j / 16][j % 16] - m_use);
+      sa[j / 16][j % 16] = pj;
+      ps[j % 4] += pj;
+    }
+    l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    m_run = m_new;
+    if constexpr (kStats) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const int kj = slot_key(g, j);
+        const bool vis_j = !kCausal || key0 + kj <= myrow;
+        const bool nonsink = !has_bias || bk[j] == 0.0f;
+        // the bf16 code of P is zero only when P itself rounds to zero
+        const bool z = (__builtin_bit_cast(uint16_t, (__bf16)sa[j / 16][j % 16]) & 0x7FFFu) == 0;
+        cnt_tot += (vis_j && nonsink);
+        cnt_zero += (vis_j && nonsink && z);
+      }
+    }
+    return alpha;
+  };
+
+  auto step = [&](int it, auto cur_c) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
+    const int t = tile_of(it);
+    // K of block it+2 replaces K of block it (read during step it-1); V and bias of
+    // block it+1 replace those of block it-1.  Both land while this step computes.
+    if (it + 2 < n_it) load_k(tile_of(it + 2), cur);
+    if (it + 1 < n_it) load_v(tile_of(it + 1), nxt);
+    const bool vis = visible(t);
+    const bool vis1 = it + 1 < n_it && visible(tile_of(it + 1));
+    if (vis) {
+      const int key0 = t * kKvBlock;
+      const bool diag = kCausal && (key0 + kKvBlock - 1 > wrow0);
+      const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bbuf(cur)[lane] != 0.0f) != 0;
+      const float alpha = softmax(sacc, key0, diag, has_bias, cur);
+      uint32_t pw[16];
+#pragma unroll
+      for (int w = 0; w < 16; ++w) pw[w] = cast2_bf16(sacc[w / 8][(2 * w) % 16], sacc[w / 8][(2 * w + 1) % 16]);
+      // O^T = alpha O^T, skipped when alpha == 1 in every lane (an exact no-op)
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      }
+      if (vis1) issue_s(nxt, sacc);
+      // O^T += V^T P^T: four k-steps of 16 keys per 32-column tile
+      const uint8_t* vl = vbuf(cur) + li * kVRow;
+      const int xv = SV::key(li);
+#pragma unroll
+      for (int dt = 0; dt < G::kDTiles; ++dt) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vl + dt * 32 * kVRow + (((4 * g + s) ^ xv) << 4));
+          const i32x4_t bw = {(int)pw[4 * s], (int)pw[4 * s + 1], (int)pw[4 * s + 2], (int)pw[4 * s + 3]};
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bw), oacc[dt], 0, 0, 0);
+        }
+      }
+    } else if (vis1) {
+      issue_s(nxt, sacc);
+    }
+    wait_loads();
+    __syncthreads();
+  };
+
+  // prologue: K, V and bias of the first block, K of the second; logits of the first block
+  load_k(tile_of(0), 0);
+  load_v(tile_of(0), 0);
+  if (n_it > 1) load_k(tile_of(1), 1);
+  wait_loads();
+  __syncthreads();
+  if (visible(tile_of(0))) issue_s(0, sacc);
+  // step 0 reloads K buffer 0: every wave must have read block 0's K first
+  __syncthreads();
+  for (int it = 0; it < n_it; it += 2) {
+    step(it, BufIndex<0>{});
+    if (it + 1 < n_it) step(it + 1, BufIndex<1>{});
+  }
+
+  // ---- epilogue: O = A / l (S = 1 on this path) ----
+  if (wave_active) {
+    const float inv = 1.0f / (p.S * halves_sum(l_run));
+    float* orow = p.out + (((int64_t)b * p.Hq + h) * p.N + myrow) * D;
+#pragma unroll
+    for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float4 v;
+        v.x = oacc[dt][r4 * 4 + 0] * inv;
+        v.y = oacc[dt][r4 * 4 + 1] * inv;
+        v.z = oacc[dt][r4 * 4 + 2] * inv;
+        v.w = oacc[dt][r4 * 4 + 3] * inv;
+        *reinterpret_cast<float4*>(orow + dt * 32 + r4 * 8 + g * 4) = v;
+      }
+  }
+  if constexpr (kStats) {
+    unsigned int a = cnt_tot, z = cnt_zero;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      a += __shfl_xor(a, off);
+      z += __shfl_xor(z, off);
+    }
+    if (lane == 0 && wave_active) {
+      atomicAdd(&lds_cnt[wave / 2][0], a);
+      atomicAdd(&lds_cnt[wave / 2][1], z);
+    }
+    __syncthreads();
+    if (tid < 2) {
+      const int r64 = row0 / kKvBlock + tid;  // 64-row block index
+      if (r64 * kKvBlock < p.N) {
+        unsigned long long* st = p.stats + 2 * (((int64_t)b * p.Hq + h) * (p.N / kKvBlock) + r64);
+        st[0] = lds_cnt[tid][0];
+        st[1] = lds_cnt[tid][1];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention kernel for the FP8 P-cast modes, software-pipelined by one block:
+// step j exponentiates and casts block j (its logits sit in one of two logit
+// buffers) while the same wave's MFMAs form block j+1's logits in the other
+// buffer and accumulate block j-1's P.V, deferred by one step (the rescale by
+// block j-1's alpha comes first).  The three streams are independent, so the
+// MFMAs interleave with the exponentials inside one basic block.
+// ---------------------------------------------------------------------------
+template <int D, int kMode, bool kCausal, bool kStats>
+__global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p) {
+  static_assert(kMode != kBf16, "FP8 modes only");
+  using G = Geometry<D>;
+  constexpr int kKRow = D * 2;                // bytes per K row
+  constexpr int kVRow = kKvBlock;             // bytes per V^T row (64 E4M3 codes)
+  constexpr int kKTile = kKvBlock * kKRow;    // bytes of one K block
+  constexpr int kVTile = D * kVRow;           // bytes of one V operand block
+  using SK = Swizzle<kKRow>;
+  using SV = Swizzle<kVRow>;
+  constexpr int kKLoads = kKTile / (1024 * kWaves);  // 1 KB direct loads per wave and block
+  constexpr int kVLoads = kVTile / (1024 * kWaves);
+  static_assert(kKTile % (1024 * kWaves) == 0 && kVTile % (1024 * kWaves) == 0, "staging split");
+
+  // Each staging buffer is its own LDS object, so the compiler can tell that the
+  // direct loads into one buffer never alias reads of the other and does not make
+  // those reads wait for the loads in flight.
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[kKTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[kKTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[kVTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[kVTile];
+  __shared__ __attribute__((aligned(16))) float lds_b0[kKvBlock];
+  __shared__ __attribute__((aligned(16))) float lds_b1[kKvBlock];
+  __shared__ unsigned int lds_cnt[2][2];
+  // buffer indices are compile-time constants wherever these are called
+  auto kbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_k1 : lds_k0; };
+  auto vbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_v1 : lds_v0; };
+  auto bbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_b1 : lds_b0; };
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
@@ -290,32 +560,29 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
     vsrc[i] = r * kVRow + (((pos % SV::kChunks) ^ SV::key(r)) << 4);
   }
   const bool with_bias = p.bias != nullptr;
-  float bpend = 0.0f;  // bias of key (block start + lane) for the next step's block
-  auto tile_of = [&](int it) { return p.order ? (t_last - it) : it; };
-  auto visible = [&](int t) {
+  auto tile_of = [&](int it) __attribute__((always_inline)) { return p.order ? (t_last - it) : it; };
+  auto visible = [&](int t) __attribute__((always_inline)) {
     return wave_active && (!kCausal || t * kKvBlock <= wrow0 + kRowsPerWave - 1);
   };
-  auto load_k = [&](int t, int buf) {
+  auto load_k = [&](int t, int buf) __attribute__((always_inline)) {
     const uint8_t* ks = kbase + t * kKTile;
 #pragma unroll
-    for (int i = 0; i < kKLoads; ++i)
-      load_to_lds16(ks + ksrc[i], &lds_k[buf][(wave * kKLoads + i) * 1024]);
+    for (int i = 0; i < kKLoads; ++i) load_to_lds16(ks + ksrc[i], kbuf(buf) + (wave * kKLoads + i) * 1024);
   };
-  auto load_v = [&](int t, int buf) {
+  auto load_v = [&](int t, int buf) __attribute__((always_inline)) {
     const uint8_t* vs = vbase + t * kVTile;
 #pragma unroll
-    for (int i = 0; i < kVLoads; ++i)
-      load_to_lds16(vs + vsrc[i], &lds_v[buf][(wave * kVLoads + i) * 1024]);
-    if (with_bias && wave == 0) load_to_lds4(p.bias + t * kKvBlock + lane, &lds_bias[buf][0]);
+    for (int i = 0; i < kVLoads; ++i) load_to_lds16(vs + vsrc[i], vbuf(buf) + (wave * kVLoads + i) * 1024);
   };
-  auto load_bias = [&](int t) {
-    if (with_bias) bpend = p.bias[t * kKvBlock + lane];
+  auto load_b = [&](int t, int buf) __attribute__((always_inline)) {
+    if (with_bias && wave == 0) load_to_lds4(p.bias + t * kKvBlock + lane, bbuf(buf));
   };
-  auto wait_loads = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-  // S^T = K Q^T for the key block staged in K buffer `buf` (two 32-key halves, fp32 accumulation)
+  auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  // S^T = K Q^T for the key block in K buffer `buf`: two 32-key halves, fp32 accumulation
   const int xk = SK::key(li);  // rows li and li + 32 share the swizzle key
-  auto issue_s = [&](int buf, f32x16_t(&sa)[2]) {
-    const uint8_t* kl = lds_k[buf] + li * kKRow;
+  auto issue_s = [&](int buf, f32x16_t(&sa)[2]) __attribute__((always_inline)) {
+    const uint8_t* kl = kbuf(buf) + li * kKRow;
 #pragma unroll
     for (int s = 0; s < G::kQSteps; ++s) {
 #pragma unroll
@@ -325,30 +592,52 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
       }
     }
   };
-
-  // the 32-key half kb of the same product: 8 MFMAs into one accumulator
-  auto issue_s_half = [&](int buf, f32x16_t& out, int kb) {
-    const uint8_t* kl = lds_k[buf] + (kb * 32 + li) * kKRow;
+  // the 32-key half kb of the same product: kQSteps MFMAs into one accumulator
+  auto issue_s_half = [&](int buf, f32x16_t& out, int kb) __attribute__((always_inline)) {
+    const uint8_t* kl = kbuf(buf) + (kb * 32 + li) * kKRow;
 #pragma unroll
     for (int s = 0; s < G::kQSteps; ++s) {
       const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + (((2 * s + g) ^ xk) << 4));
       out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16_t{} : out, 0, 0, 0);
     }
   };
-
   f32x16_t oacc[G::kDTiles];
 #pragma unroll
   for (int dt = 0; dt < G::kDTiles; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
-  f32x16_t sacc[2];  // logits (then probabilities) of the block being processed
+  // O^T += V8^T P8^T for the V block in V buffer `buf`
+  auto accumulate = [&](int buf, const i32x8_t& pb) __attribute__((always_inline)) {
+    const uint8_t* vl = vbuf(buf) + li * kVRow;
+    const int xv = SV::key(li);  // rows dt*32 + li share the swizzle key
+    const int vlo = ((2 * g) ^ xv) << 4, vhi = ((2 * g + 1) ^ xv) << 4;
+#pragma unroll
+    for (int dt = 0; dt < G::kDTiles; ++dt) {
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vlo);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vhi);
+      const i32x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, oacc[dt], 0, 0, 0, 0, 0, 0);
+    }
+  };
+  auto rescale = [&](float alpha) __attribute__((always_inline)) {
+    // alpha == 1 in every lane: an exact no-op, skipped
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+  };
+
+  f32x16_t sacc[2];  // logits of the block being processed (two 32-key halves)
+  i32x8_t pbuf[2];   // E4M3 codes of blocks of even and odd step index
   float m_run = -INFINITY, l_run = 0.0f;
+  float alpha_pend = 1.0f;  // rescale owed before the pending P.V
+  bool pend = false;        // block j-1's P.V is still to be accumulated
   unsigned int cnt_tot = 0, cnt_zero = 0, cnt_nz_fast = 0, n_fast = 0;
 
-  // Softmax of a block with no mask and no sink: the max of the raw logits gives
-  // the max of s*c (c > 0), and exp2(s*c - m') is one fma and one exp2.
-  auto block_max = [&](f32x16_t(&sa)[2]) -> float {
-    // four independent max3 chains, then a tree
+  // max of a block's raw logits (four max3 chains, then a tree; both lane halves)
+  auto block_max = [&](f32x16_t(&sa)[2]) __attribute__((always_inline)) -> float {
     float m4[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -359,7 +648,9 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
     }
     return halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
   };
-  auto softmax_fast = [&](f32x16_t(&sa)[2]) -> float {
+  // Softmax and P-cast of a block with no mask and no sink: the max of the raw
+  // logits gives the max of s*c (c > 0), and exp2(s*c - m') is one fma and one exp2.
+  auto softmax_fast = [&](f32x16_t(&sa)[2], i32x8_t& pb) __attribute__((always_inline)) -> float {
     const float mx = block_max(sa);
     const float m_new = fmaxf(m_run, mx * c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -373,18 +664,23 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
     }
     l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
     m_run = m_new;
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+      pb[w] = (int)cast4<kMode>(p, sa[w / 4][4 * (w % 4)], sa[w / 4][4 * (w % 4) + 1], sa[w / 4][4 * (w % 4) + 2],
+                                sa[w / 4][4 * (w % 4) + 3]);
     return alpha;
   };
   // bias of this lane's 32 keys from the staged block: slots 4q..4q+3 are 4 consecutive keys
-  auto lane_bias = [&](int buf, float (&bk)[32]) {
+  auto lane_bias = [&](int buf, float (&bk)[32]) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const float4 v = *reinterpret_cast<const float4*>(&lds_bias[buf][slot_key(g, 4 * q)]);
+      const float4 v = *reinterpret_cast<const float4*>(bbuf(buf) + slot_key(g, 4 * q));
       bk[4 * q] = v.x; bk[4 * q + 1] = v.y; bk[4 * q + 2] = v.z; bk[4 * q + 3] = v.w;
     }
   };
-  // Softmax of a block with a causal mask or a sink bias, in place.
-  auto softmax_general = [&](f32x16_t(&sa)[2], int key0, bool diag, bool has_bias, int buf) -> float {
+  // Softmax and P-cast of a block with a causal mask or a sink bias, in place.
+  auto softmax_general = [&](f32x16_t(&sa)[2], i32x8_t& pb, int key0, bool diag, bool has_bias, int buf)
+      __attribute__((always_inline)) -> float {
     float bk[32];
     if (has_bias) lane_bias(buf, bk);
 #pragma unroll
@@ -410,209 +706,204 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd(const Params p) {
     }
     l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
     m_run = m_new;
-    return alpha;
-  };
-  // P-cast of the 32 probabilities into the FP8 operand (slot order)
-  auto cast_p = [&](f32x16_t(&sa)[2]) {
-    i32x8_t pb;
 #pragma unroll
     for (int w = 0; w < 8; ++w)
-      pb[w] = (int)cast4<kMode>(p, sa[w / 4][4 * (w % 4)], sa[w / 4][4 * (w % 4) + 1],
-                                sa[w / 4][4 * (w % 4) + 2], sa[w / 4][4 * (w % 4) + 3]);
-    return pb;
-  };
-  // underflow counters of a block with a mask or a sink: per key
-  auto count_general = [&](const i32x8_t& pb, int key0, bool has_bias, int buf) {
-    float bk[32];
-    if (has_bias) lane_bias(buf, bk);
+      pb[w] = (int)cast4<kMode>(p, sa[w / 4][4 * (w % 4)], sa[w / 4][4 * (w % 4) + 1], sa[w / 4][4 * (w % 4) + 2],
+                                sa[w / 4][4 * (w % 4) + 3]);
+    if constexpr (kStats) {
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const int kj = slot_key(g, j);
-      const bool vis = !kCausal || key0 + kj <= myrow;
-      const bool nonsink = !has_bias || bk[j] == 0.0f;
-      const bool z = (((uint32_t)pb[j / 4] >> (8 * (j % 4))) & 0xFFu) == 0;
-      cnt_tot += (vis && nonsink);
-      cnt_zero += (vis && nonsink && z);
+      for (int j = 0; j < 32; ++j) {
+        const int kj = slot_key(g, j);
+        const bool vis = !kCausal || key0 + kj <= myrow;
+        const bool nonsink = !has_bias || bk[j] == 0.0f;
+        const bool z = (((uint32_t)pb[j / 4] >> (8 * (j % 4))) & 0xFFu) == 0;
+        cnt_tot += (vis && nonsink);
+        cnt_zero += (vis && nonsink && z);
+      }
     }
+    return alpha;
   };
   // non-zero codes of a block where every pair is visible and non-sink: v_msad_u8
   // sums |(w | 0x80808080) - w| = 0x80 over the bytes where w is non-zero, so the
   // accumulator holds 128 times the count
-  auto count_fast = [&](const i32x8_t& pb) {
+  auto count_fast = [&](const i32x8_t& pb) __attribute__((always_inline)) {
     ++n_fast;
 #pragma unroll
     for (int w = 0; w < 8; ++w)
       cnt_nz_fast = __builtin_amdgcn_msad_u8((uint32_t)pb[w] | 0x80808080u, (uint32_t)pb[w], cnt_nz_fast);
   };
-  // O^T = alpha O^T (alpha == 1 in every lane: exact no-op, skipped), overlapped
-  // with the 16 logit MFMAs of the next block when there is one.
-  auto rescale_and_next = [&](float alpha, bool next, int nbuf) {
-    const bool rs = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
-    if (next && rs) {
-      issue_s(nbuf, sacc);
-#pragma unroll
-      for (int dt = 0; dt < G::kDTiles; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * G::kQSteps; ++i) {
-        if (i + 2 < 2 * G::kQSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 16 * G::kDTiles / (2 * G::kQSteps), 0);
-      }
-    } else if (next) {
-      issue_s(nbuf, sacc);
-    } else if (rs) {
-#pragma unroll
-      for (int dt = 0; dt < G::kDTiles; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-    }
-  };
-  // O^T += V8^T P8^T
-  auto accumulate_fp8 = [&](int buf, const i32x8_t& pb) {
-    const uint8_t* vl = lds_v[buf] + li * kVRow;
-    const int xv = SV::key(li);  // rows dt*32 + li share the swizzle key
-    const int vlo = ((2 * g) ^ xv) << 4, vhi = ((2 * g + 1) ^ xv) << 4;
-#pragma unroll
-    for (int dt = 0; dt < G::kDTiles; ++dt) {
-      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vlo);
-      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vhi);
-      const i32x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, oacc[dt], 0, 0, 0, 0, 0, 0);
-    }
-  };
 
-  // One step: softmax, P-cast and P.V of block `it` (its logits are in sacc); the
-  // logits of block it+1 are formed into sacc once the P-cast has consumed it.
-  auto step = [&](int it) {
+  // Step j: block j in buffers cur = j % 2 (its logits, codes, V and bias), blocks
+  // j-1 and j+1 in nxt.
+  auto step = [&](int it, auto cur_c) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
     const int t = tile_of(it);
-    const int cur = it & 1, nxt = cur ^ 1;
-    const bool more1 = it + 1 < n_it, more2 = it + 2 < n_it;
-    // K of block it+2 replaces K of block it (last read during step it-1); V of
-    // block it+1 replaces V of block it-1.  Both land while this step computes.
-    if (more2) load_k(tile_of(it + 2), cur);
-    if (more1) load_v(tile_of(it + 1), nxt);
-    const float bl_lane = bpend;  // bias of key key0 + lane
-    if (more1) load_bias(tile_of(it + 1));
+    // K of block j+2 replaces K of block j (read during step j-1); V of block j
+    // replaces V of block j-2 (read during step j-1); bias of block j+1 replaces
+    // that of block j-1.  All land before the barrier that ends this step.
+    if (it + 2 < n_it) load_k(tile_of(it + 2), cur);
+    load_v(t, cur);
+    if (it + 1 < n_it) load_b(tile_of(it + 1), nxt);
     const bool vis = visible(t);
-    const bool vis1 = more1 && visible(tile_of(it + 1));
-    if (vis) {
-      const int key0 = t * kKvBlock;
-      const bool diag = kCausal && (key0 + kKvBlock - 1 > wrow0);
-      const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bl_lane != 0.0f) != 0;
-      const bool fast = !diag && !has_bias;
-      if (kFp8 && fast && vis1) {
-        // Pipelined by key halves, in place: once the first half's probabilities are
-        // cast, its registers take the next block's logits for keys 0..31 while the
-        // second half is exponentiated; then keys 32..63 of the next block while O is
-        // rescaled and the codes counted.
-        const float mx = block_max(sacc);
-        const float m_new = fmaxf(m_run, mx * c);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        const float neg = -m_new;
-        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        i32x8_t pb;
+    const bool vis1 = it + 1 < n_it && visible(tile_of(it + 1));
+    const int key0 = t * kKvBlock;
+    const bool diag = kCausal && (key0 + kKvBlock - 1 > wrow0);
+    const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bbuf(cur)[lane] != 0.0f) != 0;
+    const bool fast = vis && !diag && !has_bias;
+    if (fast && pend && vis1) {
+      // Steady state: 20 MFMAs, each in a chunk of its own with the fragment read
+      // two MFMAs ahead and a slice of VALU work that does not depend on any MFMA
+      // in flight; sched_barrier fences keep the chunks in this order.
+      //   A: block j-1's P.V      | max, alpha, first half's exponentials and casts
+      //   B: block j+1's logits, first half (over block j's, already cast)
+      //                           | second half's exponentials and casts
+      //   C: second half          | counters
+      // The rescale owed by block j-1 comes first, skipped when no row's max grew.
+      rescale(alpha_pend);
+      i32x8_t& pb = pbuf[cur];
+      const uint8_t* vl = vbuf(nxt) + li * kVRow;
+      const int xv = SV::key(li);
+      const int vlo = ((2 * g) ^ xv) << 4, vhi = ((2 * g + 1) ^ xv) << 4;
+      auto vfrag = [&](int dt) __attribute__((always_inline)) {
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vlo);
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vhi);
+        return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      const uint8_t* kl = kbuf(nxt) + li * kKRow;
+      auto kfrag = [&](int f) __attribute__((always_inline)) {  // f = half * kQSteps + step
+        const int hh = f / G::kQSteps, st = f % G::kQSteps;
+        return *reinterpret_cast<const bf16x8_t*>(kl + hh * 32 * kKRow + (((2 * st + g) ^ xk) << 4));
+      };
+      auto pv = [&](int dt, const i32x8_t& a) __attribute__((always_inline)) {
+        oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pbuf[nxt], oacc[dt], 0, 0, 0, 0, 0, 0);
+      };
+      auto smfma = [&](int f, const bf16x8_t& a) __attribute__((always_inline)) {
+        const int hh = f / G::kQSteps, st = f % G::kQSteps;
+        sacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], st == 0 ? f32x16_t{} : sacc[hh], 0, 0, 0);
+      };
+      constexpr int kS = 2 * G::kQSteps;  // logit MFMAs
+      i32x8_t vf[G::kDTiles];
+      bf16x8_t kf[kS];
+      float m4[4], ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      auto chain = [&](int q) __attribute__((always_inline)) {
+        m4[q] = fmaxf(sacc[q / 2][(q % 2) * 8], sacc[q / 2][(q % 2) * 8 + 1]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pj = __builtin_amdgcn_exp2f(fmaf(sacc[0][r], c, neg));
-          sacc[0][r] = pj;
-          ps[r % 4] += pj;
+        for (int r = 2; r < 8; r += 2)
+          m4[q] = fmaxf(fmaxf(m4[q], sacc[q / 2][(q % 2) * 8 + r]), sacc[q / 2][(q % 2) * 8 + r + 1]);
+      };
+      float m_new = 0.0f, alpha = 1.0f, neg = 0.0f;
+      auto expo = [&](int hh, int r) __attribute__((always_inline)) {
+        const float pj = __builtin_amdgcn_exp2f(fmaf(sacc[hh][r], c, neg));
+        sacc[hh][r] = pj;
+        ps[r % 4] += pj;
+      };
+      auto cast = [&](int w) __attribute__((always_inline)) {  // codes of slots 4w..4w+3
+        const int hh = w / 4, r = 4 * (w % 4);
+        pb[w] = (int)cast4<kMode>(p, sacc[hh][r], sacc[hh][r + 1], sacc[hh][r + 2], sacc[hh][r + 3]);
+      };
+#define PCAST_FENCE __builtin_amdgcn_sched_barrier(0)
+      // operand fragments run kAhead MFMAs ahead: MFMA i (P.V tiles first, then the
+      // logit halves) takes fragment i
+      constexpr int kAhead = 2;
+      constexpr int kM = G::kDTiles + kS;
+      auto fetch = [&](int i) __attribute__((always_inline)) {
+        if (i < G::kDTiles) vf[i] = vfrag(i);
+        else if (i < kM) kf[i - G::kDTiles] = kfrag(i - G::kDTiles);
+      };
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) fetch(i);
+      PCAST_FENCE;
+      // ---- A: P.V MFMAs, the VALU work in 25 units (four max chains, the max
+      // itself and alpha, 16 exponentials, four casts) spread evenly over them ----
+      constexpr int kAUnits = 4 + 1 + 16 + 4;
+      auto aunit = [&](int u) __attribute__((always_inline)) {
+        if (u < 4) {
+          chain(u);
+        } else if (u == 4) {
+          const float mx = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+          m_new = fmaxf(m_run, mx * c);
+          alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          neg = -m_new;
+        } else if (u < 21) {
+          expo(0, u - 5);
+        } else {
+          cast(u - 21);
         }
+      };
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          pb[w] = (int)cast4<kMode>(p, sacc[0][4 * w], sacc[0][4 * w + 1], sacc[0][4 * w + 2], sacc[0][4 * w + 3]);
-        issue_s_half(nxt, sacc[0], 0);
+      for (int i = 0; i < G::kDTiles; ++i) {
+        pv(i, vf[i]);
+        fetch(kAhead + i);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pj = __builtin_amdgcn_exp2f(fmaf(sacc[1][r], c, neg));
-          sacc[1][r] = pj;
-          ps[r % 4] += pj;
-        }
+        for (int u = i * kAUnits / G::kDTiles; u < (i + 1) * kAUnits / G::kDTiles; ++u) aunit(u);
+        PCAST_FENCE;
+      }
+      // ---- B and C ----
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          pb[4 + w] = (int)cast4<kMode>(p, sacc[1][4 * w], sacc[1][4 * w + 1], sacc[1][4 * w + 2], sacc[1][4 * w + 3]);
-        l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
-        m_run = m_new;
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int f = 0; f < kS; ++f) {
+        smfma(f, kf[f]);
+        fetch(G::kDTiles + f + kAhead);
+        if (f < G::kQSteps) {
+          // second half's exponentials, 16 over kQSteps chunks, casts as they complete
+          constexpr int kPer = 16 / G::kQSteps;
 #pragma unroll
-        for (int i = 0; i < G::kQSteps; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i + 2 < G::kQSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x402, 56 / G::kQSteps, 0);
-        }
-        issue_s_half(nxt, sacc[1], 1);
+          for (int r = 0; r < kPer; ++r) expo(1, f * kPer + r);
+          if (((f + 1) * kPer) % 4 == 0) cast(4 + ((f + 1) * kPer) / 4 - 1);
+        } else {
+          const int k = f - G::kQSteps;
+          if constexpr (kStats) {
+            constexpr int kW = 8 / G::kQSteps;
 #pragma unroll
-        for (int dt = 0; dt < G::kDTiles; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;  // alpha == 1: exact no-op
-        if constexpr (kStats) count_fast(pb);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int i = 0; i < G::kQSteps; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i + 2 < G::kQSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, (16 * G::kDTiles + (kStats ? 16 : 0)) / G::kQSteps, 0);
-        }
-        accumulate_fp8(cur, pb);
-      } else {
-      const float alpha = fast ? softmax_fast(sacc) : softmax_general(sacc, key0, diag, has_bias, cur);
-      if constexpr (kFp8) {
-        const i32x8_t pb = cast_p(sacc);
-        if constexpr (kStats) {
-          if (fast) count_fast(pb);
-          else count_general(pb, key0, has_bias, cur);
-        }
-        rescale_and_next(alpha, vis1, nxt);
-        accumulate_fp8(cur, pb);
-      } else {
-        uint32_t pw[16];
-#pragma unroll
-        for (int w = 0; w < 16; ++w) pw[w] = cast2_bf16(sacc[w / 8][(2 * w) % 16], sacc[w / 8][(2 * w + 1) % 16]);
-        if constexpr (kStats) {
-#pragma unroll
-          for (int j = 0; j < 32; ++j) {
-            const int kj = slot_key(g, j);
-            const bool vis_j = !kCausal || key0 + kj <= myrow;
-            const bool nonsink = !has_bias || lds_bias[cur][kj] == 0.0f;
-            const bool z = ((pw[j / 2] >> (16 * (j % 2))) & 0xFFFFu) == 0;
-            cnt_tot += (vis_j && nonsink);
-            cnt_zero += (vis_j && nonsink && z);
+            for (int e = 0; e < kW; ++e) {
+              const int w = k * kW + e;
+              cnt_nz_fast = __builtin_amdgcn_msad_u8((uint32_t)pb[w] | 0x80808080u, (uint32_t)pb[w], cnt_nz_fast);
+            }
           }
         }
-        rescale_and_next(alpha, vis1, nxt);
-        const uint8_t* vl = lds_v[cur] + li * kVRow;
-        const int xv = SV::key(li);
-#pragma unroll
-        for (int dt = 0; dt < G::kDTiles; ++dt) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vl + dt * 32 * kVRow + (((4 * g + s) ^ xv) << 4));
-            const i32x4_t bw = {(int)pw[4 * s], (int)pw[4 * s + 1], (int)pw[4 * s + 2], (int)pw[4 * s + 3]};
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bw), oacc[dt], 0, 0, 0);
-          }
-        }
+        PCAST_FENCE;
       }
+#undef PCAST_FENCE
+      if constexpr (kStats) ++n_fast;
+      l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+      m_run = m_new;
+      alpha_pend = alpha;  // owed before block j's P.V, at the start of the next step
+    } else {
+      if (pend) {
+        rescale(alpha_pend);
+        accumulate(nxt, pbuf[nxt]);
       }
-    } else if (vis1) {
-      issue_s(nxt, sacc);
+      alpha_pend = 1.0f;
+      if (vis) {
+        alpha_pend = fast ? softmax_fast(sacc, pbuf[cur])
+                          : softmax_general(sacc, pbuf[cur], key0, diag, has_bias, cur);
+        if (kStats && fast) count_fast(pbuf[cur]);
+      }
+      if (vis1) issue_s(nxt, sacc);
     }
+    pend = vis;
     wait_loads();
     __syncthreads();
   };
 
-  // prologue: K and V of the first block, K of the second; logits of the first block
+  // prologue: K of the first two blocks and the first bias block; logits of the first block
   load_k(tile_of(0), 0);
-  load_v(tile_of(0), 0);
-  load_bias(tile_of(0));
   if (n_it > 1) load_k(tile_of(1), 1);
+  load_b(tile_of(0), 0);
   wait_loads();
   __syncthreads();
   if (visible(tile_of(0))) issue_s(0, sacc);
   // step 0 reloads K buffer 0: every wave must have read block 0's K first
   __syncthreads();
-  for (int it = 0; it < n_it; ++it) step(it);
+  for (int it = 0; it < n_it; it += 2) {
+    step(it, BufIndex<0>{});
+    if (it + 1 < n_it) step(it + 1, BufIndex<1>{});
+  }
+  // the last block's P.V (its V landed before the last step's barrier)
+  if (pend) {
+    rescale(alpha_pend);
+    if ((n_it - 1) & 1) accumulate(1, pbuf[1]);
+    else accumulate(0, pbuf[0]);
+  }
 
   // ---- epilogue: O = A / (S l) ----
   if (wave_active) {
@@ -705,10 +996,17 @@ template <int D, int kMode, bool kCausal>
 void launch_attn3(const Params& p, hipStream_t stream) {
   const int n_rb = (p.N + kBlockRows - 1) / kBlockRows;
   const dim3 grid((unsigned)(n_rb * p.Hq * p.B));
-  if (p.stats)
-    hipLaunchKernelGGL((pcast_attn_fwd<D, kMode, kCausal, true>), grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((pcast_attn_fwd<D, kMode, kCausal, false>), grid, dim3(kThreads), 0, stream, p);
+  if constexpr (kMode == kBf16) {
+    if (p.stats)
+      hipLaunchKernelGGL((pcast_attn_fwd_bf16<D, kCausal, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((pcast_attn_fwd_bf16<D, kCausal, false>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    if (p.stats)
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, false>), grid, dim3(kThreads), 0, stream, p);
+  }
 }
 
 template <int D, int kMode>
