@@ -6,7 +6,7 @@
 // max m' includes the current block; P = exp(s - m') is summed un-cast into l;
 // P*S is rounded to E4M3 and multiplied with E4M3(V) on the FP8 matrix cores;
 // the accumulator is rescaled by exp(m - m') when the max grows and divided by
-// S*l at the end.  S = 0 runs the same pipeline with P and V in bf16.
+// S*l at the end.  S = 0 (no cast) runs a separate kernel with P and V in bf16.
 //
 // Mapping to CDNA4:
 // * One workgroup = 4 waves = 128 query rows of one (batch, head); each wave
@@ -21,8 +21,10 @@
 //   keys is taken as the MFMA's k order, and V is copied once per call (by
 //   pcast_prep_v) into E4M3 in the same key order, transposed to [d][key], so
 //   both operands agree without any shuffle.
-// * K and V tiles are staged through LDS, double-buffered: the global loads
-//   of block j+1 are in flight while block j is computed.
+// * K and V tiles are staged through LDS by direct global->LDS loads, double
+//   buffered, each buffer its own LDS object.  The FP8 kernel is software-
+//   pipelined by one block: step j holds block j-1's P.V, block j's softmax
+//   and block j+1's logits, interleaved MFMA by MFMA.
 // * Exactness of the scale: for S = 2^k the product P*S is formed inside the
 //   conversion (v_cvt_scalef32_pk_fp8_f32 with scale 2^-k), which is exact;
 //   1/(S*l) is exact up to the final reciprocal.  Other S use an fp32 multiply
@@ -690,11 +692,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
       if (diag && key0 + kj > myrow) xj = -INFINITY;
       sa[j / 16][j % 16] = xj;
     }
-    float mx = sa[0][0];
-#pragma unroll
-    for (int j = 1; j < 32; ++j) mx = fmaxf(mx, sa[j / 16][j % 16]);
-    mx = halves_max(mx);
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, block_max(sa));
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -711,14 +709,32 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
       pb[w] = (int)cast4<kMode>(p, sa[w / 4][4 * (w % 4)], sa[w / 4][4 * (w % 4) + 1], sa[w / 4][4 * (w % 4) + 2],
                                 sa[w / 4][4 * (w % 4) + 3]);
     if constexpr (kStats) {
+      if (has_bias) {
+        // per key: visible, non-sink, code zero
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const int kj = slot_key(g, j);
-        const bool vis = !kCausal || key0 + kj <= myrow;
-        const bool nonsink = !has_bias || bk[j] == 0.0f;
-        const bool z = (((uint32_t)pb[j / 4] >> (8 * (j % 4))) & 0xFFu) == 0;
-        cnt_tot += (vis && nonsink);
-        cnt_zero += (vis && nonsink && z);
+        for (int j = 0; j < 32; ++j) {
+          const int kj = slot_key(g, j);
+          const bool vis = !kCausal || key0 + kj <= myrow;
+          const bool nonsink = bk[j] == 0.0f;
+          const bool z = (((uint32_t)pb[j / 4] >> (8 * (j % 4))) & 0xFFu) == 0;
+          cnt_tot += (vis && nonsink);
+          cnt_zero += (vis && nonsink && z);
+        }
+      } else {
+        // causal mask only.  The lane's 32 keys are eight runs of four consecutive
+        // keys starting at h*32 + q*8 + g*4; the visible ones are those <= myrow -
+        // key0.  Masked keys have P = 0, whose code is 0, so the zero codes among
+        // the visible keys are all zero codes minus the masked keys.
+        const int lim = myrow - key0 + 1;  // keys below lim are visible
+        int vis = 0;
+#pragma unroll
+        for (int run = 0; run < 8; ++run) vis += min(max(lim - ((run / 4) * 32 + (run % 4) * 8 + g * 4), 0), 4);
+        unsigned int nz = 0;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) nz = __builtin_amdgcn_msad_u8((uint32_t)pb[w] | 0x80808080u, (uint32_t)pb[w], nz);
+        const int zeros = 32 - (int)(nz >> 7);
+        cnt_tot += vis;
+        cnt_zero += zeros - (32 - vis);
       }
     }
     return alpha;
