@@ -594,15 +594,6 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
       }
     }
   };
-  // the 32-key half kb of the same product: kQSteps MFMAs into one accumulator
-  auto issue_s_half = [&](int buf, f32x16_t& out, int kb) __attribute__((always_inline)) {
-    const uint8_t* kl = kbuf(buf) + (kb * 32 + li) * kKRow;
-#pragma unroll
-    for (int s = 0; s < G::kQSteps; ++s) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + (((2 * s + g) ^ xk) << 4));
-      out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16_t{} : out, 0, 0, 0);
-    }
-  };
   f32x16_t oacc[G::kDTiles];
 #pragma unroll
   for (int dt = 0; dt < G::kDTiles; ++dt)
@@ -767,7 +758,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
     const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bbuf(cur)[lane] != 0.0f) != 0;
     const bool fast = vis && !diag && !has_bias;
     if (fast && pend && vis1) {
-      // Steady state: 20 MFMAs, each in a chunk of its own with the fragment read
+      // Steady state: the block's MFMAs (20 at d = 128), each in a chunk of its own with the fragment read
       // two MFMAs ahead and a slice of VALU work that does not depend on any MFMA
       // in flight; sched_barrier fences keep the chunks in this order.
       //   A: block j-1's P.V      | max, alpha, first half's exponentials and casts
