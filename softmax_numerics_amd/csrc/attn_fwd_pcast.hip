@@ -758,9 +758,10 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
     const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bbuf(cur)[lane] != 0.0f) != 0;
     const bool fast = vis && !diag && !has_bias;
     if (fast && pend && vis1) {
-      // Steady state: the block's MFMAs (20 at d = 128), each in a chunk of its own with the fragment read
-      // two MFMAs ahead and a slice of VALU work that does not depend on any MFMA
-      // in flight; sched_barrier fences keep the chunks in this order.
+      // Steady state: the step's MFMAs (20 at d = 128), each in a chunk of its own
+      // with the fragment read two MFMAs ahead and a slice of VALU work that does
+      // not depend on any MFMA in flight; sched_barrier fences keep the chunks in
+      // this order.
       //   A: block j-1's P.V      | max, alpha, first half's exponentials and casts
       //   B: block j+1's logits, first half (over block j's, already cast)
       //                           | second half's exponentials and casts
