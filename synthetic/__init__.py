@@ -80,6 +80,15 @@ def sink_bias(n: int, delta: float, sink_keys: int = SINK_KEYS) -> np.ndarray:
     return b
 
 
+def random_bias(n: int, seed: int, zero_frac: float = 0.5, scale: float = 2.0) -> np.ndarray:
+    """float32 [n]: N(0, scale^2) on a random subset of keys, exactly 0 on a
+    fraction ``zero_frac`` of them (numpy's PCG64 stream seeded with ``seed``)."""
+    rng = np.random.default_rng(seed)
+    b = (rng.standard_normal(n) * scale).astype(np.float32)
+    b[rng.random(n) < zero_frac] = 0.0
+    return b
+
+
 def qkv_bf16(B: int, Hq: int, Hkv: int, N: int, d: int, seed: int):
     """(Q, K, V) bf16 bit arrays shaped [B,Hq,N,d], [B,Hkv,N,d], [B,Hkv,N,d]."""
     q = gaussian_bf16(seed, TENSOR_Q, (B, Hq, N, d))

@@ -67,6 +67,35 @@ def test_sink_strengths(sna, delta, order):
         assert rep["underflow_gpu"] > 0.99
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("S", [1.0, 256.0, 0.0])
+def test_random_bias(sna, d, causal, order, S):
+    """A bias on about half of all keys: every block takes the general path, and
+    the counters skip exactly the biased keys."""
+    B, Hq, Hkv, N, seed = 1, 3, 3, 384, 31
+    print(f"\n[case] random bias: d={d} causal={causal} order={order} S={S}", flush=True)
+    qb, kb, vb = synthetic.qkv_bf16(B, Hq, Hkv, N, d, seed)
+    bias = synthetic.random_bias(N, seed)
+    out, st = _run(sna, qb, kb, vb, bias, causal, S, order)
+    rep = _parity.compare(out, st, qb, kb, vb, bias, causal, S, order)
+    print(f"[case] random bias: {rep}", flush=True)
+
+
+@pytest.mark.parametrize("N", [64, 192])
+@pytest.mark.parametrize("order", [0, 1])
+def test_partial_workgroups(sna, N, order):
+    # 128-row workgroups: N = 64 leaves two waves of the only workgroup without rows,
+    # N = 192 the last workgroup half empty; GQA groups of 2
+    _case(sna, f"partial N={N}", 3, 6, 3, N, 128, True, 7.0, 256.0, order, 32)
+
+
+def test_many_small_heads(sna):
+    # a wide grid of short rows: 8 x 16 heads of 128 rows, groups of 4 query heads
+    _case(sna, "many heads", 8, 16, 4, 128, 128, False, 7.0, 256.0, 1, 33)
+
+
 def test_zero_queries_exact_mean(sna):
     """Q = 0: every p = 1, so out = mean of E4M3(V) over the visible keys."""
     print("\n[case] zero queries", flush=True)
