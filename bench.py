@@ -12,7 +12,9 @@ FlashAttention convention 2*B*H*N^2*d for causal), the attention kernel's own
 time from HIP events on the launch stream, its fraction of the FP8 dense MFMA
 peak, the CPU oracle timed on a bounded sample of the same workload, and the
 output MSE against fp64 attention on that sample for S=256 reverse and S=1
-forward.
+forward.  The "qk_fp8" object times the variant with FP8 logits
+(pcast_prepare_qk8 + attn_fwd_pcast_qk8_prepared) on the same input, and its
+MSE against the same fp64 attention of the unquantised Q and K.
 """
 from __future__ import annotations
 
@@ -58,7 +60,7 @@ def causal_row_flops(rows, N: int, d: int, causal: bool):
     return float(np.sum(4.0 * d * keys))
 
 
-def cpu_baseline(w, qb, kb, vb, bias, out_rev, out_fwd1, target_s: float, seed: int = 0):
+def cpu_baseline(w, qb, kb, vb, bias, out_rev, out_fwd1, target_s: float, seed: int = 0, out_qk8=None):
     """Time the oracle (kernel-mode block pipeline + exact attention, fp64, all
     host threads) on random 64-row blocks of the same workload, and use its
     exact result for the output-MSE comparison of the two GPU runs."""
@@ -89,7 +91,10 @@ def cpu_baseline(w, qb, kb, vb, bias, out_rev, out_fwd1, target_s: float, seed: 
     flops = causal_row_flops(ids, w.N, w.d, w.causal)
     o1 = ref["o1"]
     mse = {}
-    for name, out in (("S256_reverse", out_rev), ("S1_forward", out_fwd1)):
+    runs = [("S256_reverse", out_rev), ("S1_forward", out_fwd1)]
+    if out_qk8 is not None:
+        runs.append(("qk_fp8_S256_reverse", out_qk8))
+    for name, out in runs:
         got = out.reshape(-1, w.d)[ids].astype(np.float64)
         mse[name] = float(np.mean((got - o1) ** 2))
     mse["oracle_S256_reverse"] = float(np.mean((ref["o2"] - o1) ** 2))
@@ -110,6 +115,7 @@ def main() -> int:
     ap.add_argument("--no-stats", action="store_true", help="time without the underflow counters")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-qk8", action="store_true", help="skip the FP8-logit variant")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes, 3 times (scale for "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
@@ -171,6 +177,24 @@ def main() -> int:
         if rc != sna.PCAST_OK:
             raise sna.PcastError(rc, sna.strerror(rc))
 
+    ws8 = None if args.no_qk8 else torch.empty(sna.workspace_bytes_qk8(w.B, w.Hq, w.Hkv, w.N, w.d),
+                                               dtype=torch.uint8, device=dev)
+
+    def step_qk8(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        rc = sna.prepare_qk8(q.data_ptr(), k.data_ptr(), v.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d,
+                             ws8.data_ptr(), sh)
+        if ev is not None:
+            ev[1].record(stream)
+        rc = rc or sna.attn_fwd_pcast_qk8_prepared(
+            ws8.data_ptr(), bias_t.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), S, order,
+            out.data_ptr(), 0 if stats is None else stats.data_ptr(), sh)
+        if ev is not None:
+            ev[2].record(stream)
+        if rc != sna.PCAST_OK:
+            raise sna.PcastError(rc, sna.strerror(rc))
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -211,12 +235,35 @@ def main() -> int:
         "frac_mixed_roof": round(achieved / mixed_roof, 4),
     }
 
+    out_rev = out.cpu().numpy() if not args.no_cpu_baseline else None
+    out_qk8 = None
+    if ws8 is not None:
+        # the FP8-logit variant on the same input, same configuration
+        for _ in range(args.warmup):
+            step_qk8()
+        ev8 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step_qk8(ev=ev8[i])
+        torch.cuda.synchronize()
+        wall8 = time.perf_counter() - t0
+        prep8 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev8]))
+        attn8 = float(np.mean([e[1].elapsed_time(e[2]) for e in ev8]))
+        ach8 = flops / (attn8 * 1e-3) / 1e12
+        print(f"[bench] FP8 logits: {wall8 * 1e3 / args.steps:.4f} ms/step (wall), attention kernel "
+              f"{attn8:.4f} ms, Q/K/V pre-pass {prep8:.4f} ms", file=sys.stderr, flush=True)
+        result["qk_fp8"] = {"ms_per_step": round(wall8 * 1e3 / args.steps, 5),
+                            "value": round(flops / wall8 * args.steps / 1e12, 2),
+                            "attention_kernel_ms": round(attn8, 5), "prepass_ms": round(prep8, 5),
+                            "achieved": round(ach8, 2), "frac": round(ach8 / PEAK_FP8, 4)}
+        out_qk8 = out.cpu().numpy()
+
     if not args.no_cpu_baseline:
-        out_rev = out.cpu().numpy()
         step(S_=1.0, order_=0)                      # S = 1 forward, for the error contrast
         torch.cuda.synchronize()
         out_fwd1 = out.cpu().numpy()
-        base, mse = cpu_baseline(w, qb, kb, vb, bias, out_rev, out_fwd1, args.cpu_seconds)
+        base, mse = cpu_baseline(w, qb, kb, vb, bias, out_rev, out_fwd1, args.cpu_seconds, out_qk8=out_qk8)
         result["cpu_baseline"] = base
         result["mse_vs_fp64_sampled"] = mse
     else:

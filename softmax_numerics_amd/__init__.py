@@ -20,7 +20,8 @@ ORDERS = {"forward": 0, "reverse": 1, 0: 0, 1: 1}
 
 # Every symbol include/pcast_attn.h declares.
 EXPORTS = ("attn_fwd_pcast", "pcast_prepare_v", "attn_fwd_pcast_prepared", "pcast_stats_words",
-           "pcast_workspace_bytes", "pcast_strerror", "pcast_abi_version")
+           "pcast_workspace_bytes", "pcast_strerror", "pcast_abi_version", "pcast_workspace_bytes_qk8",
+           "pcast_prepare_qk8", "attn_fwd_pcast_qk8_prepared", "attn_fwd_pcast_qk8")
 
 _lock = threading.Lock()
 _lib = None
@@ -57,6 +58,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.pcast_strerror.restype = ctypes.c_char_p
             lib.pcast_abi_version.argtypes = []
             lib.pcast_abi_version.restype = I
+            lib.pcast_workspace_bytes_qk8.argtypes = [I, I, I, I, I]
+            lib.pcast_workspace_bytes_qk8.restype = ctypes.c_size_t
+            lib.pcast_prepare_qk8.argtypes = [P, P, P, I, I, I, I, I, P, P]
+            lib.pcast_prepare_qk8.restype = I
+            lib.attn_fwd_pcast_qk8_prepared.argtypes = [P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P]
+            lib.attn_fwd_pcast_qk8_prepared.restype = I
+            lib.attn_fwd_pcast_qk8.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P]
+            lib.attn_fwd_pcast_qk8.restype = I
             _lib = lib
     return _lib
 
@@ -84,6 +93,29 @@ def attn_fwd_pcast_prepared(Q, K, workspace, bias, B, Hq, Hkv, N, d, causal, S, 
         stats or None, stream or None))
 
 
+def attn_fwd_pcast_qk8(Q, K, V, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats, stream) -> int:
+    """Raw attn_fwd_pcast_qk8 (FP8 logits) with integer device addresses; returns the C return code."""
+    return int(load_library().attn_fwd_pcast_qk8(Q, K, V, bias or None, B, Hq, Hkv, N, d, int(causal),
+                                                 float(S), int(order), out, stats or None, stream or None))
+
+
+def prepare_qk8(Q, K, V, B, Hq, Hkv, N, d, workspace, stream) -> int:
+    """Raw pcast_prepare_qk8 with integer device addresses; returns the C return code."""
+    return int(load_library().pcast_prepare_qk8(Q, K, V, B, Hq, Hkv, N, d, workspace, stream or None))
+
+
+def attn_fwd_pcast_qk8_prepared(workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
+                                stream) -> int:
+    """Raw attn_fwd_pcast_qk8_prepared with integer device addresses; returns the C return code."""
+    return int(load_library().attn_fwd_pcast_qk8_prepared(
+        workspace, bias or None, B, Hq, Hkv, N, d, int(causal), float(S), int(order), out,
+        stats or None, stream or None))
+
+
+def workspace_bytes_qk8(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
+    return int(load_library().pcast_workspace_bytes_qk8(B, Hq, Hkv, N, d))
+
+
 def stats_words(B: int, Hq: int, N: int) -> int:
     return int(load_library().pcast_stats_words(B, Hq, N))
 
@@ -93,12 +125,14 @@ def workspace_bytes(B: int, Hkv: int, N: int, d: int, S: float) -> int:
 
 
 def forward(q, k, v, bias=None, causal: bool = True, S: float = 256.0, order="reverse",
-            stats: bool = False, out=None):
+            stats: bool = False, out=None, qk_fp8: bool = False):
     """O = softmax(q k^T / sqrt(d) + bias) v with the P-cast, on the current stream.
 
     q: bf16 [B, Hq, N, d]; k, v: bf16 [B, Hkv, N, d]; bias: fp32 [N] or None.
-    S > 0: P*S cast to E4M3; S = 0: the bf16 reference path.  Returns
-    (out fp32 [B, Hq, N, d], stats int64 [B, Hq, N/64, 2] or None).
+    S > 0: P*S cast to E4M3; S = 0: the bf16 reference path.  qk_fp8: Q and K
+    rounded to E4M3 with a power-of-two scale per head, logits on the FP8
+    matrix cores (needs S > 0).  Returns (out fp32 [B, Hq, N, d], stats int64
+    [B, Hq, N/64, 2] or None).
     """
     import torch
 
@@ -118,9 +152,10 @@ def forward(q, k, v, bias=None, causal: bool = True, S: float = 256.0, order="re
     if stats:
         st = torch.empty(stats_words(B, Hq, N), dtype=torch.int64, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = attn_fwd_pcast(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                        0 if bias is None else bias.data_ptr(), B, Hq, Hkv, N, d, causal, S,
-                        ORDERS[order], out.data_ptr(), 0 if st is None else st.data_ptr(), stream)
+    call = attn_fwd_pcast_qk8 if qk_fp8 else attn_fwd_pcast
+    rc = call(q.data_ptr(), k.data_ptr(), v.data_ptr(), 0 if bias is None else bias.data_ptr(),
+              B, Hq, Hkv, N, d, causal, S, ORDERS[order], out.data_ptr(),
+              0 if st is None else st.data_ptr(), stream)
     if rc != PCAST_OK:
         raise PcastError(rc, strerror(rc))
     if st is not None:

@@ -130,6 +130,81 @@ __global__ __launch_bounds__(256) void pcast_prep_v(const uint16_t* __restrict__
   }
 }
 
+// ---------------------------------------------------------------------------
+// FP8 logits (an extension of the P-cast path): Q and K rounded to E4M3 with a
+// per-head power-of-two scale.  The scale of a head is the smallest 2^e with
+// max|x| <= 448 * 2^e, so x * 2^-e is exact and never exceeds 448.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pcast_fill_u32(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// max |x| of each head of a bf16 tensor [heads][per_head] as fp32 bits (bf16 bits
+// << 16; for values >= 0 the integer order is the float order).  Grid: (chunks,
+// heads), 16 elements per thread and kAbsChunk per workgroup.
+constexpr int kAbsChunk = 256 * 16 * 4;
+__global__ __launch_bounds__(256) void pcast_absmax(const uint16_t* __restrict__ x, int64_t per_head,
+                                                    uint32_t* __restrict__ amax) {
+  const int64_t head = blockIdx.y;
+  const int64_t base = head * per_head + (int64_t)blockIdx.x * kAbsChunk;
+  const int64_t end = min((int64_t)kAbsChunk, per_head - (int64_t)blockIdx.x * kAbsChunk);
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)threadIdx.x * 8; i < end; i += 256 * 8) {
+    const i32x4_t v = *reinterpret_cast<const i32x4_t*>(x + base + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w = (uint32_t)v[e];
+      m = max(m, max(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t part[4];
+  if (threadIdx.x % 64 == 0) part[threadIdx.x / 64] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(amax + head, max(max(part[0], part[1]), max(part[2], part[3])) << 16);
+}
+
+// the head's scale exponent from its max |x| (fp32 bits): smallest e with
+// amax <= 448 * 2^e, 448 = 0.875 * 2^9
+__device__ inline int scale_exp(uint32_t amax_bits) {
+  const float a = __builtin_bit_cast(float, amax_bits);
+  if (a == 0.0f) return 0;
+  int E;
+  const float m = frexpf(a, &E);
+  return m <= 0.875f ? E - 9 : E - 8;
+}
+
+// E4M3 codes of x * 2^-e (RNE; |x * 2^-e| <= 448 by the choice of e), 16 per thread.
+__global__ __launch_bounds__(256) void pcast_quant_fp8(const uint16_t* __restrict__ x, int64_t per_head,
+                                                       const uint32_t* __restrict__ amax,
+                                                       uint8_t* __restrict__ out) {
+  const int64_t head = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * (256 * 16) + (int64_t)threadIdx.x * 16;
+  if (i >= per_head) return;
+  const int e = scale_exp(amax[head]);
+  const uint16_t* src = x + head * per_head + i;
+  const i32x4_t a = *reinterpret_cast<const i32x4_t*>(src);
+  const i32x4_t b = *reinterpret_cast<const i32x4_t*>(src + 8);
+  const uint32_t w[8] = {(uint32_t)a[0], (uint32_t)a[1], (uint32_t)a[2], (uint32_t)a[3],
+                         (uint32_t)b[0], (uint32_t)b[1], (uint32_t)b[2], (uint32_t)b[3]};
+  i32x4_t o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float f[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f[2 * t] = ldexpf(__builtin_bit_cast(float, w[2 * q + t] << 16), -e);
+      f[2 * t + 1] = ldexpf(__builtin_bit_cast(float, w[2 * q + t] & 0xFFFF0000u), -e);
+    }
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], word, true);
+    o[q] = word;
+  }
+  *reinterpret_cast<i32x4_t*>(out + head * per_head + i) = o;
+}
+
 struct Params {
   const uint16_t* q;
   const uint16_t* k;
@@ -143,6 +218,11 @@ struct Params {
   float S;            // P-cast scale (1 in the bf16 path)
   float inv_S;        // 1/S: the conversion scale when S is a power of two
   float p_clamp;      // largest P kept before conversion when S > 448 (448/S)
+  // FP8 logits: E4M3 codes of Q and K ([B][H][N][d] bytes) and per-head max |x| bits
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const uint32_t* amax_q;
+  const uint32_t* amax_k;
 };
 
 // How P becomes an MFMA operand.
@@ -220,6 +300,15 @@ __device__ inline void decode_block(int lin, int total, int n_rb, int Hq, bool c
   b = hh / Hq;
   h = hh % Hq;
 }
+
+template <bool kB, class T, class F>
+struct Select {
+  using type = T;
+};
+template <class T, class F>
+struct Select<false, T, F> {
+  using type = F;
+};
 
 template <int V>
 struct BufIndex {
@@ -489,11 +578,14 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params 
 // block j-1's alpha comes first).  The three streams are independent, so the
 // MFMAs interleave with the exponentials inside one basic block.
 // ---------------------------------------------------------------------------
-template <int D, int kMode, bool kCausal, bool kStats>
+template <int D, int kMode, bool kCausal, bool kStats, bool kQ8>
 __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p) {
   static_assert(kMode != kBf16, "FP8 modes only");
   using G = Geometry<D>;
-  constexpr int kKRow = D * 2;                // bytes per K row
+  // kQ8: Q and K as E4M3 codes, logits on the FP8 MFMA (K = 64 per step), else bf16
+  constexpr int kKRow = kQ8 ? D : D * 2;      // bytes per K row
+  constexpr int kSSteps = kQ8 ? D / 64 : G::kQSteps;  // logit MFMA k-steps per 32-key half
+  using KFrag = typename Select<kQ8, i32x8_t, bf16x8_t>::type;  // one operand fragment
   constexpr int kVRow = kKvBlock;             // bytes per V^T row (64 E4M3 codes)
   constexpr int kKTile = kKvBlock * kKRow;    // bytes of one K block
   constexpr int kVTile = D * kVRow;           // bytes of one V operand block
@@ -532,19 +624,36 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
   const bool wave_active = wrow0 < p.N;
   const int t_last = kCausal ? min((row0 + kBlockRows - 1) / kKvBlock, n_tiles - 1) : n_tiles - 1;
   const int n_it = t_last + 1;
-  const float c = p.logit_scale;
+  // log2(e)/sqrt(d), times the heads' power-of-two scales for FP8 logits (exact)
+  const float c = kQ8 ? ldexpf(p.logit_scale, scale_exp(p.amax_q[b * p.Hq + h]) +
+                                                  scale_exp(p.amax_k[b * p.Hkv + hk]))
+                      : p.logit_scale;
 
   if (kStats && tid < 4) lds_cnt[tid / 2][tid % 2] = 0;
 
-  // Q operand (B of S^T = K Q^T): lane holds Q[myrow][s*16 + g*8 .. +8) for each step s.
-  bf16x8_t qf[G::kQSteps];
+  // Q operand (B of S^T = K Q^T): lane holds Q[myrow][s*16 + g*8 .. +8) for each step s
+  // (bf16), or the codes Q8[myrow][s*64 + g*32 .. +32) (FP8).  The K fragments take the
+  // same d order, so slot k of the two operands holds the same d.
+  KFrag qf[kSSteps];
   if (wave_active) {
-    const uint16_t* qrow = p.q + (((int64_t)b * p.Hq + h) * p.N + myrow) * D + g * 8;
+    const int64_t row = ((int64_t)b * p.Hq + h) * p.N + myrow;
+    if constexpr (kQ8) {
+      const uint8_t* qrow = p.q8 + row * D + g * 32;
 #pragma unroll
-    for (int s = 0; s < G::kQSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + s * 16);
+      for (int s = 0; s < kSSteps; ++s) {
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(qrow + s * 64);
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(qrow + s * 64 + 16);
+        qf[s] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    } else {
+      const uint16_t* qrow = p.q + row * D + g * 8;
+#pragma unroll
+      for (int s = 0; s < kSSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + s * 16);
+    }
   }
 
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k + ((int64_t)b * p.Hkv + hk) * p.N * D);
+  const uint8_t* kbase = kQ8 ? p.k8 + ((int64_t)b * p.Hkv + hk) * p.N * D
+                             : reinterpret_cast<const uint8_t*>(p.k + ((int64_t)b * p.Hkv + hk) * p.N * D);
   const uint8_t* vbase = static_cast<const uint8_t*>(p.vop) + ((int64_t)b * p.Hkv + hk) * (int64_t)n_tiles * kVTile;
 
   // Each lane's source offsets for the direct loads: lane i of load j of wave w fills
@@ -583,15 +692,26 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
 
   // S^T = K Q^T for the key block in K buffer `buf`: two 32-key halves, fp32 accumulation
   const int xk = SK::key(li);  // rows li and li + 32 share the swizzle key
+  // K fragment of 32-key half kb and k-step s from K buffer `buf`
+  auto kread = [&](int buf, int kb, int s) __attribute__((always_inline)) -> KFrag {
+    const uint8_t* kl = kbuf(buf) + (kb * 32 + li) * kKRow;
+    if constexpr (kQ8) {
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kl + (((4 * s + 2 * g) ^ xk) << 4));
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(kl + (((4 * s + 2 * g + 1) ^ xk) << 4));
+      return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      return *reinterpret_cast<const bf16x8_t*>(kl + (((2 * s + g) ^ xk) << 4));
+    }
+  };
+  auto smma = [&](const KFrag& a, int s, const f32x16_t& acc) __attribute__((always_inline)) -> f32x16_t {
+    if constexpr (kQ8) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[s], acc, 0, 0, 0, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc, 0, 0, 0);
+  };
   auto issue_s = [&](int buf, f32x16_t(&sa)[2]) __attribute__((always_inline)) {
-    const uint8_t* kl = kbuf(buf) + li * kKRow;
 #pragma unroll
-    for (int s = 0; s < G::kQSteps; ++s) {
+    for (int s = 0; s < kSSteps; ++s) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + kb * 32 * kKRow + (((2 * s + g) ^ xk) << 4));
-        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16_t{} : sa[kb], 0, 0, 0);
-      }
+      for (int kb = 0; kb < 2; ++kb) sa[kb] = smma(kread(buf, kb, s), s, s == 0 ? f32x16_t{} : sa[kb]);
     }
   };
   f32x16_t oacc[G::kDTiles];
@@ -777,21 +897,19 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
         const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vhi);
         return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       };
-      const uint8_t* kl = kbuf(nxt) + li * kKRow;
-      auto kfrag = [&](int f) __attribute__((always_inline)) {  // f = half * kQSteps + step
-        const int hh = f / G::kQSteps, st = f % G::kQSteps;
-        return *reinterpret_cast<const bf16x8_t*>(kl + hh * 32 * kKRow + (((2 * st + g) ^ xk) << 4));
+      auto kfrag = [&](int f) __attribute__((always_inline)) {  // f = half * kSSteps + step
+        return kread(nxt, f / kSSteps, f % kSSteps);
       };
       auto pv = [&](int dt, const i32x8_t& a) __attribute__((always_inline)) {
         oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pbuf[nxt], oacc[dt], 0, 0, 0, 0, 0, 0);
       };
-      auto smfma = [&](int f, const bf16x8_t& a) __attribute__((always_inline)) {
-        const int hh = f / G::kQSteps, st = f % G::kQSteps;
-        sacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], st == 0 ? f32x16_t{} : sacc[hh], 0, 0, 0);
+      auto smfma = [&](int f, const KFrag& a) __attribute__((always_inline)) {
+        const int hh = f / kSSteps, st = f % kSSteps;
+        sacc[hh] = smma(a, st, st == 0 ? f32x16_t{} : sacc[hh]);
       };
-      constexpr int kS = 2 * G::kQSteps;  // logit MFMAs
+      constexpr int kS = 2 * kSSteps;  // logit MFMAs
       i32x8_t vf[G::kDTiles];
-      bf16x8_t kf[kS];
+      KFrag kf[kS];
       float m4[4], ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       auto chain = [&](int q) __attribute__((always_inline)) {
         m4[q] = fmaxf(sacc[q / 2][(q % 2) * 8], sacc[q / 2][(q % 2) * 8 + 1]);
@@ -851,16 +969,18 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
       for (int f = 0; f < kS; ++f) {
         smfma(f, kf[f]);
         fetch(G::kDTiles + f + kAhead);
-        if (f < G::kQSteps) {
-          // second half's exponentials, 16 over kQSteps chunks, casts as they complete
-          constexpr int kPer = 16 / G::kQSteps;
+        if (f < kSSteps) {
+          // second half's exponentials, 16 over kSSteps chunks, each group of four
+          // cast as soon as it is complete
+          constexpr int kPer = 16 / kSSteps;
 #pragma unroll
           for (int r = 0; r < kPer; ++r) expo(1, f * kPer + r);
-          if (((f + 1) * kPer) % 4 == 0) cast(4 + ((f + 1) * kPer) / 4 - 1);
+#pragma unroll
+          for (int w = f * kPer / 4; w < (f + 1) * kPer / 4; ++w) cast(4 + w);
         } else {
-          const int k = f - G::kQSteps;
+          const int k = f - kSSteps;
           if constexpr (kStats) {
-            constexpr int kW = 8 / G::kQSteps;
+            constexpr int kW = 8 / kSSteps;
 #pragma unroll
             for (int e = 0; e < kW; ++e) {
               const int w = k * kW + e;
@@ -1009,11 +1129,16 @@ void launch_attn3(const Params& p, hipStream_t stream) {
       hipLaunchKernelGGL((pcast_attn_fwd_bf16<D, kCausal, true>), grid, dim3(kThreads), 0, stream, p);
     else
       hipLaunchKernelGGL((pcast_attn_fwd_bf16<D, kCausal, false>), grid, dim3(kThreads), 0, stream, p);
+  } else if (p.q8) {
+    if (p.stats)
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, true, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, false, true>), grid, dim3(kThreads), 0, stream, p);
   } else {
     if (p.stats)
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, true>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, true, false>), grid, dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, false, false>), grid, dim3(kThreads), 0, stream, p);
   }
 }
 
@@ -1036,6 +1161,24 @@ void launch_attn(const Params& p, int mode, int causal, hipStream_t stream) {
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
+// Workspace of the FP8-logit path, byte offsets from its start (each 256-aligned):
+// the V operand copy (as in the plain workspace), the E4M3 codes of Q and of K in
+// their own layouts, and the per-head max |Q| and max |K| (fp32 bits).
+struct Qk8Layout {
+  size_t q, k, amax_q, amax_k, total;
+};
+Qk8Layout qk8_layout(int B, int Hq, int Hkv, int N, int d) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t nkv = (size_t)B * Hkv * N * d, nq = (size_t)B * Hq * N * d;
+  Qk8Layout l;
+  l.q = up(nkv);
+  l.k = up(l.q + nq);
+  l.amax_q = up(l.k + nkv);
+  l.amax_k = up(l.amax_q + (size_t)B * Hq * 4);
+  l.total = up(l.amax_k + (size_t)B * Hkv * 4);
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1048,6 +1191,11 @@ size_t pcast_stats_words(int B, int Hq, int N) {
 size_t pcast_workspace_bytes(int B, int Hkv, int N, int d, float S) {
   if (B <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return 0;
   return (size_t)B * Hkv * N * d * ((S == 0.0f) ? 2 : 1);
+}
+
+size_t pcast_workspace_bytes_qk8(int B, int Hq, int Hkv, int N, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return 0;
+  return qk8_layout(B, Hq, Hkv, N, d).total;
 }
 
 int pcast_abi_version(void) { return PCAST_ABI_VERSION; }
@@ -1120,11 +1268,50 @@ int enqueue_prep(const void* V, int B, int Hkv, int N, int d, float S, void* ws,
   return e == hipSuccess ? PCAST_OK : hip_fail(e, "V pre-pass launch");
 }
 
+// Per-head max |x|, then the E4M3 codes of x * 2^-e, for x = Q and x = K.
+int enqueue_prep_qk8(const void* Q, const void* K, int B, int Hq, int Hkv, int N, int d, void* ws,
+                     hipStream_t st) {
+  const Qk8Layout l = qk8_layout(B, Hq, Hkv, N, d);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint32_t* amax_q = reinterpret_cast<uint32_t*>(base + l.amax_q);
+  uint32_t* amax_k = reinterpret_cast<uint32_t*>(base + l.amax_k);
+  const int n_words = (int)((l.total - l.amax_q) / 4);
+  hipLaunchKernelGGL(pcast_fill_u32, dim3((unsigned)((n_words + 255) / 256)), dim3(256), 0, st, amax_q, n_words);
+  const int64_t per_head = (int64_t)N * d;  // a multiple of 4096: N % 64 == 0, d >= 64
+  const unsigned chunks = (unsigned)((per_head + kAbsChunk - 1) / kAbsChunk);
+  const unsigned qblocks = (unsigned)(per_head / 4096);
+  const uint16_t* Qb = static_cast<const uint16_t*>(Q);
+  const uint16_t* Kb = static_cast<const uint16_t*>(K);
+  hipLaunchKernelGGL(pcast_absmax, dim3(chunks, (unsigned)(B * Hq)), dim3(256), 0, st, Qb, per_head, amax_q);
+  hipLaunchKernelGGL(pcast_absmax, dim3(chunks, (unsigned)(B * Hkv)), dim3(256), 0, st, Kb, per_head, amax_k);
+  hipLaunchKernelGGL(pcast_quant_fp8, dim3(qblocks, (unsigned)(B * Hq)), dim3(256), 0, st, Qb, per_head,
+                     (const uint32_t*)amax_q, base + l.q);
+  hipLaunchKernelGGL(pcast_quant_fp8, dim3(qblocks, (unsigned)(B * Hkv)), dim3(256), 0, st, Kb, per_head,
+                     (const uint32_t*)amax_k, base + l.k);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PCAST_OK : hip_fail(e, "Q/K pre-pass launch");
+}
+
+// Extra limits of the FP8-logit path: an FP8 P cast, and heads on the second grid axis.
+int check_qk8(int B, int Hq, float S) {
+  if (S == 0.0f) return fail(PCAST_ENOTSUP, "FP8 logits need S > 0 (the FP8 P.V path)");
+  if ((int64_t)B * Hq > 65535) return fail(PCAST_ENOTSUP, "B * Hq = %lld: at most 65535 heads", (long long)B * Hq);
+  return PCAST_OK;
+}
+
 int enqueue_attn(const void* Q, const void* K, const void* ws, const float* bias, int B, int Hq,
                  int Hkv, int N, int d, int causal, float S, int order, float* out,
-                 unsigned long long* stats, hipStream_t st) {
+                 unsigned long long* stats, hipStream_t st, bool qk8 = false) {
   const bool fp8 = S != 0.0f;
   Params p{};
+  if (qk8) {
+    const Qk8Layout l = qk8_layout(B, Hq, Hkv, N, d);
+    const uint8_t* base = static_cast<const uint8_t*>(ws);
+    p.q8 = base + l.q;
+    p.k8 = base + l.k;
+    p.amax_q = reinterpret_cast<const uint32_t*>(base + l.amax_q);
+    p.amax_k = reinterpret_cast<const uint32_t*>(base + l.amax_k);
+  }
   p.q = static_cast<const uint16_t*>(Q);
   p.k = static_cast<const uint16_t*>(K);
   p.vop = ws;
@@ -1194,6 +1381,62 @@ int attn_fwd_pcast(const void* Q, const void* K, const void* V, const float* bia
   if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
   rc = enqueue_prep(V, B, Hkv, N, d, S, ws, st);
   if (rc == PCAST_OK) rc = enqueue_attn(Q, K, ws, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats, st);
+  e = hipFreeAsync(ws, st);
+  if (rc != PCAST_OK) return rc;
+  if (e != hipSuccess) return hip_fail(e, "hipFreeAsync(workspace)");
+  return PCAST_OK;
+}
+
+int pcast_prepare_qk8(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int N, int d,
+                      void* workspace, void* stream) {
+  g_last_error[0] = '\0';
+  if (!Q || !K || !V || !workspace) return fail(PCAST_EINVAL, "Q, K, V and workspace must be non-null");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(workspace, 16))
+    return fail(PCAST_EINVAL, "Q, K, V and workspace must be 16-byte aligned");
+  int rc = check_shape(B, Hq, Hkv, N, d, 1.0f);
+  if (rc != PCAST_OK) return rc;
+  if ((rc = check_qk8(B, Hq, 1.0f)) != PCAST_OK) return rc;
+  if ((rc = check_device()) != PCAST_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = enqueue_prep(V, B, Hkv, N, d, 1.0f, workspace, st);
+  return rc != PCAST_OK ? rc : enqueue_prep_qk8(Q, K, B, Hq, Hkv, N, d, workspace, st);
+}
+
+int attn_fwd_pcast_qk8_prepared(const void* workspace, const float* bias, int B, int Hq, int Hkv, int N,
+                                int d, int causal, float S, int order, float* out,
+                                unsigned long long* stats, void* stream) {
+  g_last_error[0] = '\0';
+  if (!workspace) return fail(PCAST_EINVAL, "workspace must be non-null");
+  if (!aligned(workspace, 16)) return fail(PCAST_EINVAL, "workspace must be 16-byte aligned");
+  int rc = check_attn_args(workspace, workspace, bias, causal, order, out, stats);
+  if (rc != PCAST_OK) return rc;
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  if ((rc = check_qk8(B, Hq, S)) != PCAST_OK) return rc;
+  if ((rc = check_device()) != PCAST_OK) return rc;
+  return enqueue_attn(nullptr, nullptr, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
+                      static_cast<hipStream_t>(stream), true);
+}
+
+int attn_fwd_pcast_qk8(const void* Q, const void* K, const void* V, const float* bias, int B, int Hq,
+                       int Hkv, int N, int d, int causal, float S, int order, float* out,
+                       unsigned long long* stats, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_attn_args(Q, K, bias, causal, order, out, stats);
+  if (rc != PCAST_OK) return rc;
+  if (!V) return fail(PCAST_EINVAL, "V must be non-null");
+  if (!aligned(V, 16)) return fail(PCAST_EINVAL, "V must be 16-byte aligned");
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  if ((rc = check_qk8(B, Hq, S)) != PCAST_OK) return rc;
+  if ((rc = check_device()) != PCAST_OK) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, pcast_workspace_bytes_qk8(B, Hq, Hkv, N, d), st);
+  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
+  rc = enqueue_prep(V, B, Hkv, N, d, 1.0f, ws, st);
+  if (rc == PCAST_OK) rc = enqueue_prep_qk8(Q, K, B, Hq, Hkv, N, d, ws, st);
+  if (rc == PCAST_OK)
+    rc = enqueue_attn(nullptr, nullptr, ws, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats, st, true);
   e = hipFreeAsync(ws, st);
   if (rc != PCAST_OK) return rc;
   if (e != hipSuccess) return hip_fail(e, "hipFreeAsync(workspace)");

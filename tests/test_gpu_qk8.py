@@ -1,0 +1,197 @@
+"""GPU parity of the FP8-logit path (attn_fwd_pcast_qk8) against the oracle.
+
+The pre-passes are compared bit for bit with the oracle's quantisation
+(oracle.qk8): the per-head max |x| and the E4M3 code of every element of Q
+and K.  The attention output is compared with the oracle run on the
+dequantised Q and K, within the tolerance tests/_parity.compare_qk8 derives
+from the FP8 matrix cores' accumulation error.
+"""
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import e4m3, qk8
+from tests import _parity
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sna():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import softmax_numerics_amd
+    softmax_numerics_amd.load_library()
+    return softmax_numerics_amd
+
+
+def _up(x):
+    return (x + 255) // 256 * 256
+
+
+def _prepare(sna, qb, kb, vb):
+    B, Hq, N, d = qb.shape
+    Hkv = kb.shape[1]
+    q, k, v = (_parity.to_gpu_bf16(x) for x in (qb, kb, vb))
+    ws = torch.zeros(sna.workspace_bytes_qk8(B, Hq, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    rc = sna.prepare_qk8(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, N, d, ws.data_ptr(),
+                         torch.cuda.current_stream().cuda_stream)
+    assert rc == sna.PCAST_OK, sna.strerror(rc)
+    torch.cuda.synchronize()
+    w = ws.cpu().numpy()
+    nkv, nq = B * Hkv * N * d, B * Hq * N * d
+    off_q = _up(nkv)
+    off_k = _up(off_q + nq)
+    off_aq = _up(off_k + nkv)
+    off_ak = _up(off_aq + 4 * B * Hq)
+    parts = {"q8": w[off_q:off_q + nq].reshape(qb.shape), "k8": w[off_k:off_k + nkv].reshape(kb.shape),
+             "amax_q": w[off_aq:off_aq + 4 * B * Hq].view(np.uint32).reshape(B, Hq),
+             "amax_k": w[off_ak:off_ak + 4 * B * Hkv].view(np.uint32).reshape(B, Hkv)}
+    return parts
+
+
+def _check_prepass(parts, name, bits):
+    x = ((bits.astype(np.uint32) & 0xFFFF) << 16).view(np.float32).astype(np.float64)
+    amax = np.max(np.abs(x), axis=(2, 3)).astype(np.float32).view(np.uint32)
+    assert np.array_equal(parts["amax_" + name], amax), f"max |{name}| per head"
+    _, exps = qk8.quantize_heads(bits)
+    want = e4m3.e4m3_encode(np.ldexp(x, -exps[:, :, None, None]))
+    got = parts[name + "8"]
+    assert not np.any((got & 0x7F) == 0x7F), "NaN code"
+    # equal values (+0 and -0 are both zero to the matrix cores)
+    assert np.array_equal(e4m3.DECODE_TABLE[got], e4m3.DECODE_TABLE[want]), f"{name} codes"
+
+
+def _scaled_heads(B, H, N, d, seed, tensor_id):
+    """Gaussian heads at very different scales, with a zero head, an outlier
+    channel and a head whose max sits exactly on 448 * 2^k."""
+    bits = synthetic.gaussian_bf16(seed, tensor_id, (B, H, N, d))
+    x = ((bits.astype(np.uint32)) << 16).view(np.float32).reshape(B * H, N, d).copy()
+    scales = [1.0, 2.0 ** -20, 3.0e4, 0.0, 1.0, 7.5e-3, 1.0, 2.0 ** 40]
+    for i in range(B * H):
+        x[i] *= np.float32(scales[i % len(scales)])
+    if B * H > 4:
+        x[4, :, 5] *= 200.0                    # one outlier channel
+    if B * H > 6:
+        x[6] = np.clip(x[6], -3.0, 3.0)
+        x[6, 3, 7] = 448.0 * 2.0 ** -7       # amax exactly 448 * 2^-7 (= 3.5)
+    u = x.reshape(B, H, N, d).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)   # back to bf16, RNE
+
+
+def test_prepass_bit_exact(sna):
+    print("\n[case] qk8 pre-pass: B=2 Hq=4 Hkv=2 N=192 d=128", flush=True)
+    qb = _scaled_heads(2, 4, 192, 128, 41, 0)
+    kb = _scaled_heads(2, 2, 192, 128, 41, 1)
+    vb = synthetic.gaussian_bf16(41, 2, kb.shape)
+    parts = _prepare(sna, qb, kb, vb)
+    _check_prepass(parts, "q", qb)
+    _check_prepass(parts, "k", kb)
+
+
+def test_prepass_bit_exact_many_chunks(sna):
+    # N * d = 40 * 4096 elements per head: ten absmax workgroups per head, ragged
+    print("\n[case] qk8 pre-pass: B=1 Hq=8 Hkv=8 N=2560 d=64", flush=True)
+    qb = _scaled_heads(1, 8, 2560, 64, 42, 0)
+    kb = _scaled_heads(1, 8, 2560, 64, 42, 1)
+    vb = synthetic.gaussian_bf16(42, 2, kb.shape)
+    parts = _prepare(sna, qb, kb, vb)
+    _check_prepass(parts, "q", qb)
+    _check_prepass(parts, "k", kb)
+
+
+def _run_qk8(sna, qb, kb, vb, bias, causal, S, order, stats=True):
+    q, k, v = (_parity.to_gpu_bf16(x) for x in (qb, kb, vb))
+    bt = None if bias is None else torch.from_numpy(bias).cuda()
+    out, st = sna.forward(q, k, v, bt, causal=causal, S=S, order=order, stats=stats, qk_fp8=True)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (None if st is None else st.cpu().numpy())
+
+
+def _case(sna, name, B, Hq, Hkv, N, d, causal, bias, S, order, seed, blocks=None, qkv=None):
+    print(f"\n[case] qk8 {name}: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal} S={S} "
+          f"order={order} seed={seed}", flush=True)
+    qb, kb, vb = synthetic.qkv_bf16(B, Hq, Hkv, N, d, seed) if qkv is None else qkv
+    out, st = _run_qk8(sna, qb, kb, vb, bias, causal, S, order)
+    qd, _ = qk8.quantize_heads(qb)
+    kd, _ = qk8.quantize_heads(kb)
+    if isinstance(blocks, int):
+        blocks = _parity.sample_blocks(B, Hq, N, blocks, seed)
+    rep = _parity.compare_qk8(out, st, qd, kd, vb, bias, causal, S, order, blocks)
+    print(f"[case] qk8 {name}: {rep}", flush=True)
+    return rep
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("S", [1.0, 256.0, 448.0, 512.0])
+def test_small_grid(sna, d, causal, order, S):
+    # five key blocks, a half-empty last row block, grouped kv heads, sink bias 7
+    _case(sna, "grid", 2, 4, 2, 320, d, causal, synthetic.sink_bias(320, 7.0), S, order, 43)
+
+
+@pytest.mark.parametrize("order", [0, 1])
+def test_random_bias(sna, order):
+    _case(sna, "random bias", 1, 3, 3, 384, 128, True, synthetic.random_bias(384, 44), 256.0, order, 44)
+
+
+def test_scaled_heads(sna):
+    # heads at scales from 2^-20 to 2^40 and a zero head: the per-head exponents
+    # must cancel exactly in the logits
+    B, Hq, Hkv, N, d = 1, 8, 8, 256, 128
+    qb = _scaled_heads(B, Hq, N, d, 45, 0)
+    kb = np.ascontiguousarray(_scaled_heads(B, Hkv, N, d, 45, 1)[:, ::-1])
+    vb = synthetic.gaussian_bf16(45, 2, kb.shape)
+    # keep the logits moderate: a power of two per Q head brings max|q| max|k| near 30
+    qf = ((qb.astype(np.uint32)) << 16).view(np.float32)
+    kf = ((kb.astype(np.uint32)) << 16).view(np.float32)
+    for h in range(Hq):
+        aq = np.max(np.abs(qf[0, h])) or 1.0
+        ak = np.max(np.abs(kf[0, h])) or 1.0
+        qf[0, h] *= np.float32(2.0 ** np.round(np.log2(30.0 / aq / ak)))
+    qb = (qf.view(np.uint32) >> 16).astype(np.uint16)
+    _case(sna, "scaled heads", B, Hq, Hkv, N, d, True, None, 256.0, 1, 45, qkv=(qb, kb, vb))
+
+
+def test_single_block_orders_identical(sna):
+    print("\n[case] qk8 one key block, both orders", flush=True)
+    qb, kb, vb = synthetic.qkv_bf16(2, 2, 2, 64, 128, 46)
+    bias = synthetic.sink_bias(64, 7.0)
+    a, sa = _run_qk8(sna, qb, kb, vb, bias, True, 256.0, 0)
+    b, sb = _run_qk8(sna, qb, kb, vb, bias, True, 256.0, 1)
+    assert np.array_equal(a, b) and np.array_equal(sa, sb)
+
+
+def test_deterministic(sna):
+    print("\n[case] qk8 determinism", flush=True)
+    qb, kb, vb = synthetic.qkv_bf16(1, 4, 4, 1024, 128, 47)
+    bias = synthetic.sink_bias(1024, 7.0)
+    a, sa = _run_qk8(sna, qb, kb, vb, bias, True, 256.0, 1)
+    b, sb = _run_qk8(sna, qb, kb, vb, bias, True, 256.0, 1)
+    c, _ = _run_qk8(sna, qb, kb, vb, bias, True, 256.0, 1, stats=False)
+    assert np.array_equal(a, b) and np.array_equal(sa, sb) and np.array_equal(a, c)
+
+
+def test_zero_scale_is_rejected(sna):
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sna.PcastError) as ei:
+        sna.forward(q, q, q, None, S=0.0, qk_fp8=True)
+    assert ei.value.code == sna.PCAST_ENOTSUP
+
+
+W = synthetic.WORKLOADS
+
+
+@pytest.mark.parametrize("S,order", [(256.0, 1), (1.0, 0)])
+def test_throughput_full_size(sna, S, order):
+    w = W["throughput"]
+    _case(sna, "throughput", w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, synthetic.sink_bias(w.N, 7.0), S, order,
+          w.seed, blocks=8)
+
+
+def test_gqa_full_size(sna):
+    w = W["gqa"]
+    _case(sna, "gqa", w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, synthetic.sink_bias(w.N, 7.0), 256.0, 1,
+          w.seed, blocks=6)
