@@ -1,18 +1,23 @@
-"""FP8 logits, an extension of the P-cast path: Q and K rounded to E4M3 with a
-per-head power-of-two scale before Q K^T.
+"""FP8 logits, an extension of the P-cast path: Q and K rounded to E4M3 with
+power-of-two block scales before Q K^T.
 
 TEST INFRASTRUCTURE: only the tests, the smoke check and the CPU-baseline leg of
 the benchmark use this package.
 
-The FlashAttention blog ("FA3: Meccanica della tramoggia") names FP8 inputs
-with a per-block descale as the way to the FP8 matrix rate; the P-cast summaries
-only cast P.  Reading taken here (the plainest one that keeps every step exact):
+The FlashAttention blog ("FA3: Meccanica della tramoggia", item 3) describes
+FP8 attention inputs quantised block by block, one scale per block; the P-cast
+summaries only cast P.  Reading taken here (the plainest one that keeps every
+step exact):
 
-* the scale of a head is the smallest power of two 2^e with max|x| <= 448 * 2^e,
-  so x / 2^e is exact in fp32 and no value saturates; a head of zeros takes e = 0;
-* a value enters the logits as E4M3_RNE(x / 2^e) * 2^e.  With 3 mantissa bits and
-  an exponent well inside bf16's range that product is exactly a bf16 value, so
-  the rest of the oracle runs unchanged on the quantised Q and K.
+* blocks: every query row is a block of Q (the finest block of rows), and every
+  64-key block of a head is a block of K (the key block of the online softmax);
+* the scale of a block is the smallest power of two 2^e with
+  max|x| <= 448 * 2^e over the block, so x / 2^e is exact and no value
+  saturates; a block of zeros takes e = 0;
+* a value enters the logits as E4M3_RNE(x / 2^e) * 2^e.  With 3 mantissa bits
+  and an exponent well inside bf16's range that product is exactly a bf16
+  value, so the rest of the oracle runs unchanged on the quantised Q and K, and
+  the logit of (i, j) is sum_d code_q * code_k * 2^(e_i + e_block(j)) / sqrt(d).
 """
 from __future__ import annotations
 
@@ -21,6 +26,9 @@ import math
 import numpy as np
 
 from .e4m3 import E4M3_MAX, e4m3_rne
+
+Q_BLOCK_ROWS = 1    # one scale per query row
+K_BLOCK_ROWS = 64   # one scale per key block
 
 
 def head_scale_exp(amax: float) -> int:
@@ -46,20 +54,38 @@ def _f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return (u >> 16).astype(np.uint16)
 
 
-def quantize_heads(bits: np.ndarray):
-    """Quantise a bf16 tensor [B, H, N, d] head by head.
+def scale_exps(amax) -> np.ndarray:
+    """head_scale_exp applied elementwise to an array of maxima."""
+    a = np.asarray(amax, dtype=np.float64)
+    m, E = np.frexp(a)
+    e = np.where(m <= 0.875, E - 9, E - 8)
+    return np.where(a == 0.0, 0, e).astype(np.int64)
 
-    Returns (bf16 bits of E4M3_RNE(x / 2^e) * 2^e, exponents e [B, H]).
+
+def quantize_blocks(bits: np.ndarray, rows: int):
+    """Quantise a bf16 tensor [B, H, N, d] in blocks of `rows` consecutive rows
+    of one head (N % rows == 0).
+
+    Returns (bf16 bits of E4M3_RNE(x / 2^e) * 2^e, exponents e [B, H, N / rows]).
     """
     x = _bf16_bits_to_f64(bits)
-    B, H = x.shape[:2]
-    exps = np.zeros((B, H), dtype=np.int64)
-    out = np.empty_like(x)
-    for b in range(B):
-        for h in range(H):
-            e = head_scale_exp(np.max(np.abs(x[b, h])))
-            exps[b, h] = e
-            q = e4m3_rne(np.ldexp(x[b, h], -e))
-            assert np.max(np.abs(q)) <= E4M3_MAX
-            out[b, h] = np.ldexp(q, e)
+    B, H, N, d = x.shape
+    if N % rows:
+        raise ValueError("N must be a multiple of the block rows")
+    blocks = x.reshape(B, H, N // rows, rows * d)
+    exps = scale_exps(np.max(np.abs(blocks), axis=3))
+    e = exps[..., None]
+    q = e4m3_rne(np.ldexp(blocks, -e))
+    assert q.size == 0 or np.max(np.abs(q)) <= E4M3_MAX
+    out = np.ldexp(q, e).reshape(x.shape)
     return _f64_to_bf16_bits(out).reshape(np.shape(bits)), exps
+
+
+def quantize_q(bits: np.ndarray):
+    """Q with one scale per row: (dequantised bf16 bits, exponents [B, H, N])."""
+    return quantize_blocks(bits, Q_BLOCK_ROWS)
+
+
+def quantize_k(bits: np.ndarray):
+    """K with one scale per 64-key block: (dequantised bf16 bits, exponents [B, H, N/64])."""
+    return quantize_blocks(bits, K_BLOCK_ROWS)

@@ -1,16 +1,19 @@
-"""Pins for the FP8-logits extension of the oracle (Q and K in E4M3 with a
-per-head power-of-two scale).
+"""Pins for the FP8-logits extension of the oracle (Q and K in E4M3 with
+power-of-two block scales: one per query row, one per 64-key block).
 
 What pins it:
 * the scale rule against its definition by brute force (smallest e with
-  max|x| <= 448 * 2^e), at the boundaries 448 * 2^k and between them;
+  max|x| <= 448 * 2^e), at the boundaries 448 * 2^k and between them, and the
+  array form against the scalar one;
 * quantised values lie on the scaled E4M3 grid, never saturate, are exactly
-  bf16-representable, and quantising twice changes nothing;
-* Q and K already on the E4M3 grid with max|x| = 448 quantise to themselves, so
-  the oracle's output is unchanged bit for bit;
+  bf16-representable, are the RNE points, and quantising twice changes nothing;
+* blocks are independent: scaling one block by 2^k moves its exponent by k and
+  leaves every other block as it was;
+* Q and K already on the E4M3 grid with max|x| = 448 in every block quantise to
+  themselves, so the oracle's output is unchanged bit for bit;
 * the logits computed from the quantised tensors equal the sum of E4M3 code
-  products times 2^(e_q + e_k) / sqrt(d), written out by hand on a small case;
-* a planted mistake (dropping the scale) fails the round-trip pin.
+  products times 2^(e_i + e_block(j)) / sqrt(d), written out by hand;
+* planted mistakes (no scale; one scale per head) fail the pins.
 """
 import math
 
@@ -38,63 +41,135 @@ def test_scale_exp_definition_random():
     assert qk8.head_scale_exp(0.0) == 0
 
 
-def test_quantised_values_on_scaled_grid():
+def test_scale_exps_matches_scalar_rule():
+    rng = np.random.default_rng(5)
+    a = np.concatenate([np.exp(rng.uniform(-40, 20, 3000)), [0.0],
+                        448.0 * 2.0 ** np.arange(-20, 10.0), np.nextafter(448.0 * 2.0 ** np.arange(-20, 10.0), 1e9)])
+    assert np.array_equal(qk8.scale_exps(a), [qk8.head_scale_exp(x) for x in a])
+
+
+@pytest.mark.parametrize("rows", [1, 64, 256])
+def test_quantised_values_on_scaled_grid(rows):
     q, _, _ = synthetic.qkv_bf16(2, 3, 3, 256, 64, 41)
-    qq, exps = qk8.quantize_heads(q)
+    qq, exps = qk8.quantize_blocks(q, rows)
+    assert exps.shape == (2, 3, 256 // rows)
     x = reference.bf16_to_f64(q)
     y = reference.bf16_to_f64(qq)
     grid = e4m3.grid()
     for b in range(2):
         for h in range(3):
-            e = int(exps[b, h])
-            assert np.max(np.abs(x[b, h])) <= 448.0 * 2.0 ** e
-            z = np.abs(np.ldexp(y[b, h], -e))
-            assert z.max() <= 448.0
-            assert np.all(np.isin(z, grid))
-            # the nearest grid point: |x/2^e - z| is at most half a grid step
-            assert np.array_equal(np.ldexp(y[b, h], -e), e4m3.e4m3_rne(np.ldexp(x[b, h], -e)))
-    q2, e2 = qk8.quantize_heads(qq)
-    assert np.array_equal(q2, qq) and np.array_equal(e2, exps)
+            for r in range(256 // rows):
+                sl = slice(r * rows, (r + 1) * rows)
+                e = int(exps[b, h, r])
+                amax = np.max(np.abs(x[b, h, sl]))
+                assert amax <= 448.0 * 2.0 ** e and amax > 448.0 * 2.0 ** (e - 1)
+                z = np.abs(np.ldexp(y[b, h, sl], -e))
+                assert z.max() <= 448.0
+                assert np.all(np.isin(z, grid))
+                # the nearest grid point: |x/2^e - z| is at most half a grid step
+                assert np.array_equal(np.ldexp(y[b, h, sl], -e), e4m3.e4m3_rne(np.ldexp(x[b, h, sl], -e)))
+    # quantising again changes no value; a block's exponent drops by one exactly
+    # when its max rounded down onto 448 * 2^(e-1)
+    q2, e2 = qk8.quantize_blocks(qq, rows)
+    assert np.array_equal(q2, qq)
+    ymax = np.max(np.abs(y.reshape(2, 3, 256 // rows, -1)), axis=3)
+    drop = e2 != exps
+    assert np.all(e2[drop] == exps[drop] - 1)
+    assert np.all(ymax[drop] == 448.0 * 2.0 ** (exps[drop] - 1.0))
+
+
+def test_named_granularities():
+    q, k, _ = synthetic.qkv_bf16(1, 2, 2, 128, 64, 45)
+    assert qk8.Q_BLOCK_ROWS == 1 and qk8.K_BLOCK_ROWS == 64
+    for f, rows in ((qk8.quantize_q, 1), (qk8.quantize_k, 64)):
+        a, ea = f(q)
+        b, eb = qk8.quantize_blocks(q, rows)
+        assert np.array_equal(a, b) and np.array_equal(ea, eb)
+
+
+@pytest.mark.parametrize("rows", [1, 64])
+def test_blocks_are_independent(rows):
+    q, _, _ = synthetic.qkv_bf16(1, 2, 2, 256, 64, 46)
+    base, e0 = qk8.quantize_blocks(q, rows)
+    x = reference.bf16_to_f64(q).copy()
+    blk = 1 if rows == 64 else 77                  # one block of head 1
+    sl = slice(blk * rows, (blk + 1) * rows)
+    x[0, 1, sl] *= 2.0 ** 9
+    bits = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    moved, e1 = qk8.quantize_blocks(bits, rows)
+    diff = e1 - e0
+    assert diff[0, 1, blk] == 9 and np.count_nonzero(diff) == 1
+    y0, y1 = reference.bf16_to_f64(base), reference.bf16_to_f64(moved)
+    assert np.array_equal(y1[0, 1, sl], y0[0, 1, sl] * 2.0 ** 9)
+    y1[0, 1, sl] = y0[0, 1, sl]
+    assert np.array_equal(y1, y0)
 
 
 def test_grid_inputs_unchanged():
-    """Q, K drawn from the E4M3 grid with max |x| = 448: quantisation is the identity."""
+    """Q, K drawn from the E4M3 grid with max |x| = 448 in every row: quantisation
+    is the identity at both granularities."""
     rng = np.random.default_rng(1)
     grid = e4m3.grid()
     shape = (1, 2, 128, 64)
     vals = rng.choice(np.concatenate([-grid, grid]), size=shape)
-    vals[..., 0, 0] = 448.0
+    vals[..., 0] = 448.0
     bits = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
-    qq, exps = qk8.quantize_heads(bits)
-    assert np.array_equal(qq, bits) and np.all(exps == 0)
+    qq, eq = qk8.quantize_q(bits)
+    kq, ek = qk8.quantize_k(bits)
+    assert np.array_equal(qq, bits) and np.all(eq == 0)
+    assert np.array_equal(kq, bits) and np.all(ek == 0)
     _, _, v = synthetic.qkv_bf16(1, 2, 2, 128, 64, 42)
     bias = synthetic.sink_bias(128, 7.0)
     a = core.rows(bits, bits, v, bias, True, 256.0, 1, "kernel")
-    b = core.rows(qq, qq, v, bias, True, 256.0, 1, "kernel")
+    b = core.rows(qq, kq, v, bias, True, 256.0, 1, "kernel")
     assert np.array_equal(a["o2"], b["o2"]) and np.array_equal(a["zero"], b["zero"])
 
 
 def test_logits_are_scaled_code_products():
-    q, k, _ = synthetic.qkv_bf16(1, 1, 1, 16, 32, 43)
-    qq, eq = qk8.quantize_heads(q)
-    kq, ek = qk8.quantize_heads(k)
+    q, k, _ = synthetic.qkv_bf16(1, 1, 1, 128, 32, 43)
+    xq = reference.bf16_to_f64(q).copy()
+    xk = reference.bf16_to_f64(k).copy()
+    xq[0, 0, ::3] *= 2.0 ** -5                    # rows at different scales
+    xk[0, 0, 64:] *= 2.0 ** 6                     # the second key block larger
+    q = (xq.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    k = (xk.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    qq, eq = qk8.quantize_q(q)
+    kq, ek = qk8.quantize_k(k)
+    assert len(set(eq[0, 0].tolist())) > 1 and ek[0, 0, 1] - ek[0, 0, 0] >= 5
     s = reference.logits(reference.bf16_to_f64(qq[0, 0]), reference.bf16_to_f64(kq[0, 0]), None, False)
     # by hand: decode the E4M3 codes, multiply, sum, then scale
-    cq = e4m3.e4m3_encode(np.ldexp(reference.bf16_to_f64(q[0, 0]), -int(eq[0, 0])))
-    ck = e4m3.e4m3_encode(np.ldexp(reference.bf16_to_f64(k[0, 0]), -int(ek[0, 0])))
-    dq, dk = e4m3.DECODE_TABLE[cq], e4m3.DECODE_TABLE[ck]
-    for i in range(16):
-        for j in range(16):
+    rows = [0, 1, 5, 63, 64, 127]
+    for i in rows:
+        cq = e4m3.e4m3_encode(np.ldexp(xq[0, 0, i], -int(eq[0, 0, i])))
+        for j in rows:
+            ck = e4m3.e4m3_encode(np.ldexp(xk[0, 0, j], -int(ek[0, 0, j // 64])))
             acc = 0.0
             for c in range(32):
-                acc += dq[i, c] * dk[j, c]
-            expect = acc * 2.0 ** (int(eq[0, 0]) + int(ek[0, 0])) / math.sqrt(32)
+                acc += e4m3.DECODE_TABLE[cq[c]] * e4m3.DECODE_TABLE[ck[c]]
+            expect = acc * 2.0 ** (int(eq[0, 0, i]) + int(ek[0, 0, j // 64])) / math.sqrt(32)
             assert abs(s[i, j] - expect) <= 1e-12 * max(1.0, abs(expect))
 
 
 def test_planted_missing_scale_is_caught():
     q, _, _ = synthetic.qkv_bf16(1, 1, 1, 64, 32, 44)
     x = reference.bf16_to_f64(q)
-    wrong = e4m3.e4m3_rne(x)                 # no per-head scale: |x| < 448 so nothing saturates,
-    qq, _ = qk8.quantize_heads(q)            # but the grid is far too coarse near zero
+    wrong = e4m3.e4m3_rne(x)                 # no scale: |x| < 448 so nothing saturates,
+    qq, _ = qk8.quantize_q(q)                # but the grid is far too coarse near zero
     assert not np.array_equal(wrong, reference.bf16_to_f64(qq))
+
+
+def test_planted_head_scale_is_caught():
+    """One scale for the whole head instead of one per row: rows far below the
+    head's max fall into E4M3's subnormal range and lose precision."""
+    q, _, _ = synthetic.qkv_bf16(1, 1, 1, 64, 32, 47)
+    x = reference.bf16_to_f64(q).copy()
+    x[0, 0, 1::2] *= 2.0 ** -16
+    bits = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    per_head, _ = qk8.quantize_blocks(bits, 64)
+    per_row, _ = qk8.quantize_q(bits)
+    err_head = np.abs(reference.bf16_to_f64(per_head) - x)[0, 0, 1::2]
+    err_row = np.abs(reference.bf16_to_f64(per_row) - x)[0, 0, 1::2]
+    assert not np.array_equal(per_head, per_row)
+    # per row: relative error at most 2^-4 (3 mantissa bits, no subnormals at these maxima)
+    assert np.all(err_row <= 2.0 ** -4 * np.abs(x[0, 0, 1::2]) + 1e-300)
+    assert np.sum(err_head ** 2) > 100 * np.sum(err_row ** 2)
