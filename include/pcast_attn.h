@@ -118,45 +118,46 @@ int attn_fwd_pcast_prepared(const void* Q, const void* K, const void* workspace,
 /*
  * The forward with FP8 logits: Q and K rounded to E4M3 as well, so that Q K^T
  * runs on the FP8 matrix cores too (FlashAttention blog by marketmaker.cc,
- * section "FA3: Meccanica della tramoggia", item 3: FP8 attention with
- * block-wise scaled Q and K; the P-cast summary on gist.science, closing
- * remarks, names Q/K/V quantisation as the noise that may outweigh the P-cast
- * gain).  This path has no random rotation: one scale per head.
+ * section "FA3: Meccanica della tramoggia", item 3: FP8 attention inputs
+ * quantised block by block, one scale per block; the P-cast summary on
+ * gist.science, closing remarks, names Q/K/V quantisation as the noise that
+ * may outweigh the P-cast gain).  This path has no random rotation.
  *
- * Each (batch, head) of Q and of K gets its own power-of-two scale 2^e, the
- * smallest with max|x| <= 448 * 2^e over that head; the codes are
- * E4M3(x * 2^-e) (round to nearest even; the choice of e keeps them in range,
- * so none saturates).  The kernel multiplies the fp32 accumulation of the
- * code products by 2^(e_q + e_k) / sqrt(d), which is exact, so the logits are
- * those of the rounded Q and K up to the matrix cores' accumulation.  Softmax,
- * P-cast, V and the epilogue are as in attn_fwd_pcast.  Inputs must be finite.
+ * Blocks: each query row of Q, and each 64-key block of each head of K.  The
+ * scale of a block is the smallest power of two 2^e with max|x| <= 448 * 2^e
+ * over the block; the codes are E4M3(x * 2^-e) (round to nearest even; the
+ * choice of e keeps them in range, so none saturates).  The logit of (i, j)
+ * is the fp32 accumulation of the code products times 2^(e_i + e_block(j)) /
+ * sqrt(d), which is exact, so the logits are those of the rounded Q and K up
+ * to the matrix cores' accumulation.  Softmax, P-cast, V and the epilogue are
+ * as in attn_fwd_pcast.  Inputs must be finite.
  *
- * pcast_workspace_bytes_qk8 -- bytes of the workspace: the V operand copy,
- * the codes of Q and of K, and the per-head maxima, 256-byte aligned each.
+ * pcast_workspace_bytes_qk8 -- bytes of the workspace: the V operand copy, the
+ * codes of K and the exponents of the key blocks, 256-byte aligned each.
  *
- * pcast_prepare_qk8 -- enqueue the pre-passes that fill that workspace from Q,
- * K and V (bf16, layouts as for attn_fwd_pcast, 16-byte aligned).  The
- * workspace (16-byte aligned, owned by the caller) is overwritten.
+ * pcast_prepare_qk8 -- enqueue the pre-pass that fills that workspace from K
+ * and V (bf16 [B][Hkv][N][d], 16-byte aligned), one key block per workgroup.
+ * The workspace (16-byte aligned, owned by the caller) is overwritten.  Q
+ * needs no pre-pass: the attention kernel rounds each row as it loads it.
  *
- * attn_fwd_pcast_qk8_prepared -- enqueue the attention kernel on a workspace
- * that pcast_prepare_qk8 filled with the same B, Hq, Hkv, N, d (stream order,
- * or other synchronisation, must complete the pre-passes first).  Allocates
- * nothing.
+ * attn_fwd_pcast_qk8_prepared -- enqueue the attention kernel reading Q (bf16,
+ * as for attn_fwd_pcast) and a workspace that pcast_prepare_qk8 filled with
+ * the same B, Hkv, N, d (stream order, or other synchronisation, must
+ * complete the pre-pass first).  Allocates nothing.
  *
  * attn_fwd_pcast_qk8 -- both, with a workspace from HIP's stream-ordered
  * allocator on `stream`, released on the same stream.
  *
  * Arguments, results and errors as for attn_fwd_pcast, and further: S must be
- * > 0 (PCAST_ENOTSUP for S = 0, which has no FP8 P.V), and B * Hq <= 65535
- * (PCAST_ENOTSUP beyond).
+ * > 0 (PCAST_ENOTSUP for S = 0, which has no FP8 P.V).
  */
-size_t pcast_workspace_bytes_qk8(int B, int Hq, int Hkv, int N, int d);
+size_t pcast_workspace_bytes_qk8(int B, int Hkv, int N, int d);
 
-int pcast_prepare_qk8(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int N, int d,
-                      void* workspace, void* stream);
+int pcast_prepare_qk8(const void* K, const void* V, int B, int Hkv, int N, int d, void* workspace,
+                      void* stream);
 
-int attn_fwd_pcast_qk8_prepared(const void* workspace, const float* bias, int B, int Hq, int Hkv, int N,
-                                int d, int causal, float S, int order, float* out,
+int attn_fwd_pcast_qk8_prepared(const void* Q, const void* workspace, const float* bias, int B, int Hq,
+                                int Hkv, int N, int d, int causal, float S, int order, float* out,
                                 unsigned long long* stats, void* stream);
 
 int attn_fwd_pcast_qk8(const void* Q, const void* K, const void* V, const float* bias, int B, int Hq,

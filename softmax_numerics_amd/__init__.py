@@ -58,11 +58,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.pcast_strerror.restype = ctypes.c_char_p
             lib.pcast_abi_version.argtypes = []
             lib.pcast_abi_version.restype = I
-            lib.pcast_workspace_bytes_qk8.argtypes = [I, I, I, I, I]
+            lib.pcast_workspace_bytes_qk8.argtypes = [I, I, I, I]
             lib.pcast_workspace_bytes_qk8.restype = ctypes.c_size_t
-            lib.pcast_prepare_qk8.argtypes = [P, P, P, I, I, I, I, I, P, P]
+            lib.pcast_prepare_qk8.argtypes = [P, P, I, I, I, I, P, P]
             lib.pcast_prepare_qk8.restype = I
-            lib.attn_fwd_pcast_qk8_prepared.argtypes = [P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P]
+            lib.attn_fwd_pcast_qk8_prepared.argtypes = [P, P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P,
+                                                        P]
             lib.attn_fwd_pcast_qk8_prepared.restype = I
             lib.attn_fwd_pcast_qk8.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P]
             lib.attn_fwd_pcast_qk8.restype = I
@@ -99,21 +100,21 @@ def attn_fwd_pcast_qk8(Q, K, V, bias, B, Hq, Hkv, N, d, causal, S, order, out, s
                                                  float(S), int(order), out, stats or None, stream or None))
 
 
-def prepare_qk8(Q, K, V, B, Hq, Hkv, N, d, workspace, stream) -> int:
+def prepare_qk8(K, V, B, Hkv, N, d, workspace, stream) -> int:
     """Raw pcast_prepare_qk8 with integer device addresses; returns the C return code."""
-    return int(load_library().pcast_prepare_qk8(Q, K, V, B, Hq, Hkv, N, d, workspace, stream or None))
+    return int(load_library().pcast_prepare_qk8(K, V, B, Hkv, N, d, workspace, stream or None))
 
 
-def attn_fwd_pcast_qk8_prepared(workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
+def attn_fwd_pcast_qk8_prepared(Q, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
                                 stream) -> int:
     """Raw attn_fwd_pcast_qk8_prepared with integer device addresses; returns the C return code."""
     return int(load_library().attn_fwd_pcast_qk8_prepared(
-        workspace, bias or None, B, Hq, Hkv, N, d, int(causal), float(S), int(order), out,
+        Q, workspace, bias or None, B, Hq, Hkv, N, d, int(causal), float(S), int(order), out,
         stats or None, stream or None))
 
 
-def workspace_bytes_qk8(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
-    return int(load_library().pcast_workspace_bytes_qk8(B, Hq, Hkv, N, d))
+def workspace_bytes_qk8(B: int, Hkv: int, N: int, d: int) -> int:
+    return int(load_library().pcast_workspace_bytes_qk8(B, Hkv, N, d))
 
 
 def stats_words(B: int, Hq: int, N: int) -> int:
@@ -130,8 +131,8 @@ def forward(q, k, v, bias=None, causal: bool = True, S: float = 256.0, order="re
 
     q: bf16 [B, Hq, N, d]; k, v: bf16 [B, Hkv, N, d]; bias: fp32 [N] or None.
     S > 0: P*S cast to E4M3; S = 0: the bf16 reference path.  qk_fp8: Q and K
-    rounded to E4M3 with a power-of-two scale per head, logits on the FP8
-    matrix cores (needs S > 0).  Returns (out fp32 [B, Hq, N, d], stats int64
+    rounded to E4M3 with power-of-two scales per query row and per 64-key
+    block, logits on the FP8 matrix cores (needs S > 0).  Returns (out fp32 [B, Hq, N, d], stats int64
     [B, Hq, N/64, 2] or None).
     """
     import torch

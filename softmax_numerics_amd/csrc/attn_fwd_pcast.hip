@@ -86,11 +86,9 @@ struct Swizzle {
 // in slot order, E4M3 (RNE, saturating) or bf16.
 // ---------------------------------------------------------------------------
 template <int D, bool kFp8>
-__global__ __launch_bounds__(256) void pcast_prep_v(const uint16_t* __restrict__ V,
-                                                     void* __restrict__ vop) {
+__device__ inline void prep_v_block(const uint16_t* __restrict__ V, void* __restrict__ vop, int64_t blk) {
   __shared__ uint16_t tile[kKvBlock][D + 2];
   const int tid = threadIdx.x;
-  const int64_t blk = blockIdx.x;  // flat (b, hkv, key block)
   const uint16_t* src = V + blk * kKvBlock * D;
   for (int c = tid; c < kKvBlock * D / 8; c += 256) {
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
@@ -130,79 +128,82 @@ __global__ __launch_bounds__(256) void pcast_prep_v(const uint16_t* __restrict__
   }
 }
 
-// ---------------------------------------------------------------------------
-// FP8 logits (an extension of the P-cast path): Q and K rounded to E4M3 with a
-// per-head power-of-two scale.  The scale of a head is the smallest 2^e with
-// max|x| <= 448 * 2^e, so x * 2^-e is exact and never exceeds 448.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void pcast_fill_u32(uint32_t* __restrict__ p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0u;
+template <int D, bool kFp8>
+__global__ __launch_bounds__(256) void pcast_prep_v(const uint16_t* __restrict__ V,
+                                                     void* __restrict__ vop) {
+  prep_v_block<D, kFp8>(V, vop, blockIdx.x);  // one (b, hkv, key block) per workgroup
 }
 
-// max |x| of each head of a bf16 tensor [heads][per_head] as fp32 bits (bf16 bits
-// << 16; for values >= 0 the integer order is the float order).  Grid: (chunks,
-// heads), 16 elements per thread and kAbsChunk per workgroup.
-constexpr int kAbsChunk = 256 * 16 * 4;
-__global__ __launch_bounds__(256) void pcast_absmax(const uint16_t* __restrict__ x, int64_t per_head,
-                                                    uint32_t* __restrict__ amax) {
-  const int64_t head = blockIdx.y;
-  const int64_t base = head * per_head + (int64_t)blockIdx.x * kAbsChunk;
-  const int64_t end = min((int64_t)kAbsChunk, per_head - (int64_t)blockIdx.x * kAbsChunk);
+// ---------------------------------------------------------------------------
+// FP8 logits (an extension of the P-cast path): Q and K rounded to E4M3 with a
+// power-of-two scale per block -- per query row for Q, per 64-key block for K.
+// The scale of a block is the smallest 2^e with max|x| <= 448 * 2^e, so
+// x * 2^-e is exact and never exceeds 448, and the E4M3 conversion (RNE) never
+// saturates.
+// ---------------------------------------------------------------------------
+__device__ inline int scale_exp(uint32_t amax_bits) {  // amax as fp32 bits
+  const float a = __builtin_bit_cast(float, amax_bits);
+  if (a == 0.0f) return 0;
+  int E;
+  const float m = frexpf(a, &E);  // a = m * 2^E, m in [0.5, 1); 448 = 0.875 * 2^9
+  return m <= 0.875f ? E - 9 : E - 8;
+}
+
+// max |x| over the 8 bf16 values in w, as fp32 bits (bf16 bits << 16 order as floats)
+__device__ inline uint32_t absmax8(const i32x4_t w) {
   uint32_t m = 0;
-  for (int64_t i = (int64_t)threadIdx.x * 8; i < end; i += 256 * 8) {
-    const i32x4_t v = *reinterpret_cast<const i32x4_t*>(x + base + i);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t w = (uint32_t)v[e];
-      m = max(m, max(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
-    }
+  for (int e = 0; e < 4; ++e) m = max(m, max((uint32_t)w[e] & 0x7FFFu, ((uint32_t)w[e] >> 16) & 0x7FFFu));
+  return m << 16;
+}
+
+// E4M3 codes of x * 2^-e for the 8 bf16 values in w, in order, 4 per word
+__device__ inline void codes8(const i32x4_t w, int e, int& lo, int& hi) {
+  float f[8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f[2 * t] = ldexpf(__builtin_bit_cast(float, (uint32_t)w[t] << 16), -e);
+    f[2 * t + 1] = ldexpf(__builtin_bit_cast(float, (uint32_t)w[t] & 0xFFFF0000u), -e);
+  }
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+}
+
+// One key block of K per workgroup: the block's exponent e and the codes of
+// K * 2^-e, [B][Hkv][N][D] bytes, plus the V operand copy of the same block.
+template <int D>
+__global__ __launch_bounds__(256) void pcast_prep_kv8(const uint16_t* __restrict__ K,
+                                                      const uint16_t* __restrict__ V,
+                                                      uint8_t* __restrict__ vop, uint8_t* __restrict__ k8,
+                                                      int* __restrict__ kexp) {
+  constexpr int kChunks = kKvBlock * D / 8 / 256;  // 16-byte chunks per thread
+  const int tid = threadIdx.x;
+  const int64_t blk = blockIdx.x;  // flat (b, hkv, key block)
+  const uint16_t* src = K + blk * kKvBlock * D;
+  i32x4_t w[kChunks];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    w[i] = *reinterpret_cast<const i32x4_t*>(src + (i * 256 + tid) * 8);
+    m = max(m, absmax8(w[i]));
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
   __shared__ uint32_t part[4];
-  if (threadIdx.x % 64 == 0) part[threadIdx.x / 64] = m;
+  if (tid % 64 == 0) part[tid / 64] = m;
   __syncthreads();
-  if (threadIdx.x == 0) atomicMax(amax + head, max(max(part[0], part[1]), max(part[2], part[3])) << 16);
-}
-
-// the head's scale exponent from its max |x| (fp32 bits): smallest e with
-// amax <= 448 * 2^e, 448 = 0.875 * 2^9
-__device__ inline int scale_exp(uint32_t amax_bits) {
-  const float a = __builtin_bit_cast(float, amax_bits);
-  if (a == 0.0f) return 0;
-  int E;
-  const float m = frexpf(a, &E);
-  return m <= 0.875f ? E - 9 : E - 8;
-}
-
-// E4M3 codes of x * 2^-e (RNE; |x * 2^-e| <= 448 by the choice of e), 16 per thread.
-__global__ __launch_bounds__(256) void pcast_quant_fp8(const uint16_t* __restrict__ x, int64_t per_head,
-                                                       const uint32_t* __restrict__ amax,
-                                                       uint8_t* __restrict__ out) {
-  const int64_t head = blockIdx.y;
-  const int64_t i = (int64_t)blockIdx.x * (256 * 16) + (int64_t)threadIdx.x * 16;
-  if (i >= per_head) return;
-  const int e = scale_exp(amax[head]);
-  const uint16_t* src = x + head * per_head + i;
-  const i32x4_t a = *reinterpret_cast<const i32x4_t*>(src);
-  const i32x4_t b = *reinterpret_cast<const i32x4_t*>(src + 8);
-  const uint32_t w[8] = {(uint32_t)a[0], (uint32_t)a[1], (uint32_t)a[2], (uint32_t)a[3],
-                         (uint32_t)b[0], (uint32_t)b[1], (uint32_t)b[2], (uint32_t)b[3]};
-  i32x4_t o;
+  const int e = scale_exp(max(max(part[0], part[1]), max(part[2], part[3])));
+  uint8_t* dst = k8 + blk * kKvBlock * D;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float f[4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f[2 * t] = ldexpf(__builtin_bit_cast(float, w[2 * q + t] << 16), -e);
-      f[2 * t + 1] = ldexpf(__builtin_bit_cast(float, w[2 * q + t] & 0xFFFF0000u), -e);
-    }
-    int word = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-    word = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], word, true);
-    o[q] = word;
+  for (int i = 0; i < kChunks; ++i) {
+    int lo, hi;
+    codes8(w[i], e, lo, hi);
+    *reinterpret_cast<int2*>(dst + (i * 256 + tid) * 8) = make_int2(lo, hi);
   }
-  *reinterpret_cast<i32x4_t*>(out + head * per_head + i) = o;
+  if (tid == 0) kexp[blk] = e;
+  prep_v_block<D, true>(V, vop, blk);
 }
 
 struct Params {
@@ -218,11 +219,9 @@ struct Params {
   float S;            // P-cast scale (1 in the bf16 path)
   float inv_S;        // 1/S: the conversion scale when S is a power of two
   float p_clamp;      // largest P kept before conversion when S > 448 (448/S)
-  // FP8 logits: E4M3 codes of Q and K ([B][H][N][d] bytes) and per-head max |x| bits
-  const uint8_t* q8;
+  // FP8 logits: E4M3 codes of K ([B][Hkv][N][d] bytes) and the exponent of each key block
   const uint8_t* k8;
-  const uint32_t* amax_q;
-  const uint32_t* amax_k;
+  const int* kexp;
 };
 
 // How P becomes an MFMA operand.
@@ -624,27 +623,43 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
   const bool wave_active = wrow0 < p.N;
   const int t_last = kCausal ? min((row0 + kBlockRows - 1) / kKvBlock, n_tiles - 1) : n_tiles - 1;
   const int n_it = t_last + 1;
-  // log2(e)/sqrt(d), times the heads' power-of-two scales for FP8 logits (exact)
-  const float c = kQ8 ? ldexpf(p.logit_scale, scale_exp(p.amax_q[b * p.Hq + h]) +
-                                                  scale_exp(p.amax_k[b * p.Hkv + hk]))
-                      : p.logit_scale;
+  // log2(e)/sqrt(d); with FP8 logits times 2^(e_row + e_block) of the row's and the
+  // key block's scales (exact), set per block
+  float c = p.logit_scale;
 
   if (kStats && tid < 4) lds_cnt[tid / 2][tid % 2] = 0;
 
   // Q operand (B of S^T = K Q^T): lane holds Q[myrow][s*16 + g*8 .. +8) for each step s
-  // (bf16), or the codes Q8[myrow][s*64 + g*32 .. +32) (FP8).  The K fragments take the
-  // same d order, so slot k of the two operands holds the same d.
+  // (bf16), or the E4M3 codes of Q[myrow][s*64 + g*32 .. +32) * 2^-e_row (FP8, the row's
+  // scale from the max over both lane halves).  The K fragments take the same d order,
+  // so slot k of the two operands holds the same d.
   KFrag qf[kSSteps];
+  float c_row = p.logit_scale;
   if (wave_active) {
     const int64_t row = ((int64_t)b * p.Hq + h) * p.N + myrow;
     if constexpr (kQ8) {
-      const uint8_t* qrow = p.q8 + row * D + g * 32;
+      const uint16_t* qrow = p.q + row * D + g * 32;
+      i32x4_t w[kSSteps][4];
+      uint32_t m = 0;
 #pragma unroll
-      for (int s = 0; s < kSSteps; ++s) {
-        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(qrow + s * 64);
-        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(qrow + s * 64 + 16);
-        qf[s] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
+      for (int s = 0; s < kSSteps; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          w[s][t] = *reinterpret_cast<const i32x4_t*>(qrow + s * 64 + t * 8);
+          m = max(m, absmax8(w[s][t]));
+        }
+      m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+      const int e = scale_exp(m);
+#pragma unroll
+      for (int s = 0; s < kSSteps; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          int lo, hi;
+          codes8(w[s][t], e, lo, hi);
+          qf[s][2 * t] = lo;
+          qf[s][2 * t + 1] = hi;
+        }
+      c_row = ldexpf(p.logit_scale, e);
     } else {
       const uint16_t* qrow = p.q + row * D + g * 8;
 #pragma unroll
@@ -862,9 +877,17 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
 
   // Step j: block j in buffers cur = j % 2 (its logits, codes, V and bias), blocks
   // j-1 and j+1 in nxt.
+  // FP8 logits: exponent of each key block's scale, read one step ahead
+  const int* kexp_head = kQ8 ? p.kexp + ((int64_t)b * p.Hkv + hk) * n_tiles : nullptr;
+  int ke_next = kQ8 ? kexp_head[tile_of(0)] : 0;
+
   auto step = [&](int it, auto cur_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
     const int t = tile_of(it);
+    if constexpr (kQ8) {
+      c = ldexpf(c_row, ke_next);
+      if (it + 1 < n_it) ke_next = kexp_head[tile_of(it + 1)];
+    }
     // K of block j+2 replaces K of block j (read during step j-1); V of block j
     // replaces V of block j-2 (read during step j-1); bias of block j+1 replaces
     // that of block j-1.  All land before the barrier that ends this step.
@@ -1129,7 +1152,7 @@ void launch_attn3(const Params& p, hipStream_t stream) {
       hipLaunchKernelGGL((pcast_attn_fwd_bf16<D, kCausal, true>), grid, dim3(kThreads), 0, stream, p);
     else
       hipLaunchKernelGGL((pcast_attn_fwd_bf16<D, kCausal, false>), grid, dim3(kThreads), 0, stream, p);
-  } else if (p.q8) {
+  } else if (p.k8) {
     if (p.stats)
       hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, true, true>), grid, dim3(kThreads), 0, stream, p);
     else
@@ -1162,20 +1185,18 @@ void launch_attn(const Params& p, int mode, int causal, hipStream_t stream) {
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
 // Workspace of the FP8-logit path, byte offsets from its start (each 256-aligned):
-// the V operand copy (as in the plain workspace), the E4M3 codes of Q and of K in
-// their own layouts, and the per-head max |Q| and max |K| (fp32 bits).
+// the V operand copy (as in the plain workspace), the E4M3 codes of K in K's own
+// layout, and the exponent of each key block's scale (int32).
 struct Qk8Layout {
-  size_t q, k, amax_q, amax_k, total;
+  size_t k8, kexp, total;
 };
-Qk8Layout qk8_layout(int B, int Hq, int Hkv, int N, int d) {
+Qk8Layout qk8_layout(int B, int Hkv, int N, int d) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t nkv = (size_t)B * Hkv * N * d, nq = (size_t)B * Hq * N * d;
+  const size_t nkv = (size_t)B * Hkv * N * d;
   Qk8Layout l;
-  l.q = up(nkv);
-  l.k = up(l.q + nq);
-  l.amax_q = up(l.k + nkv);
-  l.amax_k = up(l.amax_q + (size_t)B * Hq * 4);
-  l.total = up(l.amax_k + (size_t)B * Hkv * 4);
+  l.k8 = up(nkv);
+  l.kexp = up(l.k8 + nkv);
+  l.total = up(l.kexp + (size_t)B * Hkv * (N / kKvBlock) * 4);
   return l;
 }
 
@@ -1193,9 +1214,9 @@ size_t pcast_workspace_bytes(int B, int Hkv, int N, int d, float S) {
   return (size_t)B * Hkv * N * d * ((S == 0.0f) ? 2 : 1);
 }
 
-size_t pcast_workspace_bytes_qk8(int B, int Hq, int Hkv, int N, int d) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return 0;
-  return qk8_layout(B, Hq, Hkv, N, d).total;
+size_t pcast_workspace_bytes_qk8(int B, int Hkv, int N, int d) {
+  if (B <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return 0;
+  return qk8_layout(B, Hkv, N, d).total;
 }
 
 int pcast_abi_version(void) { return PCAST_ABI_VERSION; }
@@ -1268,34 +1289,25 @@ int enqueue_prep(const void* V, int B, int Hkv, int N, int d, float S, void* ws,
   return e == hipSuccess ? PCAST_OK : hip_fail(e, "V pre-pass launch");
 }
 
-// Per-head max |x|, then the E4M3 codes of x * 2^-e, for x = Q and x = K.
-int enqueue_prep_qk8(const void* Q, const void* K, int B, int Hq, int Hkv, int N, int d, void* ws,
-                     hipStream_t st) {
-  const Qk8Layout l = qk8_layout(B, Hq, Hkv, N, d);
+// K codes and block exponents, and the FP8 V operand copy, in one pass over the key blocks.
+int enqueue_prep_qk8(const void* K, const void* V, int B, int Hkv, int N, int d, void* ws, hipStream_t st) {
+  const Qk8Layout l = qk8_layout(B, Hkv, N, d);
   uint8_t* base = static_cast<uint8_t*>(ws);
-  uint32_t* amax_q = reinterpret_cast<uint32_t*>(base + l.amax_q);
-  uint32_t* amax_k = reinterpret_cast<uint32_t*>(base + l.amax_k);
-  const int n_words = (int)((l.total - l.amax_q) / 4);
-  hipLaunchKernelGGL(pcast_fill_u32, dim3((unsigned)((n_words + 255) / 256)), dim3(256), 0, st, amax_q, n_words);
-  const int64_t per_head = (int64_t)N * d;  // a multiple of 4096: N % 64 == 0, d >= 64
-  const unsigned chunks = (unsigned)((per_head + kAbsChunk - 1) / kAbsChunk);
-  const unsigned qblocks = (unsigned)(per_head / 4096);
-  const uint16_t* Qb = static_cast<const uint16_t*>(Q);
+  const int64_t n_blocks = (int64_t)B * Hkv * (N / kKvBlock);
   const uint16_t* Kb = static_cast<const uint16_t*>(K);
-  hipLaunchKernelGGL(pcast_absmax, dim3(chunks, (unsigned)(B * Hq)), dim3(256), 0, st, Qb, per_head, amax_q);
-  hipLaunchKernelGGL(pcast_absmax, dim3(chunks, (unsigned)(B * Hkv)), dim3(256), 0, st, Kb, per_head, amax_k);
-  hipLaunchKernelGGL(pcast_quant_fp8, dim3(qblocks, (unsigned)(B * Hq)), dim3(256), 0, st, Qb, per_head,
-                     (const uint32_t*)amax_q, base + l.q);
-  hipLaunchKernelGGL(pcast_quant_fp8, dim3(qblocks, (unsigned)(B * Hkv)), dim3(256), 0, st, Kb, per_head,
-                     (const uint32_t*)amax_k, base + l.k);
+  const uint16_t* Vb = static_cast<const uint16_t*>(V);
+  int* kexp = reinterpret_cast<int*>(base + l.kexp);
+  if (d == 64)
+    hipLaunchKernelGGL(pcast_prep_kv8<64>, dim3((unsigned)n_blocks), dim3(256), 0, st, Kb, Vb, base, base + l.k8, kexp);
+  else
+    hipLaunchKernelGGL(pcast_prep_kv8<128>, dim3((unsigned)n_blocks), dim3(256), 0, st, Kb, Vb, base, base + l.k8, kexp);
   const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? PCAST_OK : hip_fail(e, "Q/K pre-pass launch");
+  return e == hipSuccess ? PCAST_OK : hip_fail(e, "K/V pre-pass launch");
 }
 
-// Extra limits of the FP8-logit path: an FP8 P cast, and heads on the second grid axis.
-int check_qk8(int B, int Hq, float S) {
+// The FP8-logit path needs the FP8 P.V path.
+int check_qk8(float S) {
   if (S == 0.0f) return fail(PCAST_ENOTSUP, "FP8 logits need S > 0 (the FP8 P.V path)");
-  if ((int64_t)B * Hq > 65535) return fail(PCAST_ENOTSUP, "B * Hq = %lld: at most 65535 heads", (long long)B * Hq);
   return PCAST_OK;
 }
 
@@ -1305,12 +1317,10 @@ int enqueue_attn(const void* Q, const void* K, const void* ws, const float* bias
   const bool fp8 = S != 0.0f;
   Params p{};
   if (qk8) {
-    const Qk8Layout l = qk8_layout(B, Hq, Hkv, N, d);
+    const Qk8Layout l = qk8_layout(B, Hkv, N, d);
     const uint8_t* base = static_cast<const uint8_t*>(ws);
-    p.q8 = base + l.q;
-    p.k8 = base + l.k;
-    p.amax_q = reinterpret_cast<const uint32_t*>(base + l.amax_q);
-    p.amax_k = reinterpret_cast<const uint32_t*>(base + l.amax_k);
+    p.k8 = base + l.k8;
+    p.kexp = reinterpret_cast<const int*>(base + l.kexp);
   }
   p.q = static_cast<const uint16_t*>(Q);
   p.k = static_cast<const uint16_t*>(K);
@@ -1387,33 +1397,30 @@ int attn_fwd_pcast(const void* Q, const void* K, const void* V, const float* bia
   return PCAST_OK;
 }
 
-int pcast_prepare_qk8(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv, int N, int d,
-                      void* workspace, void* stream) {
+int pcast_prepare_qk8(const void* K, const void* V, int B, int Hkv, int N, int d, void* workspace,
+                      void* stream) {
   g_last_error[0] = '\0';
-  if (!Q || !K || !V || !workspace) return fail(PCAST_EINVAL, "Q, K, V and workspace must be non-null");
-  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(workspace, 16))
-    return fail(PCAST_EINVAL, "Q, K, V and workspace must be 16-byte aligned");
-  int rc = check_shape(B, Hq, Hkv, N, d, 1.0f);
+  if (!K || !V || !workspace) return fail(PCAST_EINVAL, "K, V and workspace must be non-null");
+  if (!aligned(K, 16) || !aligned(V, 16) || !aligned(workspace, 16))
+    return fail(PCAST_EINVAL, "K, V and workspace must be 16-byte aligned");
+  int rc = check_shape(B, Hkv, Hkv, N, d, 1.0f);
   if (rc != PCAST_OK) return rc;
-  if ((rc = check_qk8(B, Hq, 1.0f)) != PCAST_OK) return rc;
   if ((rc = check_device()) != PCAST_OK) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = enqueue_prep(V, B, Hkv, N, d, 1.0f, workspace, st);
-  return rc != PCAST_OK ? rc : enqueue_prep_qk8(Q, K, B, Hq, Hkv, N, d, workspace, st);
+  return enqueue_prep_qk8(K, V, B, Hkv, N, d, workspace, static_cast<hipStream_t>(stream));
 }
 
-int attn_fwd_pcast_qk8_prepared(const void* workspace, const float* bias, int B, int Hq, int Hkv, int N,
-                                int d, int causal, float S, int order, float* out,
+int attn_fwd_pcast_qk8_prepared(const void* Q, const void* workspace, const float* bias, int B, int Hq,
+                                int Hkv, int N, int d, int causal, float S, int order, float* out,
                                 unsigned long long* stats, void* stream) {
   g_last_error[0] = '\0';
   if (!workspace) return fail(PCAST_EINVAL, "workspace must be non-null");
   if (!aligned(workspace, 16)) return fail(PCAST_EINVAL, "workspace must be 16-byte aligned");
-  int rc = check_attn_args(workspace, workspace, bias, causal, order, out, stats);
+  int rc = check_attn_args(Q, workspace, bias, causal, order, out, stats);
   if (rc != PCAST_OK) return rc;
   if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
-  if ((rc = check_qk8(B, Hq, S)) != PCAST_OK) return rc;
+  if ((rc = check_qk8(S)) != PCAST_OK) return rc;
   if ((rc = check_device()) != PCAST_OK) return rc;
-  return enqueue_attn(nullptr, nullptr, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
+  return enqueue_attn(Q, nullptr, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
                       static_cast<hipStream_t>(stream), true);
 }
 
@@ -1426,17 +1433,16 @@ int attn_fwd_pcast_qk8(const void* Q, const void* K, const void* V, const float*
   if (!V) return fail(PCAST_EINVAL, "V must be non-null");
   if (!aligned(V, 16)) return fail(PCAST_EINVAL, "V must be 16-byte aligned");
   if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
-  if ((rc = check_qk8(B, Hq, S)) != PCAST_OK) return rc;
+  if ((rc = check_qk8(S)) != PCAST_OK) return rc;
   if ((rc = check_device()) != PCAST_OK) return rc;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, pcast_workspace_bytes_qk8(B, Hq, Hkv, N, d), st);
+  hipError_t e = hipMallocAsync(&ws, pcast_workspace_bytes_qk8(B, Hkv, N, d), st);
   if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
-  rc = enqueue_prep(V, B, Hkv, N, d, 1.0f, ws, st);
-  if (rc == PCAST_OK) rc = enqueue_prep_qk8(Q, K, B, Hq, Hkv, N, d, ws, st);
+  rc = enqueue_prep_qk8(K, V, B, Hkv, N, d, ws, st);
   if (rc == PCAST_OK)
-    rc = enqueue_attn(nullptr, nullptr, ws, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats, st, true);
+    rc = enqueue_attn(Q, nullptr, ws, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats, st, true);
   e = hipFreeAsync(ws, st);
   if (rc != PCAST_OK) return rc;
   if (e != hipSuccess) return hip_fail(e, "hipFreeAsync(workspace)");

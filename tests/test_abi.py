@@ -95,13 +95,12 @@ def test_prepare_argument_errors(lib, kw, code):
 
 
 def test_qk8_workspace_layout(lib):
-    # V codes, Q codes, K codes, per-head maxima of Q and of K, each 256-byte aligned
+    # V codes, K codes, one int32 exponent per key block, each 256-byte aligned
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    for B, Hq, Hkv, N, d in ((4, 32, 32, 8192, 128), (1, 3, 1, 64, 64), (2, 6, 3, 192, 128)):
-        nkv, nq = B * Hkv * N * d, B * Hq * N * d
-        want = up(up(up(up(nkv) + nq) + nkv) + 4 * B * Hq) + 4 * B * Hkv
-        assert sna.workspace_bytes_qk8(B, Hq, Hkv, N, d) == up(want)
-    assert sna.workspace_bytes_qk8(0, 1, 1, 64, 64) == 0
+    for B, Hkv, N, d in ((4, 32, 8192, 128), (1, 1, 64, 64), (2, 3, 192, 128)):
+        nkv = B * Hkv * N * d
+        assert sna.workspace_bytes_qk8(B, Hkv, N, d) == up(up(up(nkv) + nkv) + 4 * B * Hkv * (N // 64))
+    assert sna.workspace_bytes_qk8(0, 1, 64, 64) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -111,31 +110,33 @@ def test_qk8_workspace_layout(lib):
     (dict(out=0), sna.PCAST_EINVAL),
     (dict(causal=3), sna.PCAST_EINVAL),
     (dict(S=float("nan")), sna.PCAST_EINVAL),
+    (dict(Hq=3, Hkv=2), sna.PCAST_EINVAL),
     (dict(S=0.0), sna.PCAST_ENOTSUP),
-    (dict(B=2, Hq=32768, Hkv=1), sna.PCAST_ENOTSUP),
     (dict(d=96), sna.PCAST_ENOTSUP),
+    (dict(N=100), sna.PCAST_ENOTSUP),
 ])
 def test_qk8_argument_errors(lib, kw, code):
     a = dict(Q=FAKE, K=FAKE, V=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128, causal=1, S=256.0,
              order=1, out=FAKE, stats=0, stream=0)
     a.update(kw)
     assert sna.attn_fwd_pcast_qk8(**a) == code
-    p = dict(workspace=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128, causal=1, S=256.0, order=1,
+    p = dict(Q=FAKE, workspace=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128, causal=1, S=256.0, order=1,
              out=FAKE, stats=0, stream=0)
-    p.update({k: v for k, v in kw.items() if k in p})
     if set(kw) <= set(p):
+        p.update(kw)
         assert sna.attn_fwd_pcast_qk8_prepared(**p) == code
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(Q=0), sna.PCAST_EINVAL),
-    (dict(K=FAKE + 8), sna.PCAST_EINVAL),
+    (dict(K=0), sna.PCAST_EINVAL),
+    (dict(V=FAKE + 8), sna.PCAST_EINVAL),
     (dict(workspace=0), sna.PCAST_EINVAL),
-    (dict(Hq=3, Hkv=2), sna.PCAST_EINVAL),
+    (dict(B=0), sna.PCAST_EINVAL),
     (dict(N=65), sna.PCAST_ENOTSUP),
+    (dict(d=32), sna.PCAST_ENOTSUP),
 ])
 def test_prepare_qk8_argument_errors(lib, kw, code):
-    a = dict(Q=FAKE, K=FAKE, V=FAKE, B=1, Hq=2, Hkv=1, N=128, d=128, workspace=FAKE, stream=0)
+    a = dict(K=FAKE, V=FAKE, B=1, Hkv=1, N=128, d=128, workspace=FAKE, stream=0)
     a.update(kw)
     assert sna.prepare_qk8(**a) == code
 

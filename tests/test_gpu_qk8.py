@@ -1,10 +1,12 @@
 """GPU parity of the FP8-logit path (attn_fwd_pcast_qk8) against the oracle.
 
-The pre-passes are compared bit for bit with the oracle's quantisation
-(oracle.qk8): the per-head max |x| and the E4M3 code of every element of Q
-and K.  The attention output is compared with the oracle run on the
-dequantised Q and K, within the tolerance tests/_parity.compare_qk8 derives
-from the FP8 matrix cores' accumulation error.
+The K pre-pass is compared bit for bit with the oracle's quantisation
+(oracle.qk8): the exponent of every 64-key block and the E4M3 code of every
+element.  Q is rounded inside the attention kernel, row by row: feeding the
+kernel the oracle's rounded Q (and K) instead of the originals must give the
+same output bit for bit.  The attention output is compared with the oracle run
+on the dequantised Q and K, within the tolerance tests/_parity.compare_qk8
+derives from the FP8 matrix cores' accumulation error.
 """
 import numpy as np
 import pytest
@@ -30,37 +32,33 @@ def _up(x):
     return (x + 255) // 256 * 256
 
 
-def _prepare(sna, qb, kb, vb):
-    B, Hq, N, d = qb.shape
-    Hkv = kb.shape[1]
-    q, k, v = (_parity.to_gpu_bf16(x) for x in (qb, kb, vb))
-    ws = torch.zeros(sna.workspace_bytes_qk8(B, Hq, Hkv, N, d), dtype=torch.uint8, device="cuda")
-    rc = sna.prepare_qk8(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, N, d, ws.data_ptr(),
+def _prepare(sna, kb, vb):
+    B, Hkv, N, d = kb.shape
+    k, v = (_parity.to_gpu_bf16(x) for x in (kb, vb))
+    ws = torch.zeros(sna.workspace_bytes_qk8(B, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    rc = sna.prepare_qk8(k.data_ptr(), v.data_ptr(), B, Hkv, N, d, ws.data_ptr(),
                          torch.cuda.current_stream().cuda_stream)
     assert rc == sna.PCAST_OK, sna.strerror(rc)
     torch.cuda.synchronize()
     w = ws.cpu().numpy()
-    nkv, nq = B * Hkv * N * d, B * Hq * N * d
-    off_q = _up(nkv)
-    off_k = _up(off_q + nq)
-    off_aq = _up(off_k + nkv)
-    off_ak = _up(off_aq + 4 * B * Hq)
-    parts = {"q8": w[off_q:off_q + nq].reshape(qb.shape), "k8": w[off_k:off_k + nkv].reshape(kb.shape),
-             "amax_q": w[off_aq:off_aq + 4 * B * Hq].view(np.uint32).reshape(B, Hq),
-             "amax_k": w[off_ak:off_ak + 4 * B * Hkv].view(np.uint32).reshape(B, Hkv)}
-    return parts
+    nkv = B * Hkv * N * d
+    off_k = _up(nkv)
+    off_e = _up(off_k + nkv)
+    return {"k8": w[off_k:off_k + nkv].reshape(kb.shape),
+            "kexp": w[off_e:off_e + 4 * B * Hkv * (N // 64)].view(np.int32).reshape(B, Hkv, N // 64)}
 
 
-def _check_prepass(parts, name, bits):
+def _check_k_prepass(parts, bits):
     x = ((bits.astype(np.uint32) & 0xFFFF) << 16).view(np.float32).astype(np.float64)
-    amax = np.max(np.abs(x), axis=(2, 3)).astype(np.float32).view(np.uint32)
-    assert np.array_equal(parts["amax_" + name], amax), f"max |{name}| per head"
-    _, exps = qk8.quantize_heads(bits)
-    want = e4m3.e4m3_encode(np.ldexp(x, -exps[:, :, None, None]))
-    got = parts[name + "8"]
+    _, exps = qk8.quantize_k(bits)
+    assert np.array_equal(parts["kexp"], exps), "key block exponents"
+    B, H, N, d = bits.shape
+    e = np.repeat(exps, 64, axis=2)[..., None]
+    want = e4m3.e4m3_encode(np.ldexp(x, -e))
+    got = parts["k8"]
     assert not np.any((got & 0x7F) == 0x7F), "NaN code"
     # equal values (+0 and -0 are both zero to the matrix cores)
-    assert np.array_equal(e4m3.DECODE_TABLE[got], e4m3.DECODE_TABLE[want]), f"{name} codes"
+    assert np.array_equal(e4m3.DECODE_TABLE[got], e4m3.DECODE_TABLE[want]), "K codes"
 
 
 def _scaled_heads(B, H, N, d, seed, tensor_id):
@@ -80,25 +78,39 @@ def _scaled_heads(B, H, N, d, seed, tensor_id):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)   # back to bf16, RNE
 
 
-def test_prepass_bit_exact(sna):
-    print("\n[case] qk8 pre-pass: B=2 Hq=4 Hkv=2 N=192 d=128", flush=True)
-    qb = _scaled_heads(2, 4, 192, 128, 41, 0)
-    kb = _scaled_heads(2, 2, 192, 128, 41, 1)
+def test_k_prepass_bit_exact(sna):
+    print("\n[case] qk8 K pre-pass: B=2 Hkv=4 N=192 d=128", flush=True)
+    kb = _scaled_heads(2, 4, 192, 128, 41, 1)
     vb = synthetic.gaussian_bf16(41, 2, kb.shape)
-    parts = _prepare(sna, qb, kb, vb)
-    _check_prepass(parts, "q", qb)
-    _check_prepass(parts, "k", kb)
+    _check_k_prepass(_prepare(sna, kb, vb), kb)
 
 
-def test_prepass_bit_exact_many_chunks(sna):
-    # N * d = 40 * 4096 elements per head: ten absmax workgroups per head, ragged
-    print("\n[case] qk8 pre-pass: B=1 Hq=8 Hkv=8 N=2560 d=64", flush=True)
-    qb = _scaled_heads(1, 8, 2560, 64, 42, 0)
-    kb = _scaled_heads(1, 8, 2560, 64, 42, 1)
+def test_k_prepass_bit_exact_d64(sna):
+    print("\n[case] qk8 K pre-pass: B=1 Hkv=8 N=640 d=64", flush=True)
+    kb = _scaled_heads(1, 8, 640, 64, 42, 1)
+    # blocks inside one head at very different scales too
+    x = ((kb.astype(np.uint32)) << 16).view(np.float32).copy()
+    x[0, 0, 64:128] *= np.float32(2.0 ** 30)
+    x[0, 0, 128:192] = 0.0
+    x[0, 0, 200, 3] = np.float32(448.0 * 2.0 ** 3)
+    kb = (x.view(np.uint32) >> 16).astype(np.uint16)
     vb = synthetic.gaussian_bf16(42, 2, kb.shape)
-    parts = _prepare(sna, qb, kb, vb)
-    _check_prepass(parts, "q", qb)
-    _check_prepass(parts, "k", kb)
+    _check_k_prepass(_prepare(sna, kb, vb), kb)
+
+
+def test_v_copy_matches_plain_prepass(sna):
+    """The fused pre-pass writes the same V operand copy as pcast_prepare_v."""
+    print("\n[case] qk8 V copy: B=2 Hkv=2 N=256 d=128", flush=True)
+    kb = synthetic.gaussian_bf16(48, 1, (2, 2, 256, 128))
+    vb = synthetic.gaussian_bf16(48, 2, (2, 2, 256, 128))
+    k, v = (_parity.to_gpu_bf16(x) for x in (kb, vb))
+    ws8 = torch.zeros(sna.workspace_bytes_qk8(2, 2, 256, 128), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(sna.workspace_bytes(2, 2, 256, 128, 256.0), dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert sna.prepare_qk8(k.data_ptr(), v.data_ptr(), 2, 2, 256, 128, ws8.data_ptr(), st) == 0
+    assert sna.prepare_v(v.data_ptr(), 2, 2, 256, 128, 256.0, ws.data_ptr(), st) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(ws8[:ws.numel()].cpu(), ws.cpu())
 
 
 def _run_qk8(sna, qb, kb, vb, bias, causal, S, order, stats=True):
@@ -114,8 +126,8 @@ def _case(sna, name, B, Hq, Hkv, N, d, causal, bias, S, order, seed, blocks=None
           f"order={order} seed={seed}", flush=True)
     qb, kb, vb = synthetic.qkv_bf16(B, Hq, Hkv, N, d, seed) if qkv is None else qkv
     out, st = _run_qk8(sna, qb, kb, vb, bias, causal, S, order)
-    qd, _ = qk8.quantize_heads(qb)
-    kd, _ = qk8.quantize_heads(kb)
+    qd, _ = qk8.quantize_q(qb)
+    kd, _ = qk8.quantize_k(kb)
     if isinstance(blocks, int):
         blocks = _parity.sample_blocks(B, Hq, N, blocks, seed)
     rep = _parity.compare_qk8(out, st, qd, kd, vb, bias, causal, S, order, blocks)
@@ -138,8 +150,8 @@ def test_random_bias(sna, order):
 
 
 def test_scaled_heads(sna):
-    # heads at scales from 2^-20 to 2^40 and a zero head: the per-head exponents
-    # must cancel exactly in the logits
+    # heads at scales from 2^-20 to 2^40 and a zero head: the row and block
+    # exponents must cancel exactly in the logits
     B, Hq, Hkv, N, d = 1, 8, 8, 256, 128
     qb = _scaled_heads(B, Hq, N, d, 45, 0)
     kb = np.ascontiguousarray(_scaled_heads(B, Hkv, N, d, 45, 1)[:, ::-1])
@@ -153,6 +165,24 @@ def test_scaled_heads(sna):
         qf[0, h] *= np.float32(2.0 ** np.round(np.log2(30.0 / aq / ak)))
     qb = (qf.view(np.uint32) >> 16).astype(np.uint16)
     _case(sna, "scaled heads", B, Hq, Hkv, N, d, True, None, 256.0, 1, 45, qkv=(qb, kb, vb))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rounded_inputs_give_the_same_output(sna, d):
+    """Q and K replaced by the oracle's rounded values: the kernel's own rounding
+    of Q (per row) and the pre-pass's of K (per block) are then identities up to
+    a power of two, so the output is the same bit for bit."""
+    print(f"\n[case] qk8 rounded inputs, d={d}", flush=True)
+    qb, kb, vb = synthetic.qkv_bf16(2, 4, 2, 320, d, 49)
+    x = ((qb.astype(np.uint32)) << 16).view(np.float32).copy()
+    x[:, :, ::5] *= np.float32(2.0 ** -9)            # rows at different scales
+    qb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    qd, _ = qk8.quantize_q(qb)
+    kd, _ = qk8.quantize_k(kb)
+    bias = synthetic.sink_bias(320, 7.0)
+    a, sa = _run_qk8(sna, qb, kb, vb, bias, True, 256.0, 1)
+    b, sb = _run_qk8(sna, qd, kd, vb, bias, True, 256.0, 1)
+    assert np.array_equal(a, b) and np.array_equal(sa, sb)
 
 
 def test_single_block_orders_identical(sna):
