@@ -33,6 +33,7 @@ PEAK_FP8 = 5000.0    # TFLOP/s, MI355X dense FP8 MFMA
 PEAK_BF16 = 2500.0   # TFLOP/s, MI355X dense bf16 MFMA
 KERNEL_SRC = os.path.join(ROOT, "softmax_numerics_amd", "csrc", "attn_fwd_pcast.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_throughput.json")
+TRAFFIC_FILE_QK8 = os.path.join(ROOT, "profiles", "traffic_attn_fwd_qk8_throughput.json")
 
 
 def kernel_source_hash() -> str:
@@ -40,11 +41,11 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, path: str = TRAFFIC_FILE):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -255,7 +256,8 @@ def main() -> int:
         result["qk_fp8"] = {"ms_per_step": round(wall8 * 1e3 / args.steps, 5),
                             "value": round(flops / wall8 * args.steps / 1e12, 2),
                             "attention_kernel_ms": round(attn8, 5), "prepass_ms": round(prep8, 5),
-                            "achieved": round(ach8, 2), "frac": round(ach8 / PEAK_FP8, 4)}
+                            "achieved": round(ach8, 2), "peak": PEAK_FP8, "frac": round(ach8 / PEAK_FP8, 4),
+                            "traffic": measured_traffic(w.name, TRAFFIC_FILE_QK8)}
         out_qk8 = out.cpu().numpy()
 
     if not args.no_cpu_baseline:
