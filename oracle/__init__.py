@@ -13,8 +13,9 @@ Contents
                 (O2), sequential and telescoped forms
 * ``core``      the same O1/O2 in C (pcast_oracle.c, OpenMP), for large inputs,
                 with per-row parity slack and underflow counters
-* ``qk8``       the FP8-logits extension: per-head power-of-two scales and
-                E4M3 rounding of Q and K
+* ``qk8``       the FP8-logits extension: power-of-two block scales (per query
+                row, per 64-key block) and E4M3 rounding of Q and K
+* ``rowdiag``   per-row log-sum-exp and lost non-sink mass of the pipeline
 * ``theory``    the closed forms F(Delta, S), delta_k, Delta_c and a Monte Carlo
                 of the collapse model
 
@@ -22,4 +23,4 @@ Parity pins: every function here is checked by ``tests/test_oracle_*.py``
 against facts fixed by the pages or by mathematics (see the test docstrings).
 """
 
-from . import e4m3, qk8, reference, theory  # noqa: F401
+from . import e4m3, qk8, reference, rowdiag, theory  # noqa: F401
