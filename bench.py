@@ -236,6 +236,7 @@ def main() -> int:
     }
 
     out_rev = out.cpu().numpy() if not args.no_cpu_baseline else None
+    st_rev = None if stats is None else stats.cpu().numpy().reshape(-1, 2)
     out_qk8 = None
     if ws8 is not None:
         # the FP8-logit variant on the same input, same configuration
@@ -261,9 +262,32 @@ def main() -> int:
         out_qk8 = out.cpu().numpy()
 
     if not args.no_cpu_baseline:
-        step(S_=1.0, order_=0)                      # S = 1 forward, for the error contrast
+        # S = 1 forward, for the error contrast, with the per-row diagnostics (same out, bit for bit)
+        lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+        lost = torch.empty_like(lse)
+        st1 = torch.empty(sna.stats_words(w.B, w.Hq, w.N), dtype=torch.int64, device=dev)
+        rc = sna.prepare_v(v.data_ptr(), w.B, w.Hkv, w.N, w.d, 1.0, ws.data_ptr(), sh)
+        rc = rc or sna.attn_fwd_pcast_rows(q.data_ptr(), k.data_ptr(), ws.data_ptr(), bias_t.data_ptr(), w.B, w.Hq,
+                                           w.Hkv, w.N, w.d, int(w.causal), 1.0, 0, out.data_ptr(), st1.data_ptr(),
+                                           lse.data_ptr(), lost.data_ptr(), sh)
+        if rc != sna.PCAST_OK:
+            raise sna.PcastError(rc, sna.strerror(rc))
         torch.cuda.synchronize()
         out_fwd1 = out.cpu().numpy()
+        s1 = st1.cpu().numpy().reshape(-1, 2)
+        far = lost.cpu().numpy().reshape(w.B * w.Hq, w.N)[:, min(1024, w.N // 2):]
+        result["collapse"] = {
+            "delta": delta, "sink_keys": 4,
+            "S1_forward": {"delta_critical": round(sna.delta_critical(1.0), 4),
+                           "underflow_measured": float(s1[:, 1].sum() / s1[:, 0].sum()),
+                           "underflow_model": round(sna.underflow_model(delta, 1.0), 4),
+                           "lost_mass_measured": round(float(far.mean()), 4),
+                           "lost_mass_model": round(sna.lost_mass_model(delta, 1.0), 4),
+                           "lost_mass_rows": f"mean over all heads of rows {min(1024, w.N // 2)}..{w.N - 1}"},
+            f"S{S:g}_{'reverse' if order else 'forward'}": {
+                "delta_critical": round(sna.delta_critical(S), 4),
+                "underflow_measured": None if st_rev is None else float(st_rev[:, 1].sum() / st_rev[:, 0].sum()),
+                "underflow_model_forward": sna.underflow_model(delta, S)}}
         base, mse = cpu_baseline(w, qb, kb, vb, bias, out_rev, out_fwd1, args.cpu_seconds, out_qk8=out_qk8)
         result["cpu_baseline"] = base
         result["mse_vs_fp64_sampled"] = mse

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define PCAST_ABI_VERSION 2
+#define PCAST_ABI_VERSION 3
 
 /* Keys per KV block.  The block size is part of the numerics (the running
  * max is updated once per block), so it is fixed. */
@@ -114,6 +114,49 @@ int pcast_prepare_v(const void* V, int B, int Hkv, int N, int d, float S, void* 
 int attn_fwd_pcast_prepared(const void* Q, const void* K, const void* workspace, const float* bias,
                             int B, int Hq, int Hkv, int N, int d, int causal, float S, int order,
                             float* out, unsigned long long* stats, void* stream);
+
+/*
+ * attn_fwd_pcast_rows -- attn_fwd_pcast_prepared (same arguments, same out and
+ * stats, bit for bit) that also writes two per-row diagnostics of the P-cast
+ * (P-cast summary on gist.science, sections 1 and 2: probability mass of the
+ * non-sink keys silently zeroed by the cast, and the running statistics m, l
+ * of the online softmax, FlashAttention blog section "La ricorrenza softmax
+ * online"):
+ *   lse   device, float32 [B][Hq][N], or NULL: ln sum_j exp(s_ij) over the
+ *         row's visible keys, s_ij = q.k / sqrt(d) + bias_j (natural units).
+ *   lost  device, float32 [B][Hq][N], or NULL: the fraction of the row's
+ *         non-sink probability mass whose E4M3 code is 0,
+ *         sum_{j non-sink, code 0} p_j / sum_{j non-sink} p_j with p_j the
+ *         un-cast probability (0 for a row with no non-sink key).
+ * Requires S > 0 (PCAST_ENOTSUP for S = 0).  Every key block takes the
+ * kernel's sequential step, so the call is slower than the plain one.
+ * Allocates nothing.
+ */
+int attn_fwd_pcast_rows(const void* Q, const void* K, const void* workspace, const float* bias, int B,
+                        int Hq, int Hkv, int N, int d, int causal, float S, int order, float* out,
+                        unsigned long long* stats, float* lse, float* lost, void* stream);
+
+/*
+ * Closed forms of the collapse model (P-cast summary on gist.science, section
+ * "Metodologia e Analisi" and "Contributi Chiave" point 1), for predicting
+ * from Delta, S and k whether a configuration zeroes the non-sink
+ * probabilities.  Model: non-sink logits i.i.d. N(0,1), k sink keys at
+ * z + Delta, forward order, so every later non-sink probability is taken
+ * relative to Delta + M_k, M_k the max of k standard normals; its code is 0
+ * when S * p <= 2^-10.  Host functions; NaN for S <= 0, non-finite arguments
+ * or k outside 1..1024.
+ *   pcast_sink_max_mean(k)             E[M_k] (1.0294 for k = 4)
+ *   pcast_delta_critical(S, k)         Delta_c = 10 ln 2 + ln S - E[M_k], where the
+ *                                      summary's plug-in underflow fraction is 1/2
+ *   pcast_underflow_model(Delta, S, k) E[Phi(Delta + M_k - 10 ln 2 - ln S)], the
+ *                                      expected fraction of non-sink codes at 0
+ *   pcast_lost_mass_model(Delta, S, k) E[Phi(Delta + M_k - 10 ln 2 - ln S - 1)],
+ *                                      the expected lost non-sink mass fraction
+ */
+double pcast_sink_max_mean(int k);
+double pcast_delta_critical(double S, int k);
+double pcast_underflow_model(double delta, double S, int k);
+double pcast_lost_mass_model(double delta, double S, int k);
 
 /*
  * The forward with FP8 logits: Q and K rounded to E4M3 as well, so that Q K^T

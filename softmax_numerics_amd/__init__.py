@@ -21,7 +21,9 @@ ORDERS = {"forward": 0, "reverse": 1, 0: 0, 1: 1}
 # Every symbol include/pcast_attn.h declares.
 EXPORTS = ("attn_fwd_pcast", "pcast_prepare_v", "attn_fwd_pcast_prepared", "pcast_stats_words",
            "pcast_workspace_bytes", "pcast_strerror", "pcast_abi_version", "pcast_workspace_bytes_qk8",
-           "pcast_prepare_qk8", "attn_fwd_pcast_qk8_prepared", "attn_fwd_pcast_qk8")
+           "pcast_prepare_qk8", "attn_fwd_pcast_qk8_prepared", "attn_fwd_pcast_qk8",
+           "attn_fwd_pcast_rows", "pcast_sink_max_mean", "pcast_delta_critical",
+           "pcast_underflow_model", "pcast_lost_mass_model")
 
 _lock = threading.Lock()
 _lib = None
@@ -67,6 +69,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_fwd_pcast_qk8_prepared.restype = I
             lib.attn_fwd_pcast_qk8.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P]
             lib.attn_fwd_pcast_qk8.restype = I
+            lib.attn_fwd_pcast_rows.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P, P, P]
+            lib.attn_fwd_pcast_rows.restype = I
+            D = ctypes.c_double
+            lib.pcast_sink_max_mean.argtypes = [I]
+            lib.pcast_sink_max_mean.restype = D
+            lib.pcast_delta_critical.argtypes = [D, I]
+            lib.pcast_delta_critical.restype = D
+            lib.pcast_underflow_model.argtypes = [D, D, I]
+            lib.pcast_underflow_model.restype = D
+            lib.pcast_lost_mass_model.argtypes = [D, D, I]
+            lib.pcast_lost_mass_model.restype = D
             _lib = lib
     return _lib
 
@@ -111,6 +124,31 @@ def attn_fwd_pcast_qk8_prepared(Q, workspace, bias, B, Hq, Hkv, N, d, causal, S,
     return int(load_library().attn_fwd_pcast_qk8_prepared(
         Q, workspace, bias or None, B, Hq, Hkv, N, d, int(causal), float(S), int(order), out,
         stats or None, stream or None))
+
+
+def attn_fwd_pcast_rows(Q, K, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats, lse, lost,
+                        stream) -> int:
+    """Raw attn_fwd_pcast_rows with integer device addresses (0 for NULL); returns the C return code."""
+    return int(load_library().attn_fwd_pcast_rows(
+        Q, K, workspace, bias or None, B, Hq, Hkv, N, d, int(causal), float(S), int(order), out,
+        stats or None, lse or None, lost or None, stream or None))
+
+
+def sink_max_mean(k: int = 4) -> float:
+    return float(load_library().pcast_sink_max_mean(int(k)))
+
+
+def delta_critical(S: float, k: int = 4) -> float:
+    """Sink strength above which forward order zeroes most non-sink codes at scale S."""
+    return float(load_library().pcast_delta_critical(float(S), int(k)))
+
+
+def underflow_model(delta: float, S: float, k: int = 4) -> float:
+    return float(load_library().pcast_underflow_model(float(delta), float(S), int(k)))
+
+
+def lost_mass_model(delta: float, S: float, k: int = 4) -> float:
+    return float(load_library().pcast_lost_mass_model(float(delta), float(S), int(k)))
 
 
 def workspace_bytes_qk8(B: int, Hkv: int, N: int, d: int) -> int:

@@ -4,10 +4,12 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "attn_fwd_pcast.hip")
+SRC_HOST = os.path.join(PKG, "csrc", "collapse_model.cpp")
 LIB = os.path.join(PKG, "libpcast_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -25,8 +27,15 @@ FLAGS = [
 def build(verbose: bool = False) -> str:
     """Compile the library (always recompiles) and return its path."""
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    with tempfile.TemporaryDirectory() as td:
+        # the host-only part is plain C++ (no device pass)
+        obj = os.path.join(td, "collapse_model.o")
+        host = subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-c", SRC_HOST, "-o", obj],
+                              capture_output=True, text=True)
+        if host.returncode != 0:
+            raise RuntimeError(f"g++ failed ({host.returncode}):\n{host.stderr}")
+        cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-x", "none", obj, "-o", tmp]
+        res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l and l.strip())
     if res.returncode != 0:

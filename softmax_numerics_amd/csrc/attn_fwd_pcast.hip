@@ -56,6 +56,7 @@ constexpr int kRowsPerWave = 32;
 constexpr int kBlockRows = kWaves * kRowsPerWave;  // 128 query rows per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // Key (within a 64-key block) held by lane group g (= lane / 32) in operand
 // slot b (0..31).  It is the order of the S^T accumulator: register r of
@@ -222,6 +223,9 @@ struct Params {
   // FP8 logits: E4M3 codes of K ([B][Hkv][N][d] bytes) and the exponent of each key block
   const uint8_t* k8;
   const int* kexp;
+  // per-row diagnostics [B][Hq][N], or null
+  float* lse;
+  float* lost;
 };
 
 // How P becomes an MFMA operand.
@@ -577,9 +581,12 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params 
 // block j-1's alpha comes first).  The three streams are independent, so the
 // MFMAs interleave with the exponentials inside one basic block.
 // ---------------------------------------------------------------------------
-template <int D, int kMode, bool kCausal, bool kStats, bool kQ8>
+// kStats: 0 = no counting; 1 = underflow counters; 2 = counters (if p.stats) and the
+// per-row log-sum-exp and lost non-sink mass (every block then takes the sequential step).
+template <int D, int kMode, bool kCausal, int kStats, bool kQ8>
 __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p) {
   static_assert(kMode != kBf16, "FP8 modes only");
+  constexpr bool kDiag = kStats == 2;
   using G = Geometry<D>;
   // kQ8: Q and K as E4M3 codes, logits on the FP8 MFMA (K = 64 per step), else bf16
   constexpr int kKRow = kQ8 ? D : D * 2;      // bytes per K row
@@ -763,6 +770,8 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
   float alpha_pend = 1.0f;  // rescale owed before the pending P.V
   bool pend = false;        // block j-1's P.V is still to be accumulated
   unsigned int cnt_tot = 0, cnt_zero = 0, cnt_nz_fast = 0, n_fast = 0;
+  // row diagnostics, rescaled like l: un-cast P of non-sink keys, and of those whose code is 0
+  float l_ns = 0.0f, l_lost = 0.0f;
 
   // max of a block's raw logits (four max3 chains, then a tree; both lane halves)
   auto block_max = [&](f32x16_t(&sa)[2]) __attribute__((always_inline)) -> float {
@@ -790,12 +799,21 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
       sa[j / 16][j % 16] = pj;
       ps[j % 4] += pj;
     }
-    l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    const float bsum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    l_run = l_run * alpha + bsum;
     m_run = m_new;
 #pragma unroll
     for (int w = 0; w < 8; ++w)
       pb[w] = (int)cast4<kMode>(p, sa[w / 4][4 * (w % 4)], sa[w / 4][4 * (w % 4) + 1], sa[w / 4][4 * (w % 4) + 2],
                                 sa[w / 4][4 * (w % 4) + 3]);
+    if constexpr (kDiag) {  // every key visible and non-sink; summed in the order of bsum
+      float lo[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        lo[j % 4] += (((uint32_t)pb[j / 4] >> (8 * (j % 4))) & 0xFFu) == 0 ? sa[j / 16][j % 16] : 0.0f;
+      l_ns = l_ns * alpha + bsum;
+      l_lost = l_lost * alpha + ((lo[0] + lo[1]) + (lo[2] + lo[3]));
+    }
     return alpha;
   };
   // bias of this lane's 32 keys from the staged block: slots 4q..4q+3 are 4 consecutive keys
@@ -834,6 +852,19 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
     for (int w = 0; w < 8; ++w)
       pb[w] = (int)cast4<kMode>(p, sa[w / 4][4 * (w % 4)], sa[w / 4][4 * (w % 4) + 1], sa[w / 4][4 * (w % 4) + 2],
                                 sa[w / 4][4 * (w % 4) + 3]);
+    if constexpr (kDiag) {  // masked keys have P = 0 and add nothing
+      float lo = 0.0f, ns = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const bool nonsink = has_bias ? bk[j] == 0.0f : true;
+        const bool zero = (((uint32_t)pb[j / 4] >> (8 * (j % 4))) & 0xFFu) == 0;
+        const float pj = sa[j / 16][j % 16];
+        ns += nonsink ? pj : 0.0f;
+        lo += (nonsink && zero) ? pj : 0.0f;
+      }
+      l_ns = l_ns * alpha + ns;
+      l_lost = l_lost * alpha + lo;
+    }
     if constexpr (kStats) {
       if (has_bias) {
         // per key: visible, non-sink, code zero
@@ -900,7 +931,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
     const bool diag = kCausal && (key0 + kKvBlock - 1 > wrow0);
     const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bbuf(cur)[lane] != 0.0f) != 0;
     const bool fast = vis && !diag && !has_bias;
-    if (fast && pend && vis1) {
+    if (!kDiag && fast && pend && vis1) {
       // Steady state: the step's MFMAs (20 at d = 128), each in a chunk of its own
       // with the fragment read two MFMAs ahead and a slice of VALU work that does
       // not depend on any MFMA in flight; sched_barrier fences keep the chunks in
@@ -1058,8 +1089,16 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
 
   // ---- epilogue: O = A / (S l) ----
   if (wave_active) {
-    const float inv = 1.0f / (p.S * halves_sum(l_run));
-    float* orow = p.out + (((int64_t)b * p.Hq + h) * p.N + myrow) * D;
+    const float l_all = halves_sum(l_run);
+    const float inv = 1.0f / (p.S * l_all);
+    const int64_t row = ((int64_t)b * p.Hq + h) * p.N + myrow;
+    if constexpr (kDiag) {
+      // log-sum-exp of the row's logits (natural units) and the lost non-sink mass fraction
+      const float ns = halves_sum(l_ns), lo = halves_sum(l_lost);
+      if (g == 0 && p.lse) p.lse[row] = (m_run + log2f(l_all)) * kLn2;
+      if (g == 0 && p.lost) p.lost[row] = ns > 0.0f ? lo / ns : 0.0f;
+    }
+    float* orow = p.out + row * D;
 #pragma unroll
     for (int dt = 0; dt < G::kDTiles; ++dt)
 #pragma unroll
@@ -1085,7 +1124,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
       atomicAdd(&lds_cnt[wave / 2][1], z);
     }
     __syncthreads();
-    if (tid < 2) {
+    if (tid < 2 && (!kDiag || p.stats)) {
       const int r64 = row0 / kKvBlock + tid;  // 64-row block index
       if (r64 * kKvBlock < p.N) {
         unsigned long long* st = p.stats + 2 * (((int64_t)b * p.Hq + h) * (p.N / kKvBlock) + r64);
@@ -1154,14 +1193,16 @@ void launch_attn3(const Params& p, hipStream_t stream) {
       hipLaunchKernelGGL((pcast_attn_fwd_bf16<D, kCausal, false>), grid, dim3(kThreads), 0, stream, p);
   } else if (p.k8) {
     if (p.stats)
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, true, true>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, true>), grid, dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, false, true>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, true>), grid, dim3(kThreads), 0, stream, p);
+  } else if (p.lse || p.lost) {
+    hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 2, false>), grid, dim3(kThreads), 0, stream, p);
   } else {
     if (p.stats)
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, true, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, false>), grid, dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, false, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, false>), grid, dim3(kThreads), 0, stream, p);
   }
 }
 
@@ -1313,9 +1354,12 @@ int check_qk8(float S) {
 
 int enqueue_attn(const void* Q, const void* K, const void* ws, const float* bias, int B, int Hq,
                  int Hkv, int N, int d, int causal, float S, int order, float* out,
-                 unsigned long long* stats, hipStream_t st, bool qk8 = false) {
+                 unsigned long long* stats, hipStream_t st, bool qk8 = false, float* lse = nullptr,
+                 float* lost = nullptr) {
   const bool fp8 = S != 0.0f;
   Params p{};
+  p.lse = lse;
+  p.lost = lost;
   if (qk8) {
     const Qk8Layout l = qk8_layout(B, Hkv, N, d);
     const uint8_t* base = static_cast<const uint8_t*>(ws);
@@ -1395,6 +1439,23 @@ int attn_fwd_pcast(const void* Q, const void* K, const void* V, const float* bia
   if (rc != PCAST_OK) return rc;
   if (e != hipSuccess) return hip_fail(e, "hipFreeAsync(workspace)");
   return PCAST_OK;
+}
+
+int attn_fwd_pcast_rows(const void* Q, const void* K, const void* workspace, const float* bias, int B,
+                        int Hq, int Hkv, int N, int d, int causal, float S, int order, float* out,
+                        unsigned long long* stats, float* lse, float* lost, void* stream) {
+  g_last_error[0] = '\0';
+  if (!workspace) return fail(PCAST_EINVAL, "workspace must be non-null");
+  if (!aligned(workspace, 16)) return fail(PCAST_EINVAL, "workspace must be 16-byte aligned");
+  int rc = check_attn_args(Q, K, bias, causal, order, out, stats);
+  if (rc != PCAST_OK) return rc;
+  if ((lse && !aligned(lse, 4)) || (lost && !aligned(lost, 4)))
+    return fail(PCAST_EINVAL, "lse and lost must be 4-byte aligned");
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  if (S == 0.0f) return fail(PCAST_ENOTSUP, "row diagnostics need S > 0 (the FP8 P.V path)");
+  if ((rc = check_device()) != PCAST_OK) return rc;
+  return enqueue_attn(Q, K, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
+                      static_cast<hipStream_t>(stream), false, lse, lost);
 }
 
 int pcast_prepare_qk8(const void* K, const void* V, int B, int Hkv, int N, int d, void* workspace,

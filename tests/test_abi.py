@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_sizes(lib):
-    assert lib.pcast_abi_version() == 2
+    assert lib.pcast_abi_version() == 3
     assert sna.stats_words(4, 32, 8192) == 4 * 32 * 128 * 2
     assert sna.stats_words(1, 1, 100) == 4
     assert sna.workspace_bytes(4, 32, 8192, 128, 256.0) == 4 * 32 * 8192 * 128
@@ -139,6 +139,22 @@ def test_prepare_qk8_argument_errors(lib, kw, code):
     a = dict(K=FAKE, V=FAKE, B=1, Hkv=1, N=128, d=128, workspace=FAKE, stream=0)
     a.update(kw)
     assert sna.prepare_qk8(**a) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(workspace=0), sna.PCAST_EINVAL),
+    (dict(Q=0), sna.PCAST_EINVAL),
+    (dict(lse=FAKE + 2), sna.PCAST_EINVAL),
+    (dict(lost=FAKE + 1), sna.PCAST_EINVAL),
+    (dict(order=3), sna.PCAST_EINVAL),
+    (dict(S=0.0), sna.PCAST_ENOTSUP),
+    (dict(d=32), sna.PCAST_ENOTSUP),
+])
+def test_rows_argument_errors(lib, kw, code):
+    a = dict(Q=FAKE, K=FAKE, workspace=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128, causal=1,
+             S=256.0, order=1, out=FAKE, stats=0, lse=FAKE, lost=FAKE, stream=0)
+    a.update(kw)
+    assert sna.attn_fwd_pcast_rows(**a) == code
 
 
 def test_strerror_texts(lib):
