@@ -16,6 +16,8 @@ Contents
 * ``qk8``       the FP8-logits extension: power-of-two block scales (per query
                 row, per 64-key block) and E4M3 rounding of Q and K
 * ``rowdiag``   per-row log-sum-exp and lost non-sink mass of the pipeline
+* ``decode``    decode rows with the keys in ranges that each run the pipeline,
+                merged by the online-softmax rescale
 * ``theory``    the closed forms F(Delta, S), delta_k, Delta_c and a Monte Carlo
                 of the collapse model
 
@@ -23,4 +25,4 @@ Parity pins: every function here is checked by ``tests/test_oracle_*.py``
 against facts fixed by the pages or by mathematics (see the test docstrings).
 """
 
-from . import e4m3, qk8, reference, rowdiag, theory  # noqa: F401
+from . import decode, e4m3, qk8, reference, rowdiag, theory  # noqa: F401
