@@ -14,7 +14,10 @@ peak, the CPU oracle timed on a bounded sample of the same workload, and the
 output MSE against fp64 attention on that sample for S=256 reverse and S=1
 forward.  The "qk_fp8" object times the variant with FP8 logits
 (pcast_prepare_qk8 + attn_fwd_pcast_qk8_prepared) on the same input, and its
-MSE against the same fp64 attention of the unquantised Q and K.
+MSE against the same fp64 attention of the unquantised Q and K.  The "decode"
+object times attn_decode_pcast (split KV) on the decode workload (16 sequences of
+16384 cached keys, one new token each, GQA 32/8) against the HBM roofline; its V
+copy is prepared once, outside the timed calls, as a cache would be.
 """
 from __future__ import annotations
 
@@ -107,6 +110,51 @@ def cpu_baseline(w, qb, kb, vb, bias, out_rev, out_fwd1, target_s: float, seed: 
     return base, mse
 
 
+def bench_decode(sna, torch, np, synthetic, dev, stream, steps, warmup):
+    w = synthetic.DECODE_WORKLOADS["decode"]
+    delta, S, order = w.cases[0]
+    qb, kb, vb = synthetic.decode_qkv_bf16(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.seed)
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    q, k, v = to(qb), to(kb), to(vb)
+    bias = torch.from_numpy(synthetic.sink_bias(w.Nk, delta)).to(dev)
+    sh = stream.cuda_stream
+    vop = torch.empty(sna.workspace_bytes(w.B, w.Hkv, w.Nk, w.d, S), dtype=torch.uint8, device=dev)
+    ws = torch.empty(sna.decode_workspace_bytes(w.B, w.Hkv, w.Nk, w.d, w.split_keys), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((w.B, w.Hq, w.Nq, w.d), dtype=torch.float32, device=dev)
+    st = torch.empty(sna.stats_words(w.B, w.Hq, w.Nq), dtype=torch.int64, device=dev)
+    rc = sna.prepare_v(v.data_ptr(), w.B, w.Hkv, w.Nk, w.d, S, vop.data_ptr(), sh)
+
+    def call():
+        r = sna.attn_decode_pcast(q.data_ptr(), k.data_ptr(), vop.data_ptr(), bias.data_ptr(), w.B, w.Hq, w.Hkv,
+                                  w.Nq, w.Nk, w.d, S, order, w.split_keys, out.data_ptr(), st.data_ptr(),
+                                  ws.data_ptr(), sh)
+        if r != sna.PCAST_OK:
+            raise sna.PcastError(r, sna.strerror(r))
+
+    if rc != sna.PCAST_OK:
+        raise sna.PcastError(rc, sna.strerror(rc))
+    for _ in range(warmup):
+        call()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    gbs = w.bytes / (ms * 1e-3) / 1e9
+    print(f"[bench] decode {w.name}: {ms:.4f} ms per call ({gbs:.0f} GB/s)", file=sys.stderr, flush=True)
+    return {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} d={w.d}, "
+                        f"split_keys={w.split_keys}, sink bias {delta} on keys 0..3, S={S:g}, "
+                        f"{'reverse' if order else 'forward'} order, counters on",
+            "ms_per_call": round(ms, 5), "kernels": "pcast_decode_split + pcast_decode_merge",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                         "frac": round(gbs / 8000.0, 4), "algorithmic_bytes": w.bytes},
+            "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +165,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-qk8", action="store_true", help="skip the FP8-logit variant")
+    ap.add_argument("--no-decode", action="store_true", help="skip the split-KV decode measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes, 3 times (scale for "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
@@ -260,6 +309,9 @@ def main() -> int:
                             "achieved": round(ach8, 2), "peak": PEAK_FP8, "frac": round(ach8 / PEAK_FP8, 4),
                             "traffic": measured_traffic(w.name, TRAFFIC_FILE_QK8)}
         out_qk8 = out.cpu().numpy()
+
+    if not args.no_decode:
+        result["decode"] = bench_decode(sna, torch, np, synthetic, dev, stream, args.steps, args.warmup)
 
     if not args.no_cpu_baseline:
         # S = 1 forward, for the error contrast, with the per-row diagnostics (same out, bit for bit)

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define PCAST_ABI_VERSION 3
+#define PCAST_ABI_VERSION 4
 
 /* Keys per KV block.  The block size is part of the numerics (the running
  * max is updated once per block), so it is fixed. */
@@ -157,6 +157,43 @@ double pcast_sink_max_mean(int k);
 double pcast_delta_critical(double S, int k);
 double pcast_underflow_model(double delta, double S, int k);
 double pcast_lost_mass_model(double delta, double S, int k);
+
+/*
+ * attn_decode_pcast -- decode with split KV: Nq query rows at the end of a
+ * sequence of Nk keys, the keys cut into ranges of split_keys keys that each
+ * run the P-cast pipeline from their own running max, merged by rescaling the
+ * ranges' (m, l, A) to their common max (FlashAttention blog, section "La
+ * ricorrenza softmax online"; the P-cast summary, section 1, ties the cast to
+ * the running max the pipeline holds, so the split is part of the numerics:
+ * a sink only raises the max of its own range).
+ *
+ * Q      device, bf16 [B][Hq][Nq][d]; row i is at position Nk - Nq + i and sees
+ *        keys j <= Nk - Nq + i (every key when Nq = 1).
+ * K      device, bf16 [B][Hkv][Nk][d].
+ * vop    device, the V operand copy written by pcast_prepare_v(V, B, Hkv, Nk,
+ *        d, S > 0, ...): E4M3 V, reusable across calls while V is unchanged.
+ * bias   device, float32 [Nk] per-key logit bias, or NULL (sinks: bias != 0).
+ * Nq     1 <= Nq and (Hq / Hkv) * Nq <= 32 (the query heads of one kv head
+ *        and their rows share one 32-column MFMA tile), else PCAST_ENOTSUP.
+ * Nk     a multiple of 64.
+ * split_keys  keys per range, a positive multiple of 64 (PCAST_EINVAL
+ *        otherwise); the last range may be shorter.  split_keys >= Nk gives
+ *        the P-cast path itself.
+ * S, order, d as for attn_fwd_pcast; S must be > 0 (PCAST_ENOTSUP for 0).
+ * out    device, float32 [B][Hq][Nq][d].
+ * stats  device, uint64 [pcast_stats_words(B, Hq, Nq)] or NULL: per (b, h)
+ *        the non-sink (query, key) pairs of its Nq rows and those with code 0.
+ * workspace  device, pcast_decode_workspace_bytes(B, Hkv, Nk, d, split_keys)
+ *        bytes, 16-byte aligned, owned by the caller: the ranges' partial
+ *        results.  Allocates nothing.
+ * Two kernels run on `stream`: one wave per (b, kv head, range), then one
+ * workgroup per (b, kv head) for the merge.
+ */
+size_t pcast_decode_workspace_bytes(int B, int Hkv, int Nk, int d, int split_keys);
+
+int attn_decode_pcast(const void* Q, const void* K, const void* vop, const float* bias, int B, int Hq,
+                      int Hkv, int Nq, int Nk, int d, float S, int order, int split_keys, float* out,
+                      unsigned long long* stats, void* workspace, void* stream);
 
 /*
  * The forward with FP8 logits: Q and K rounded to E4M3 as well, so that Q K^T

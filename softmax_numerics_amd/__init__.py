@@ -23,7 +23,8 @@ EXPORTS = ("attn_fwd_pcast", "pcast_prepare_v", "attn_fwd_pcast_prepared", "pcas
            "pcast_workspace_bytes", "pcast_strerror", "pcast_abi_version", "pcast_workspace_bytes_qk8",
            "pcast_prepare_qk8", "attn_fwd_pcast_qk8_prepared", "attn_fwd_pcast_qk8",
            "attn_fwd_pcast_rows", "pcast_sink_max_mean", "pcast_delta_critical",
-           "pcast_underflow_model", "pcast_lost_mass_model")
+           "pcast_underflow_model", "pcast_lost_mass_model", "attn_decode_pcast",
+           "pcast_decode_workspace_bytes")
 
 _lock = threading.Lock()
 _lib = None
@@ -71,6 +72,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_fwd_pcast_qk8.restype = I
             lib.attn_fwd_pcast_rows.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P, P, P]
             lib.attn_fwd_pcast_rows.restype = I
+            lib.attn_decode_pcast.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I, I, P, P, P, P]
+            lib.attn_decode_pcast.restype = I
+            lib.pcast_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+            lib.pcast_decode_workspace_bytes.restype = ctypes.c_size_t
             D = ctypes.c_double
             lib.pcast_sink_max_mean.argtypes = [I]
             lib.pcast_sink_max_mean.restype = D
@@ -132,6 +137,18 @@ def attn_fwd_pcast_rows(Q, K, workspace, bias, B, Hq, Hkv, N, d, causal, S, orde
     return int(load_library().attn_fwd_pcast_rows(
         Q, K, workspace, bias or None, B, Hq, Hkv, N, d, int(causal), float(S), int(order), out,
         stats or None, lse or None, lost or None, stream or None))
+
+
+def attn_decode_pcast(Q, K, vop, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out, stats, workspace,
+                      stream) -> int:
+    """Raw attn_decode_pcast with integer device addresses (0 for NULL); returns the C return code."""
+    return int(load_library().attn_decode_pcast(
+        Q, K, vop, bias or None, B, Hq, Hkv, Nq, Nk, d, float(S), int(order), int(split_keys), out,
+        stats or None, workspace, stream or None))
+
+
+def decode_workspace_bytes(B: int, Hkv: int, Nk: int, d: int, split_keys: int) -> int:
+    return int(load_library().pcast_decode_workspace_bytes(B, Hkv, Nk, d, split_keys))
 
 
 def sink_max_mean(k: int = 4) -> float:

@@ -226,6 +226,12 @@ struct Params {
   // per-row diagnostics [B][Hq][N], or null
   float* lse;
   float* lost;
+  // decode with split KV: Nq query rows at the end of Nk keys, ranges of split_blocks
+  // key blocks, partial results per (b, kv head, range, packed row)
+  int Nq, Nk, n_split, split_blocks;
+  float* part_a;          // [..][32][D] un-normalised accumulator
+  float* part_ml;         // [..][32][2] running max (log2 units) and row sum
+  unsigned int* part_cnt; // [..][32][2] non-sink pairs, zero codes
 };
 
 // How P becomes an MFMA operand.
@@ -1136,6 +1142,291 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
 }
 
 // ---------------------------------------------------------------------------
+// Decode with split KV.  One wave per workgroup; workgroup (b, kv head, range)
+// takes the G = Hq/Hkv query heads times Nq rows that read this kv head, packed
+// into the 32 MFMA columns (lanes l and l + 32 hold packed row l: head l / Nq,
+// query l % Nq; rows past G*Nq are padding with Q = 0), runs the P-cast pipeline
+// over the range's key blocks from its own m = -inf, and writes the partial
+// (m, l, A) and counters of each row.  pcast_decode_merge rescales the ranges to
+// their common max and adds them.  Rows sit at the last Nq positions: row i sees
+// keys j <= Nk - Nq + i.
+// ---------------------------------------------------------------------------
+template <int D, int kMode, bool kStats>
+__global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
+  static_assert(kMode != kBf16, "FP8 modes only");
+  using G = Geometry<D>;
+  constexpr int kKRow = D * 2;
+  constexpr int kVRow = kKvBlock;
+  constexpr int kKTile = kKvBlock * kKRow;
+  constexpr int kVTile = D * kVRow;
+  using SK = Swizzle<kKRow>;
+  using SV = Swizzle<kVRow>;
+  constexpr int kKLoads = kKTile / 1024;  // 1 KB direct loads per block (one wave)
+  constexpr int kVLoads = kVTile / 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[kKTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[kKTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[kVTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[kVTile];
+  __shared__ __attribute__((aligned(16))) float lds_b0[kKvBlock];
+  __shared__ __attribute__((aligned(16))) float lds_b1[kKvBlock];
+  auto kbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_k1 : lds_k0; };
+  auto vbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_v1 : lds_v0; };
+  auto bbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_b1 : lds_b0; };
+
+  const int lane = threadIdx.x;
+  const int g = lane / 32, li = lane % 32;
+  const int n_blk = p.Nk / kKvBlock;
+  const int split = blockIdx.x % p.n_split;
+  const int bhk = blockIdx.x / p.n_split;
+  const int hk = bhk % p.Hkv, b = bhk / p.Hkv;
+  const int Gq = p.Hq / p.Hkv;
+  const bool row_ok = li < Gq * p.Nq;
+  const int h = hk * Gq + (row_ok ? li / p.Nq : 0);
+  const int qi = row_ok ? li % p.Nq : 0;
+  const int pos = p.Nk - p.Nq + qi;  // the row's position
+  const int t_first = split * p.split_blocks;
+  const int t_end = min(t_first + p.split_blocks, n_blk);
+  const int n_it = t_end - t_first;
+  const float c = p.logit_scale;
+  const bool with_bias = p.bias != nullptr;
+
+  bf16x8_t qf[G::kQSteps];
+  {
+    const uint16_t* qrow = p.q + (((int64_t)b * p.Hq + h) * p.Nq + qi) * D + g * 8;
+#pragma unroll
+    for (int s = 0; s < G::kQSteps; ++s) {
+      bf16x8_t z = {};
+      qf[s] = row_ok ? *reinterpret_cast<const bf16x8_t*>(qrow + s * 16) : z;
+    }
+  }
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k + ((int64_t)b * p.Hkv + hk) * p.Nk * D);
+  const uint8_t* vbase = static_cast<const uint8_t*>(p.vop) + ((int64_t)b * p.Hkv + hk) * (int64_t)n_blk * kVTile;
+  auto tile_of = [&](int it) __attribute__((always_inline)) { return p.order ? (t_end - 1 - it) : (t_first + it); };
+  // load i fills LDS chunk position i * 64 + lane, which holds logical chunk position ^ key(row)
+  auto load_k = [&](int t, int buf) __attribute__((always_inline)) {
+    const uint8_t* ks = kbase + (int64_t)t * kKTile;
+#pragma unroll
+    for (int i = 0; i < kKLoads; ++i) {
+      const int cp = i * 64 + lane, r = cp / SK::kChunks;
+      load_to_lds16(ks + r * kKRow + (((cp % SK::kChunks) ^ SK::key(r)) << 4), kbuf(buf) + i * 1024);
+    }
+  };
+  auto load_v = [&](int t, int buf) __attribute__((always_inline)) {
+    const uint8_t* vs = vbase + (int64_t)t * kVTile;
+#pragma unroll
+    for (int i = 0; i < kVLoads; ++i) {
+      const int cp = i * 64 + lane, r = cp / SV::kChunks;
+      load_to_lds16(vs + r * kVRow + (((cp % SV::kChunks) ^ SV::key(r)) << 4), vbuf(buf) + i * 1024);
+    }
+  };
+  auto load_b = [&](int t, int buf) __attribute__((always_inline)) {
+    if (with_bias) load_to_lds4(p.bias + t * kKvBlock + lane, bbuf(buf));
+  };
+  auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  const int xk = SK::key(li);
+  auto issue_s = [&](int buf, f32x16_t(&sa)[2]) __attribute__((always_inline)) {
+    const uint8_t* kl = kbuf(buf) + li * kKRow;
+#pragma unroll
+    for (int s = 0; s < G::kQSteps; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + kb * 32 * kKRow + (((2 * s + g) ^ xk) << 4));
+        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16_t{} : sa[kb], 0, 0, 0);
+      }
+  };
+  f32x16_t oacc[G::kDTiles];
+#pragma unroll
+  for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+  auto accumulate = [&](int buf, const i32x8_t& pb) __attribute__((always_inline)) {
+    const uint8_t* vl = vbuf(buf) + li * kVRow;
+    const int xv = SV::key(li);
+    const int vlo = ((2 * g) ^ xv) << 4, vhi = ((2 * g + 1) ^ xv) << 4;
+#pragma unroll
+    for (int dt = 0; dt < G::kDTiles; ++dt) {
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vlo);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vhi);
+      const i32x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, oacc[dt], 0, 0, 0, 0, 0, 0);
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  unsigned int cnt_tot = 0, cnt_zero = 0;
+  f32x16_t sacc[2];
+  i32x8_t pb;
+
+  auto step = [&](int it, auto cur_c) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
+    const int t = tile_of(it);
+    if (it + 1 < n_it) {
+      load_k(tile_of(it + 1), nxt);
+      load_v(tile_of(it + 1), nxt);
+      load_b(tile_of(it + 1), nxt);
+    }
+    issue_s(cur, sacc);
+    const int key0 = t * kKvBlock;
+    const bool mask = key0 + kKvBlock - 1 > p.Nk - p.Nq;  // some row cannot see some key
+    const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bbuf(cur)[lane] != 0.0f) != 0;
+    float bk[32];
+    if (has_bias) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(bbuf(cur) + slot_key(g, 4 * q));
+        bk[4 * q] = v.x; bk[4 * q + 1] = v.y; bk[4 * q + 2] = v.z; bk[4 * q + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      float xj = has_bias ? fmaf(sacc[j / 16][j % 16], c, bk[j] * kLog2e) : sacc[j / 16][j % 16] * c;
+      if (mask && key0 + slot_key(g, j) > pos) xj = -INFINITY;
+      sacc[j / 16][j % 16] = xj;
+    }
+    float m4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      m4[q] = fmaxf(sacc[q / 2][(q % 2) * 8], sacc[q / 2][(q % 2) * 8 + 1]);
+#pragma unroll
+      for (int r = 2; r < 8; r += 2)
+        m4[q] = fmaxf(fmaxf(m4[q], sacc[q / 2][(q % 2) * 8 + r]), sacc[q / 2][(q % 2) * 8 + r + 1]);
+    }
+    // every row sees at least one key of every block (Nq <= 32 < 64), so m_new is finite
+    const float m_new = fmaxf(m_run, halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))));
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float pj = __builtin_amdgcn_exp2f(sacc[j / 16][j % 16] - m_new);
+      sacc[j / 16][j % 16] = pj;
+      ps[j % 4] += pj;
+    }
+    l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    m_run = m_new;
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+      pb[w] = (int)cast4<kMode>(p, sacc[w / 4][4 * (w % 4)], sacc[w / 4][4 * (w % 4) + 1],
+                                sacc[w / 4][4 * (w % 4) + 2], sacc[w / 4][4 * (w % 4) + 3]);
+    if constexpr (kStats) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const bool vis = !mask || key0 + slot_key(g, j) <= pos;
+        const bool nonsink = has_bias ? bk[j] == 0.0f : true;
+        const bool z = (((uint32_t)pb[j / 4] >> (8 * (j % 4))) & 0xFFu) == 0;
+        cnt_tot += (vis && nonsink);
+        cnt_zero += (vis && nonsink && z);
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+    accumulate(cur, pb);
+    wait_loads();
+    __syncthreads();
+  };
+
+  load_k(tile_of(0), 0);
+  load_v(tile_of(0), 0);
+  load_b(tile_of(0), 0);
+  wait_loads();
+  __syncthreads();
+  for (int it = 0; it < n_it; it += 2) {
+    step(it, BufIndex<0>{});
+    if (it + 1 < n_it) step(it + 1, BufIndex<1>{});
+  }
+
+  // partial results of this range, one slot per packed row
+  const int64_t slot = ((int64_t)bhk * p.n_split + split) * 32 + li;
+  float* arow = p.part_a + slot * D;
+#pragma unroll
+  for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float4 v;
+      v.x = oacc[dt][r4 * 4 + 0];
+      v.y = oacc[dt][r4 * 4 + 1];
+      v.z = oacc[dt][r4 * 4 + 2];
+      v.w = oacc[dt][r4 * 4 + 3];
+      *reinterpret_cast<float4*>(arow + dt * 32 + r4 * 8 + g * 4) = v;
+    }
+  const float l_all = halves_sum(l_run);
+  const unsigned int tot = cnt_tot + (unsigned int)__shfl_xor((int)cnt_tot, 32);
+  const unsigned int zer = cnt_zero + (unsigned int)__shfl_xor((int)cnt_zero, 32);
+  if (g == 0) {
+    *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m_run, l_all);
+    if constexpr (kStats) {
+      p.part_cnt[slot * 2] = row_ok ? tot : 0u;
+      p.part_cnt[slot * 2 + 1] = row_ok ? zer : 0u;
+    }
+  }
+}
+
+// One workgroup per (b, kv head): thread t merges packed row t / 8, columns
+// (t % 8) * 4 + 32 j, over the ranges: M = max m_r, O = sum 2^(m_r - M) A_r /
+// (S sum 2^(m_r - M) l_r); counters are summed per (b, query head).
+template <int D, bool kStats>
+__global__ __launch_bounds__(256) void pcast_decode_merge(const Params p) {
+  constexpr int kJ = D / 32;
+  const int bhk = blockIdx.x;
+  const int hk = bhk % p.Hkv, b = bhk / p.Hkv;
+  const int Gq = p.Hq / p.Hkv;
+  const int r = threadIdx.x / 8, cp = threadIdx.x % 8;
+  const int R = Gq * p.Nq;
+  __shared__ unsigned long long cnt[32][2];
+  if (kStats && threadIdx.x < 64) cnt[threadIdx.x / 2][threadIdx.x % 2] = 0;
+  __syncthreads();
+  if (r < R) {
+    const int64_t slot0 = (int64_t)bhk * p.n_split * 32 + r;
+    float M = -INFINITY;
+    for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, p.part_ml[(slot0 + s * 32) * 2]);
+    float L = 0.0f;
+    float4 acc[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) acc[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    unsigned long long tot = 0, zer = 0;
+    for (int s = 0; s < p.n_split; ++s) {
+      const int64_t slot = slot0 + s * 32;
+      const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + slot * 2);
+      const float w = __builtin_amdgcn_exp2f(ml.x - M);
+      L += w * ml.y;
+      const float* a = p.part_a + slot * D + cp * 4;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const float4 v = *reinterpret_cast<const float4*>(a + j * 32);
+        acc[j].x += w * v.x; acc[j].y += w * v.y; acc[j].z += w * v.z; acc[j].w += w * v.w;
+      }
+      if (kStats && cp == 0) {
+        tot += p.part_cnt[slot * 2];
+        zer += p.part_cnt[slot * 2 + 1];
+      }
+    }
+    const float inv = 1.0f / (p.S * L);
+    const int h = hk * Gq + r / p.Nq, qi = r % p.Nq;
+    float* orow = p.out + (((int64_t)b * p.Hq + h) * p.Nq + qi) * D + cp * 4;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+      *reinterpret_cast<float4*>(orow + j * 32) =
+          make_float4(acc[j].x * inv, acc[j].y * inv, acc[j].z * inv, acc[j].w * inv);
+    if (kStats && cp == 0) {
+      atomicAdd(&cnt[r / p.Nq][0], tot);
+      atomicAdd(&cnt[r / p.Nq][1], zer);
+    }
+  }
+  if constexpr (kStats) {
+    __syncthreads();
+    if (threadIdx.x < Gq) {
+      unsigned long long* st = p.stats + 2 * ((int64_t)b * p.Hq + hk * Gq + threadIdx.x);
+      st[0] = cnt[threadIdx.x][0];
+      st[1] = cnt[threadIdx.x][1];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 thread_local char g_last_error[512] = "";
@@ -1225,6 +1516,24 @@ void launch_attn(const Params& p, int mode, int causal, hipStream_t stream) {
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
+// Workspace of the split-KV decode: per (b, kv head, range, packed row) the partial
+// accumulator [D] fp32, then (m, l) fp32, then the two counters u32; 256-aligned parts.
+struct DecodeLayout {
+  int n_split;
+  size_t a, ml, cnt, total;
+};
+DecodeLayout decode_layout(int B, int Hkv, int Nk, int d, int split_keys) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  DecodeLayout l;
+  l.n_split = (Nk + split_keys - 1) / split_keys;
+  const size_t slots = (size_t)B * Hkv * l.n_split * 32;
+  l.a = 0;
+  l.ml = up(slots * d * 4);
+  l.cnt = up(l.ml + slots * 2 * 4);
+  l.total = up(l.cnt + slots * 2 * 4);
+  return l;
+}
+
 // Workspace of the FP8-logit path, byte offsets from its start (each 256-aligned):
 // the V operand copy (as in the plain workspace), the E4M3 codes of K in K's own
 // layout, and the exponent of each key block's scale (int32).
@@ -1253,6 +1562,11 @@ size_t pcast_stats_words(int B, int Hq, int N) {
 size_t pcast_workspace_bytes(int B, int Hkv, int N, int d, float S) {
   if (B <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return 0;
   return (size_t)B * Hkv * N * d * ((S == 0.0f) ? 2 : 1);
+}
+
+size_t pcast_decode_workspace_bytes(int B, int Hkv, int Nk, int d, int split_keys) {
+  if (B <= 0 || Hkv <= 0 || Nk <= 0 || d <= 0 || split_keys <= 0) return 0;
+  return decode_layout(B, Hkv, Nk, d, split_keys).total;
 }
 
 size_t pcast_workspace_bytes_qk8(int B, int Hkv, int N, int d) {
@@ -1456,6 +1770,81 @@ int attn_fwd_pcast_rows(const void* Q, const void* K, const void* workspace, con
   if ((rc = check_device()) != PCAST_OK) return rc;
   return enqueue_attn(Q, K, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
                       static_cast<hipStream_t>(stream), false, lse, lost);
+}
+
+int attn_decode_pcast(const void* Q, const void* K, const void* vop, const float* bias, int B, int Hq,
+                      int Hkv, int Nq, int Nk, int d, float S, int order, int split_keys, float* out,
+                      unsigned long long* stats, void* workspace, void* stream) {
+  g_last_error[0] = '\0';
+  if (!Q || !K || !vop || !out || !workspace)
+    return fail(PCAST_EINVAL, "Q, K, vop, out and workspace must be non-null");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(vop, 16) || !aligned(out, 16) || !aligned(workspace, 16))
+    return fail(PCAST_EINVAL, "Q, K, vop, out and workspace must be 16-byte aligned");
+  if (bias && !aligned(bias, 4)) return fail(PCAST_EINVAL, "bias must be 4-byte aligned");
+  if (stats && !aligned(stats, 8)) return fail(PCAST_EINVAL, "stats must be 8-byte aligned");
+  if (order != PCAST_ORDER_FORWARD && order != PCAST_ORDER_REVERSE)
+    return fail(PCAST_EINVAL, "order must be 0 (forward) or 1 (reverse)");
+  if (Nq <= 0) return fail(PCAST_EINVAL, "Nq must be positive");
+  if (split_keys <= 0 || split_keys % kKvBlock != 0)
+    return fail(PCAST_EINVAL, "split_keys must be a positive multiple of %d", kKvBlock);
+  int rc = check_shape(B, Hq, Hkv, Nk, d, S);
+  if (rc != PCAST_OK) return rc;
+  if (S == 0.0f) return fail(PCAST_ENOTSUP, "decode needs S > 0 (the FP8 P.V path)");
+  if ((int64_t)(Hq / Hkv) * Nq > 32)
+    return fail(PCAST_ENOTSUP, "(Hq / Hkv) * Nq = %lld: at most 32 rows per kv head", (long long)(Hq / Hkv) * Nq);
+  const DecodeLayout l = decode_layout(B, Hkv, Nk, d, split_keys);
+  if ((int64_t)B * Hkv * l.n_split > (int64_t)INT32_MAX) return fail(PCAST_ENOTSUP, "grid too large");
+  if ((rc = check_device()) != PCAST_OK) return rc;
+
+  Params p{};
+  p.q = static_cast<const uint16_t*>(Q);
+  p.k = static_cast<const uint16_t*>(K);
+  p.vop = vop;
+  p.bias = bias;
+  p.out = out;
+  p.stats = stats;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = Nk;
+  p.order = order;
+  p.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)d));
+  p.S = S;
+  p.inv_S = 1.0f / S;
+  p.p_clamp = 448.0f / S;
+  p.Nq = Nq; p.Nk = Nk; p.n_split = l.n_split; p.split_blocks = split_keys / kKvBlock;
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  p.part_a = reinterpret_cast<float*>(base + l.a);
+  p.part_ml = reinterpret_cast<float*>(base + l.ml);
+  p.part_cnt = reinterpret_cast<unsigned int*>(base + l.cnt);
+  const int mode = (is_pow2(S) ? kPow2 : kMul) + (S > 448.0f ? 1 : 0);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)(B * Hkv * l.n_split)), mgrid((unsigned)(B * Hkv));
+#define PCAST_DECODE(DD, MM)                                                                        \
+  do {                                                                                              \
+    if (stats) {                                                                                    \
+      hipLaunchKernelGGL((pcast_decode_split<DD, MM, true>), grid, dim3(64), 0, st, p);             \
+      hipLaunchKernelGGL((pcast_decode_merge<DD, true>), mgrid, dim3(256), 0, st, p);               \
+    } else {                                                                                        \
+      hipLaunchKernelGGL((pcast_decode_split<DD, MM, false>), grid, dim3(64), 0, st, p);            \
+      hipLaunchKernelGGL((pcast_decode_merge<DD, false>), mgrid, dim3(256), 0, st, p);              \
+    }                                                                                               \
+  } while (0)
+  if (d == 64) {
+    switch (mode) {
+      case kPow2: PCAST_DECODE(64, kPow2); break;
+      case kPow2Clamp: PCAST_DECODE(64, kPow2Clamp); break;
+      case kMul: PCAST_DECODE(64, kMul); break;
+      default: PCAST_DECODE(64, kMulClamp); break;
+    }
+  } else {
+    switch (mode) {
+      case kPow2: PCAST_DECODE(128, kPow2); break;
+      case kPow2Clamp: PCAST_DECODE(128, kPow2Clamp); break;
+      case kMul: PCAST_DECODE(128, kMul); break;
+      default: PCAST_DECODE(128, kMulClamp); break;
+    }
+  }
+#undef PCAST_DECODE
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PCAST_OK : hip_fail(e, "decode kernel launch");
 }
 
 int pcast_prepare_qk8(const void* K, const void* V, int B, int Hkv, int N, int d, void* workspace,

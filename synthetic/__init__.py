@@ -19,7 +19,7 @@ import threading
 
 import numpy as np
 
-from .workloads import WORKLOADS, Workload  # noqa: F401
+from .workloads import DECODE_WORKLOADS, WORKLOADS, DecodeWorkload, Workload  # noqa: F401
 
 SINK_KEYS = 4
 TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2
@@ -94,4 +94,12 @@ def qkv_bf16(B: int, Hq: int, Hkv: int, N: int, d: int, seed: int):
     q = gaussian_bf16(seed, TENSOR_Q, (B, Hq, N, d))
     k = gaussian_bf16(seed, TENSOR_K, (B, Hkv, N, d))
     v = gaussian_bf16(seed, TENSOR_V, (B, Hkv, N, d))
+    return q, k, v
+
+
+def decode_qkv_bf16(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int):
+    """(Q, K, V) bf16 bit arrays for decode: [B,Hq,Nq,d], [B,Hkv,Nk,d], [B,Hkv,Nk,d]."""
+    q = gaussian_bf16(seed, TENSOR_Q, (B, Hq, Nq, d))
+    k = gaussian_bf16(seed, TENSOR_K, (B, Hkv, Nk, d))
+    v = gaussian_bf16(seed, TENSOR_V, (B, Hkv, Nk, d))
     return q, k, v

@@ -51,3 +51,41 @@ WORKLOADS = {
     "long": Workload("long", 1, 16, 4, 131072, 128, True, 5,
                      tuple((dl, 256.0, o) for dl in (5.0, 7.0, 9.0) for o in (0, 1))),
 }
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Decode with split KV: Nq new query rows per sequence against Nk cached keys,
+    the keys cut into ranges of split_keys."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    split_keys: int
+    seed: int
+    cases: tuple = field(default_factory=tuple)
+
+    @property
+    def flops(self) -> float:
+        """4 * d flops per visible (query, key) pair (rows at the last Nq positions)."""
+        pairs = self.Nq * self.Nk - self.Nq * (self.Nq - 1) // 2
+        return 4.0 * self.B * self.Hq * pairs * self.d
+
+    @property
+    def bytes(self) -> int:
+        """Compulsory HBM bytes of one call: Q and K (bf16) and the E4M3 V copy read
+        once, out (fp32) written once."""
+        return self.B * (self.Hq * self.Nq * self.d * (2 + 4) + self.Hkv * self.Nk * self.d * (2 + 1))
+
+
+DECODE_WORKLOADS = {
+    # one new token for each of 16 sequences of 16k cached keys, GQA 32 / 8
+    "decode": DecodeWorkload("decode", 16, 32, 8, 1, 16384, 128, 1024, 6,
+                             ((7.0, 256.0, 1), (7.0, 1.0, 0))),
+    # four new tokens of one 128k-key sequence
+    "decode_long": DecodeWorkload("decode_long", 1, 32, 8, 4, 131072, 128, 4096, 7,
+                                  ((7.0, 256.0, 1),)),
+}

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_sizes(lib):
-    assert lib.pcast_abi_version() == 3
+    assert lib.pcast_abi_version() == 4
     assert sna.stats_words(4, 32, 8192) == 4 * 32 * 128 * 2
     assert sna.stats_words(1, 1, 100) == 4
     assert sna.workspace_bytes(4, 32, 8192, 128, 256.0) == 4 * 32 * 8192 * 128
@@ -155,6 +155,37 @@ def test_rows_argument_errors(lib, kw, code):
              S=256.0, order=1, out=FAKE, stats=0, lse=FAKE, lost=FAKE, stream=0)
     a.update(kw)
     assert sna.attn_fwd_pcast_rows(**a) == code
+
+
+def test_decode_workspace_layout(lib):
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for B, Hkv, Nk, d, split in ((16, 8, 16384, 128, 1024), (1, 1, 64, 64, 64), (2, 3, 1000 * 64, 128, 4096)):
+        n = -(-Nk // split)
+        slots = B * Hkv * n * 32
+        want = up(up(up(slots * d * 4) + slots * 8) + slots * 8)
+        assert sna.decode_workspace_bytes(B, Hkv, Nk, d, split) == want
+    assert sna.decode_workspace_bytes(1, 1, 64, 64, 0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=0), sna.PCAST_EINVAL),
+    (dict(vop=0), sna.PCAST_EINVAL),
+    (dict(workspace=FAKE + 8), sna.PCAST_EINVAL),
+    (dict(Nq=0), sna.PCAST_EINVAL),
+    (dict(split_keys=100), sna.PCAST_EINVAL),
+    (dict(split_keys=0), sna.PCAST_EINVAL),
+    (dict(order=2), sna.PCAST_EINVAL),
+    (dict(Hq=3, Hkv=2), sna.PCAST_EINVAL),
+    (dict(S=0.0), sna.PCAST_ENOTSUP),
+    (dict(Hq=32, Hkv=8, Nq=9), sna.PCAST_ENOTSUP),
+    (dict(Nk=1000), sna.PCAST_ENOTSUP),
+    (dict(d=80), sna.PCAST_ENOTSUP),
+])
+def test_decode_argument_errors(lib, kw, code):
+    a = dict(Q=FAKE, K=FAKE, vop=FAKE, bias=0, B=1, Hq=8, Hkv=2, Nq=1, Nk=1024, d=128, S=256.0, order=1,
+             split_keys=256, out=FAKE, stats=0, workspace=FAKE, stream=0)
+    a.update(kw)
+    assert sna.attn_decode_pcast(**a) == code
 
 
 def test_strerror_texts(lib):
