@@ -18,6 +18,8 @@ Contents
 * ``rowdiag``   per-row log-sum-exp and lost non-sink mass of the pipeline
 * ``decode``    decode rows with the keys in ranges that each run the pipeline,
                 merged by the online-softmax rescale
+* ``backward``  gradients by recomputation from the log-sum-exp (cast passed
+                straight through)
 * ``theory``    the closed forms F(Delta, S), delta_k, Delta_c and a Monte Carlo
                 of the collapse model
 
@@ -25,4 +27,4 @@ Parity pins: every function here is checked by ``tests/test_oracle_*.py``
 against facts fixed by the pages or by mathematics (see the test docstrings).
 """
 
-from . import decode, e4m3, qk8, reference, rowdiag, theory  # noqa: F401
+from . import backward, decode, e4m3, qk8, reference, rowdiag, theory  # noqa: F401
