@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define PCAST_ABI_VERSION 4
+#define PCAST_ABI_VERSION 5
 
 /* Keys per KV block.  The block size is part of the numerics (the running
  * max is updated once per block), so it is fixed. */
@@ -157,6 +157,36 @@ double pcast_sink_max_mean(int k);
 double pcast_delta_critical(double S, int k);
 double pcast_underflow_model(double delta, double S, int k);
 double pcast_lost_mass_model(double delta, double S, int k);
+
+/*
+ * attn_bwd_pcast -- gradients of the forward by recomputation from its
+ * log-sum-exp (FlashAttention blog, section "Passaggio all'indietro: ricalcolo
+ * anziché archiviazione": only O and the softmax statistics are kept, the
+ * probability tiles are recomputed).  The P-cast is passed straight through
+ * (its derivative taken as 1): with s_ij = q_i.k_j/sqrt(d) + bias_j over the
+ * visible keys, P = exp(s - lse), dP = dO V^T, D_i = dO_i . O_i,
+ * dS = P (dP - D), dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d), dV = P^T dO;
+ * dK and dV of a kv head sum over its Hq/Hkv query heads.
+ *
+ * Q, K, V  device, bf16, layouts as for attn_fwd_pcast.
+ * O        device, float32 [B][Hq][N][d]: the forward's output.
+ * dO       device, bf16 [B][Hq][N][d].
+ * lse      device, float32 [B][Hq][N]: the forward's log-sum-exp (as written by
+ *          attn_fwd_pcast_rows, natural units).
+ * bias, B, Hq, Hkv, N, d, causal as for attn_fwd_pcast.
+ * dQ       device, float32 [B][Hq][N][d]; dK, dV device, float32 [B][Hkv][N][d];
+ *          written completely.
+ * workspace  device, pcast_bwd_workspace_bytes(B, Hq, Hkv, N, d) bytes, 16-byte
+ *          aligned, owned by the caller (transposed copies of K, Q, dO and D).
+ * All products run on bf16 matrix cores with fp32 accumulation; P and dS are
+ * rounded to bf16 where they are operands.  Allocates nothing; errors as for
+ * attn_fwd_pcast.
+ */
+size_t pcast_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+
+int attn_bwd_pcast(const void* Q, const void* K, const void* V, const float* O, const void* dO,
+                   const float* lse, const float* bias, int B, int Hq, int Hkv, int N, int d, int causal,
+                   float* dQ, float* dK, float* dV, void* workspace, void* stream);
 
 /*
  * attn_decode_pcast -- decode with split KV: Nq query rows at the end of a

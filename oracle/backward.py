@@ -32,7 +32,10 @@ def _bf16(bits):
 def grads(q_bits, k_bits, v_bits, o, do_bits, lse, bias, causal: bool, with_bounds: bool = False):
     """fp64 dQ [B,Hq,N,d], dK and dV [B,Hkv,N,d] from bf16 Q, K, V, dO, the forward's O and
     lse [B,Hq,N].  with_bounds: also return the magnitude sums |dS||K|/sqrt(d), |dS|^T|Q|/sqrt(d)
-    and |P|^T|dO| used to bound the rounding of dS and P to bf16."""
+    and |P|^T|dO| that bound the rounding of dS and P to bf16 ("dq", "dk", "dv"), and
+    P (A + E) |K| / sqrt(d), (P (A + E))^T |Q| / sqrt(d) with A_ij = |dO_i| . |v_j| and
+    E_i = |dO_i| . |O_i|, which bound the effect of an error in dP - D relative to the
+    magnitudes it is summed from ("dq2", "dk2")."""
     q, k, v, do = _bf16(q_bits), _bf16(k_bits), _bf16(v_bits), _bf16(do_bits)
     o = np.asarray(o, dtype=np.float64)
     lse = np.asarray(lse, dtype=np.float64)
@@ -44,7 +47,8 @@ def grads(q_bits, k_bits, v_bits, o, do_bits, lse, bias, causal: bool, with_boun
     dq = np.zeros_like(q)
     dk = np.zeros((B, Hkv, N, d))
     dv = np.zeros((B, Hkv, N, d))
-    bnd = {"dq": np.zeros_like(q), "dk": np.zeros((B, Hkv, N, d)), "dv": np.zeros((B, Hkv, N, d))}
+    bnd = {"dq": np.zeros_like(q), "dk": np.zeros((B, Hkv, N, d)), "dv": np.zeros((B, Hkv, N, d)),
+           "dq2": np.zeros_like(q), "dk2": np.zeros((B, Hkv, N, d))}
     mask = np.tril(np.ones((N, N), dtype=bool)) if causal else np.ones((N, N), dtype=bool)
     for b in range(B):
         for h in range(Hq):
@@ -61,6 +65,9 @@ def grads(q_bits, k_bits, v_bits, o, do_bits, lse, bias, causal: bool, with_boun
                 bnd["dq"][b, h] = np.abs(ds) @ np.abs(k[b, g]) * sc
                 bnd["dk"][b, g] += np.abs(ds).T @ np.abs(q[b, h]) * sc
                 bnd["dv"][b, g] += np.abs(p).T @ np.abs(do[b, h])
+                pe = p * (np.abs(do[b, h]) @ np.abs(v[b, g]).T + np.sum(np.abs(do[b, h] * o[b, h]), axis=1)[:, None])
+                bnd["dq2"][b, h] = pe @ np.abs(k[b, g]) * sc
+                bnd["dk2"][b, g] += pe.T @ np.abs(q[b, h]) * sc
     if with_bounds:
         return dq, dk, dv, bnd
     return dq, dk, dv
@@ -84,3 +91,56 @@ def forward_exact(q_bits, k_bits, v_bits, bias, causal: bool):
             lse[b, h] = m[:, 0] + np.log(w.sum(axis=1))
             o[b, h] = (w / w.sum(axis=1, keepdims=True)) @ v[b, h // G]
     return o, lse
+
+
+def grads_sampled(q_bits, k_bits, v_bits, o, do_bits, lse, bias, causal: bool, rows, keys):
+    """The same gradients one by one: dQ of the listed rows (b, h, i) and dK, dV of the
+    listed keys (b, kv head, j), each from its own row or column of the formulas, with
+    the bf16-rounding magnitude sums as in grads().  Returns (dq [R,d], dk [K,d],
+    dv [K,d], bounds dict)."""
+    B, Hq, N, d = np.shape(q_bits)
+    Hkv = np.shape(k_bits)[1]
+    G = Hq // Hkv
+    sc = 1.0 / math.sqrt(d)
+    bvec = np.zeros(N) if bias is None else np.asarray(bias, dtype=np.float64)
+    o = np.asarray(o)
+    lse = np.asarray(lse)
+    out_q, bq, bq2 = [], [], []
+    for b, h, i in rows:
+        g = h // G
+        qi, k, v = _bf16(q_bits[b, h, i]), _bf16(k_bits[b, g]), _bf16(v_bits[b, g])
+        do_i = _bf16(do_bits[b, h, i])
+        n = i + 1 if causal else N
+        s = k[:n] @ qi * sc + bvec[:n]
+        p = np.exp(s - float(lse[b, h, i]))
+        ds = p * (v[:n] @ do_i - float(np.dot(do_i, o[b, h, i].astype(np.float64))))
+        out_q.append(ds @ k[:n] * sc)
+        bq.append(np.abs(ds) @ np.abs(k[:n]) * sc)
+        pe = p * (np.abs(v[:n]) @ np.abs(do_i) + float(np.sum(np.abs(do_i * o[b, h, i].astype(np.float64)))))
+        bq2.append(pe @ np.abs(k[:n]) * sc)
+    out_k, out_v, bk, bv, bk2 = [], [], [], [], []
+    for b, g, j in keys:
+        kj, vj = _bf16(k_bits[b, g, j]), _bf16(v_bits[b, g, j])
+        dk, dv = np.zeros(d), np.zeros(d)
+        ak, av, ak2 = np.zeros(d), np.zeros(d), np.zeros(d)
+        for h in range(g * G, (g + 1) * G):
+            i0 = j if causal else 0
+            qh, doh = _bf16(q_bits[b, h, i0:]), _bf16(do_bits[b, h, i0:])
+            oh = o[b, h, i0:].astype(np.float64)
+            s = qh @ kj * sc + bvec[j]
+            p = np.exp(s - lse[b, h, i0:].astype(np.float64))
+            ds = p * (doh @ vj - np.sum(doh * oh, axis=1))
+            dk += ds @ qh * sc
+            dv += p @ doh
+            ak += np.abs(ds) @ np.abs(qh) * sc
+            av += np.abs(p) @ np.abs(doh)
+            pe = p * (np.abs(doh) @ np.abs(vj) + np.sum(np.abs(doh * oh), axis=1))
+            ak2 += pe @ np.abs(qh) * sc
+        out_k.append(dk)
+        out_v.append(dv)
+        bk.append(ak)
+        bv.append(av)
+        bk2.append(ak2)
+    return (np.array(out_q), np.array(out_k), np.array(out_v),
+            {"dq": np.array(bq), "dk": np.array(bk), "dv": np.array(bv), "dq2": np.array(bq2),
+             "dk2": np.array(bk2)})

@@ -24,7 +24,7 @@ EXPORTS = ("attn_fwd_pcast", "pcast_prepare_v", "attn_fwd_pcast_prepared", "pcas
            "pcast_prepare_qk8", "attn_fwd_pcast_qk8_prepared", "attn_fwd_pcast_qk8",
            "attn_fwd_pcast_rows", "pcast_sink_max_mean", "pcast_delta_critical",
            "pcast_underflow_model", "pcast_lost_mass_model", "attn_decode_pcast",
-           "pcast_decode_workspace_bytes")
+           "pcast_decode_workspace_bytes", "attn_bwd_pcast", "pcast_bwd_workspace_bytes")
 
 _lock = threading.Lock()
 _lib = None
@@ -76,6 +76,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_decode_pcast.restype = I
             lib.pcast_decode_workspace_bytes.argtypes = [I, I, I, I, I]
             lib.pcast_decode_workspace_bytes.restype = ctypes.c_size_t
+            lib.attn_bwd_pcast.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P]
+            lib.attn_bwd_pcast.restype = I
+            lib.pcast_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
+            lib.pcast_bwd_workspace_bytes.restype = ctypes.c_size_t
             D = ctypes.c_double
             lib.pcast_sink_max_mean.argtypes = [I]
             lib.pcast_sink_max_mean.restype = D
@@ -149,6 +153,16 @@ def attn_decode_pcast(Q, K, vop, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_ke
 
 def decode_workspace_bytes(B: int, Hkv: int, Nk: int, d: int, split_keys: int) -> int:
     return int(load_library().pcast_decode_workspace_bytes(B, Hkv, Nk, d, split_keys))
+
+
+def attn_bwd_pcast(Q, K, V, O, dO, lse, bias, B, Hq, Hkv, N, d, causal, dQ, dK, dV, workspace, stream) -> int:
+    """Raw attn_bwd_pcast with integer device addresses (0 for NULL); returns the C return code."""
+    return int(load_library().attn_bwd_pcast(Q, K, V, O, dO, lse, bias or None, B, Hq, Hkv, N, d, int(causal),
+                                             dQ, dK, dV, workspace, stream or None))
+
+
+def bwd_workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
+    return int(load_library().pcast_bwd_workspace_bytes(B, Hq, Hkv, N, d))
 
 
 def sink_max_mean(k: int = 4) -> float:

@@ -232,6 +232,18 @@ struct Params {
   float* part_a;          // [..][32][D] un-normalised accumulator
   float* part_ml;         // [..][32][2] running max (log2 units) and row sum
   unsigned int* part_cnt; // [..][32][2] non-sink pairs, zero codes
+  // backward: raw V (bf16), dO (bf16), the forward's lse (natural units) and the row
+  // dots D = dO . O; slot-order transposes of K, Q and dO; gradients (fp32)
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse_in;
+  const float* dvec;
+  const uint8_t* kt;
+  const uint8_t* qt;
+  const uint8_t* dot;
+  float* dq;
+  float* dk;
+  float* dv;
 };
 
 // How P becomes an MFMA operand.
@@ -1427,6 +1439,430 @@ __global__ __launch_bounds__(256) void pcast_decode_merge(const Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// Backward by recomputation from the forward's log-sum-exp, the cast passed
+// straight through: P = exp(s - lse), dP = dO V^T, dS = P (dP - D) with
+// D = dO . O, dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d), dV = P^T dO.  All
+// products on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are
+// rounded to bf16 for the products that take them as operands.
+// ---------------------------------------------------------------------------
+
+// D_i = dO_i . O_i, eight lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void pcast_bwd_rowdot(const uint16_t* __restrict__ dout, const float* __restrict__ o,
+                                                        float* __restrict__ dvec, int64_t rows) {
+  constexpr int kPer = D / 8;  // elements per lane
+  const int64_t row = (int64_t)blockIdx.x * 32 + threadIdx.x / 8;
+  const int part = threadIdx.x % 8;
+  float acc = 0.0f;
+  if (row < rows) {
+    const uint16_t* a = dout + row * D + part * kPer;
+    const float* b = o + row * D + part * kPer;
+#pragma unroll
+    for (int i = 0; i < kPer; i += 8) {
+      const i32x4_t w = *reinterpret_cast<const i32x4_t*>(a + i);
+      const float4 x = *reinterpret_cast<const float4*>(b + i);
+      const float4 y = *reinterpret_cast<const float4*>(b + i + 4);
+      acc = fmaf(__builtin_bit_cast(float, (uint32_t)w[0] << 16), x.x, acc);
+      acc = fmaf(__builtin_bit_cast(float, (uint32_t)w[0] & 0xFFFF0000u), x.y, acc);
+      acc = fmaf(__builtin_bit_cast(float, (uint32_t)w[1] << 16), x.z, acc);
+      acc = fmaf(__builtin_bit_cast(float, (uint32_t)w[1] & 0xFFFF0000u), x.w, acc);
+      acc = fmaf(__builtin_bit_cast(float, (uint32_t)w[2] << 16), y.x, acc);
+      acc = fmaf(__builtin_bit_cast(float, (uint32_t)w[2] & 0xFFFF0000u), y.y, acc);
+      acc = fmaf(__builtin_bit_cast(float, (uint32_t)w[3] << 16), y.z, acc);
+      acc = fmaf(__builtin_bit_cast(float, (uint32_t)w[3] & 0xFFFF0000u), y.w, acc);
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (row < rows && part == 0) dvec[row] = acc;
+}
+
+// dQ: a workgroup of 4 waves takes 128 query rows of one (b, h), a lane one row,
+// and walks the key blocks: S^T = K Q^T and dP^T = V dO^T (keys x rows, the
+// forward's layout), dS in registers, dQ^T += K^T dS^T with K^T from its
+// slot-order copy.
+template <int D, bool kCausal>
+__global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dq(const Params p) {
+  using G = Geometry<D>;
+  constexpr int kKRow = D * 2;
+  constexpr int kTRow = kKvBlock * 2;
+  constexpr int kKTile = kKvBlock * kKRow;
+  constexpr int kTTile = D * kTRow;
+  using SK = Swizzle<kKRow>;
+  using ST = Swizzle<kTRow>;
+  constexpr int kKLoads = kKTile / (1024 * kWaves);
+  constexpr int kTLoads = kTTile / (1024 * kWaves);
+  static_assert(kKTile % (1024 * kWaves) == 0 && kTTile % (1024 * kWaves) == 0, "staging split");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[kKTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[kKTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[kKTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[kKTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_t0[kTTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_t1[kTTile];
+  __shared__ __attribute__((aligned(16))) float lds_b0[kKvBlock];
+  __shared__ __attribute__((aligned(16))) float lds_b1[kKvBlock];
+  auto kbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_k1 : lds_k0; };
+  auto vbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_v1 : lds_v0; };
+  auto tbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_t1 : lds_t0; };
+  auto bbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_b1 : lds_b0; };
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64;
+  const int g = lane / 32, li = lane % 32;
+  const int n_rb = (p.N + kBlockRows - 1) / kBlockRows;
+  int b, h, rb;
+  decode_block(blockIdx.x, n_rb * p.Hq * p.B, n_rb, p.Hq, kCausal, b, h, rb);
+  const int hk = h / (p.Hq / p.Hkv);
+  const int n_tiles = p.N / kKvBlock;
+  const int row0 = rb * kBlockRows;
+  const int wrow0 = row0 + wave * kRowsPerWave;
+  const int myrow = wrow0 + li;
+  const bool wave_active = wrow0 < p.N;
+  const int t_last = kCausal ? min((row0 + kBlockRows - 1) / kKvBlock, n_tiles - 1) : n_tiles - 1;
+  const int n_it = t_last + 1;
+  const float c = p.logit_scale;
+  const int64_t row = ((int64_t)b * p.Hq + h) * p.N + myrow;
+
+  bf16x8_t qf[G::kQSteps], df[G::kQSteps];
+  float lse2 = 0.0f, drow = 0.0f;
+  if (wave_active) {
+    const uint16_t* qrow = p.q + row * D + g * 8;
+    const uint16_t* drw = p.dout + row * D + g * 8;
+#pragma unroll
+    for (int s = 0; s < G::kQSteps; ++s) {
+      qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + s * 16);
+      df[s] = *reinterpret_cast<const bf16x8_t*>(drw + s * 16);
+    }
+    lse2 = p.lse_in[row] * kLog2e;
+    drow = p.dvec[row];
+  }
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k + ((int64_t)b * p.Hkv + hk) * p.N * D);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v + ((int64_t)b * p.Hkv + hk) * p.N * D);
+  const uint8_t* tbase = p.kt + ((int64_t)b * p.Hkv + hk) * (int64_t)n_tiles * kTTile;
+  int ksrc[kKLoads], tsrc[kTLoads];
+#pragma unroll
+  for (int i = 0; i < kKLoads; ++i) {
+    const int pos = (wave * kKLoads + i) * 64 + lane, r = pos / SK::kChunks;
+    ksrc[i] = r * kKRow + (((pos % SK::kChunks) ^ SK::key(r)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < kTLoads; ++i) {
+    const int pos = (wave * kTLoads + i) * 64 + lane, r = pos / ST::kChunks;
+    tsrc[i] = r * kTRow + (((pos % ST::kChunks) ^ ST::key(r)) << 4);
+  }
+  const bool with_bias = p.bias != nullptr;
+  auto visible = [&](int t) __attribute__((always_inline)) {
+    return wave_active && (!kCausal || t * kKvBlock <= wrow0 + kRowsPerWave - 1);
+  };
+  auto load = [&](int t, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kKLoads; ++i) {
+      load_to_lds16(kbase + (int64_t)t * kKTile + ksrc[i], kbuf(buf) + (wave * kKLoads + i) * 1024);
+      load_to_lds16(vbase + (int64_t)t * kKTile + ksrc[i], vbuf(buf) + (wave * kKLoads + i) * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < kTLoads; ++i)
+      load_to_lds16(tbase + (int64_t)t * kTTile + tsrc[i], tbuf(buf) + (wave * kTLoads + i) * 1024);
+    if (with_bias && wave == 0) load_to_lds4(p.bias + t * kKvBlock + lane, bbuf(buf));
+  };
+  auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  f32x16_t dqacc[G::kDTiles];
+#pragma unroll
+  for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[dt][r] = 0.0f;
+  const int xk = SK::key(li);
+
+  auto step = [&](int it, auto cur_c) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
+    if (it + 1 < n_it) load(it + 1, nxt);
+    if (visible(it)) {
+      // S^T = K Q^T and dP^T = V dO^T, two 32-key halves each
+      f32x16_t sacc[2], pacc[2];
+      const uint8_t* kl = kbuf(cur) + li * kKRow;
+      const uint8_t* vl = vbuf(cur) + li * kKRow;
+#pragma unroll
+      for (int s = 0; s < G::kQSteps; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int off = kb * 32 * kKRow + (((2 * s + g) ^ xk) << 4);
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + off);
+          const bf16x8_t e = *reinterpret_cast<const bf16x8_t*>(vl + off);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16_t{} : sacc[kb], 0, 0, 0);
+          pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e, df[s], s == 0 ? f32x16_t{} : pacc[kb], 0, 0, 0);
+        }
+      const int key0 = it * kKvBlock;
+      const bool diag = kCausal && (key0 + kKvBlock - 1 > wrow0);
+      const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bbuf(cur)[lane] != 0.0f) != 0;
+      float bk[32];
+      if (has_bias) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(bbuf(cur) + slot_key(g, 4 * q));
+          bk[4 * q] = v.x; bk[4 * q + 1] = v.y; bk[4 * q + 2] = v.z; bk[4 * q + 3] = v.w;
+        }
+      }
+      uint32_t pw[16];
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        float ds2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int j = 2 * w + e;
+          const float x = has_bias ? fmaf(sacc[j / 16][j % 16], c, bk[j] * kLog2e) : sacc[j / 16][j % 16] * c;
+          float pj = __builtin_amdgcn_exp2f(x - lse2);
+          if (diag && key0 + slot_key(g, j) > myrow) pj = 0.0f;
+          ds2[e] = pj * (pacc[j / 16][j % 16] - drow);
+        }
+        pw[w] = cast2_bf16(ds2[0], ds2[1]);
+      }
+      // dQ^T += K^T dS^T: four k-steps of 16 keys per 32-column tile
+      const uint8_t* tl = tbuf(cur) + li * kTRow;
+      const int xt = ST::key(li);
+#pragma unroll
+      for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(tl + dt * 32 * kTRow + (((4 * g + s) ^ xt) << 4));
+          const i32x4_t bw = {(int)pw[4 * s], (int)pw[4 * s + 1], (int)pw[4 * s + 2], (int)pw[4 * s + 3]};
+          dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bw), dqacc[dt], 0, 0, 0);
+        }
+    }
+    wait_loads();
+    __syncthreads();
+  };
+
+  load(0, 0);
+  wait_loads();
+  __syncthreads();
+  for (int it = 0; it < n_it; it += 2) {
+    step(it, BufIndex<0>{});
+    if (it + 1 < n_it) step(it + 1, BufIndex<1>{});
+  }
+  if (wave_active) {
+    const float sc = p.logit_scale / kLog2e;  // 1 / sqrt(d)
+    float* orow = p.dq + row * D;
+#pragma unroll
+    for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float4 v;
+        v.x = dqacc[dt][r4 * 4 + 0] * sc;
+        v.y = dqacc[dt][r4 * 4 + 1] * sc;
+        v.z = dqacc[dt][r4 * 4 + 2] * sc;
+        v.w = dqacc[dt][r4 * 4 + 3] * sc;
+        *reinterpret_cast<float4*>(orow + dt * 32 + r4 * 8 + g * 4) = v;
+      }
+  }
+}
+
+// dK and dV: a workgroup of 4 waves takes 128 keys of one (b, kv head), a lane
+// one key, and walks the 64-row query blocks of every query head that reads the
+// kv head: S = Q K^T and dP = dO V^T (rows x keys: a lane holds its key's column),
+// P and dS in registers, dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T from
+// their slot-order copies.
+template <int D, bool kCausal>
+__global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p) {
+  using G = Geometry<D>;
+  constexpr int kRow = D * 2;
+  constexpr int kTRow = kKvBlock * 2;
+  constexpr int kTile = kKvBlock * kRow;
+  constexpr int kTTile = D * kTRow;
+  using SR = Swizzle<kRow>;
+  using ST = Swizzle<kTRow>;
+  constexpr int kLoads = kTile / (1024 * kWaves);
+  constexpr int kTLoads = kTTile / (1024 * kWaves);
+  static_assert(kTile % (1024 * kWaves) == 0 && kTTile % (1024 * kWaves) == 0, "staging split");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_q0[kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_q1[kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_o0[kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_o1[kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_qt0[kTTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_qt1[kTTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_ot0[kTTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_ot1[kTTile];
+  __shared__ __attribute__((aligned(16))) float lds_l0[kKvBlock];
+  __shared__ __attribute__((aligned(16))) float lds_l1[kKvBlock];
+  __shared__ __attribute__((aligned(16))) float lds_d0[kKvBlock];
+  __shared__ __attribute__((aligned(16))) float lds_d1[kKvBlock];
+  auto qbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_q1 : lds_q0; };
+  auto obuf = [&](int i) __attribute__((always_inline)) { return i ? lds_o1 : lds_o0; };
+  auto qtbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_qt1 : lds_qt0; };
+  auto otbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_ot1 : lds_ot0; };
+  auto lbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_l1 : lds_l0; };
+  auto dbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_d1 : lds_d0; };
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64;
+  const int g = lane / 32, li = lane % 32;
+  const int n_kb = (p.N + kBlockRows - 1) / kBlockRows;
+  const int kb = blockIdx.x % n_kb;  // causal: the lowest keys (the most rows) first
+  const int bhk = blockIdx.x / n_kb;
+  const int hk = bhk % p.Hkv, b = bhk / p.Hkv;
+  const int Gq = p.Hq / p.Hkv;
+  const int key0 = kb * kBlockRows;
+  const int wkey0 = key0 + wave * kRowsPerWave;
+  const int mykey = wkey0 + li;
+  const bool wave_active = wkey0 < p.N;
+  const int n_rblk = p.N / kKvBlock;
+  const int r_first = kCausal ? key0 / kKvBlock : 0;
+  const int n_r = n_rblk - r_first;
+  const int n_it = Gq * n_r;
+  const float c = p.logit_scale;
+  const int64_t krow = ((int64_t)b * p.Hkv + hk) * p.N + mykey;
+
+  bf16x8_t kf[G::kQSteps], vf[G::kQSteps];
+  float bkl = 0.0f;
+  if (wave_active) {
+    const uint16_t* kr = p.k + krow * D + g * 8;
+    const uint16_t* vr = p.v + krow * D + g * 8;
+#pragma unroll
+    for (int s = 0; s < G::kQSteps; ++s) {
+      kf[s] = *reinterpret_cast<const bf16x8_t*>(kr + s * 16);
+      vf[s] = *reinterpret_cast<const bf16x8_t*>(vr + s * 16);
+    }
+    if (p.bias) bkl = p.bias[mykey] * kLog2e;
+  }
+  int rsrc[kLoads], tsrc[kTLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int pos = (wave * kLoads + i) * 64 + lane, r = pos / SR::kChunks;
+    rsrc[i] = r * kRow + (((pos % SR::kChunks) ^ SR::key(r)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < kTLoads; ++i) {
+    const int pos = (wave * kTLoads + i) * 64 + lane, r = pos / ST::kChunks;
+    tsrc[i] = r * kTRow + (((pos % ST::kChunks) ^ ST::key(r)) << 4);
+  }
+  // iteration it: query head hk * Gq + it / n_r, row block r_first + it % n_r
+  auto head_of = [&](int it) __attribute__((always_inline)) { return hk * Gq + it / n_r; };
+  auto rblk_of = [&](int it) __attribute__((always_inline)) { return r_first + it % n_r; };
+  auto load = [&](int it, int buf) __attribute__((always_inline)) {
+    const int64_t hrow = ((int64_t)b * p.Hq + head_of(it)) * p.N;  // first row of the head
+    const int r = rblk_of(it);
+    const uint8_t* qs = reinterpret_cast<const uint8_t*>(p.q + (hrow + (int64_t)r * kKvBlock) * D);
+    const uint8_t* os = reinterpret_cast<const uint8_t*>(p.dout + (hrow + (int64_t)r * kKvBlock) * D);
+    const int64_t tblk = hrow / kKvBlock + r;  // flat 64-row block of Q^T / dO^T
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      load_to_lds16(qs + rsrc[i], qbuf(buf) + (wave * kLoads + i) * 1024);
+      load_to_lds16(os + rsrc[i], obuf(buf) + (wave * kLoads + i) * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < kTLoads; ++i) {
+      load_to_lds16(p.qt + tblk * kTTile + tsrc[i], qtbuf(buf) + (wave * kTLoads + i) * 1024);
+      load_to_lds16(p.dot + tblk * kTTile + tsrc[i], otbuf(buf) + (wave * kTLoads + i) * 1024);
+    }
+    if (wave == 0) {
+      load_to_lds4(p.lse_in + hrow + r * kKvBlock + lane, lbuf(buf));
+      load_to_lds4(p.dvec + hrow + r * kKvBlock + lane, dbuf(buf));
+    }
+  };
+  auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  f32x16_t dkacc[G::kDTiles], dvacc[G::kDTiles];
+#pragma unroll
+  for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dkacc[dt][r] = 0.0f;
+      dvacc[dt][r] = 0.0f;
+    }
+  const int xr = SR::key(li);
+
+  auto step = [&](int it, auto cur_c) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
+    if (it + 1 < n_it) load(it + 1, nxt);
+    const int rrow0 = rblk_of(it) * kKvBlock;
+    if (wave_active && (!kCausal || rrow0 + kKvBlock - 1 >= wkey0)) {
+      // S = Q K^T and dP = dO V^T, two 32-row halves each (rows in slots, keys in lanes)
+      f32x16_t sacc[2], pacc[2];
+      const uint8_t* ql = qbuf(cur) + li * kRow;
+      const uint8_t* ol = obuf(cur) + li * kRow;
+#pragma unroll
+      for (int s = 0; s < G::kQSteps; ++s)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int off = hh * 32 * kRow + (((2 * s + g) ^ xr) << 4);
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ql + off);
+          const bf16x8_t e = *reinterpret_cast<const bf16x8_t*>(ol + off);
+          sacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[s], s == 0 ? f32x16_t{} : sacc[hh], 0, 0, 0);
+          pacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e, vf[s], s == 0 ? f32x16_t{} : pacc[hh], 0, 0, 0);
+        }
+      const bool diag = kCausal && (rrow0 < wkey0 + kRowsPerWave - 1);
+      float lq[32], dq4[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 a = *reinterpret_cast<const float4*>(lbuf(cur) + slot_key(g, 4 * q));
+        const float4 e = *reinterpret_cast<const float4*>(dbuf(cur) + slot_key(g, 4 * q));
+        lq[4 * q] = a.x; lq[4 * q + 1] = a.y; lq[4 * q + 2] = a.z; lq[4 * q + 3] = a.w;
+        dq4[4 * q] = e.x; dq4[4 * q + 1] = e.y; dq4[4 * q + 2] = e.z; dq4[4 * q + 3] = e.w;
+      }
+      uint32_t pp[16], ps[16];
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        float p2[2], d2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int j = 2 * w + e;
+          float pj = __builtin_amdgcn_exp2f(fmaf(sacc[j / 16][j % 16], c, bkl) - lq[j] * kLog2e);
+          if (diag && rrow0 + slot_key(g, j) < mykey) pj = 0.0f;
+          p2[e] = pj;
+          d2[e] = pj * (pacc[j / 16][j % 16] - dq4[j]);
+        }
+        pp[w] = cast2_bf16(p2[0], p2[1]);
+        ps[w] = cast2_bf16(d2[0], d2[1]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS: four k-steps of 16 rows per 32-column tile
+      const uint8_t* otl = otbuf(cur) + li * kTRow;
+      const uint8_t* qtl = qtbuf(cur) + li * kTRow;
+      const int xt = ST::key(li);
+#pragma unroll
+      for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int off = dt * 32 * kTRow + (((4 * g + s) ^ xt) << 4);
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(otl + off);
+          const bf16x8_t e = *reinterpret_cast<const bf16x8_t*>(qtl + off);
+          const i32x4_t bp = {(int)pp[4 * s], (int)pp[4 * s + 1], (int)pp[4 * s + 2], (int)pp[4 * s + 3]};
+          const i32x4_t bs = {(int)ps[4 * s], (int)ps[4 * s + 1], (int)ps[4 * s + 2], (int)ps[4 * s + 3]};
+          dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bp), dvacc[dt], 0, 0, 0);
+          dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e, __builtin_bit_cast(bf16x8_t, bs), dkacc[dt], 0, 0, 0);
+        }
+    }
+    wait_loads();
+    __syncthreads();
+  };
+
+  load(0, 0);
+  wait_loads();
+  __syncthreads();
+  for (int it = 0; it < n_it; it += 2) {
+    step(it, BufIndex<0>{});
+    if (it + 1 < n_it) step(it + 1, BufIndex<1>{});
+  }
+  if (wave_active) {
+    const float sc = p.logit_scale / kLog2e;  // 1 / sqrt(d)
+    float* krw = p.dk + krow * D;
+    float* vrw = p.dv + krow * D;
+#pragma unroll
+    for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float4 a, e;
+        a.x = dkacc[dt][r4 * 4 + 0] * sc; a.y = dkacc[dt][r4 * 4 + 1] * sc;
+        a.z = dkacc[dt][r4 * 4 + 2] * sc; a.w = dkacc[dt][r4 * 4 + 3] * sc;
+        e.x = dvacc[dt][r4 * 4 + 0]; e.y = dvacc[dt][r4 * 4 + 1];
+        e.z = dvacc[dt][r4 * 4 + 2]; e.w = dvacc[dt][r4 * 4 + 3];
+        *reinterpret_cast<float4*>(krw + dt * 32 + r4 * 8 + g * 4) = a;
+        *reinterpret_cast<float4*>(vrw + dt * 32 + r4 * 8 + g * 4) = e;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 thread_local char g_last_error[512] = "";
@@ -1516,6 +1952,22 @@ void launch_attn(const Params& p, int mode, int causal, hipStream_t stream) {
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
+// Workspace of the backward: slot-order transposes of K, Q and dO (bf16, the
+// layout pcast_prep_v writes for V), then the row dots D (fp32); 256-aligned parts.
+struct BwdLayout {
+  size_t kt, qt, dot, dvec, total;
+};
+BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int d) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  BwdLayout l;
+  l.kt = 0;
+  l.qt = up((size_t)B * Hkv * N * d * 2);
+  l.dot = up(l.qt + (size_t)B * Hq * N * d * 2);
+  l.dvec = up(l.dot + (size_t)B * Hq * N * d * 2);
+  l.total = up(l.dvec + (size_t)B * Hq * N * 4);
+  return l;
+}
+
 // Workspace of the split-KV decode: per (b, kv head, range, packed row) the partial
 // accumulator [D] fp32, then (m, l) fp32, then the two counters u32; 256-aligned parts.
 struct DecodeLayout {
@@ -1562,6 +2014,11 @@ size_t pcast_stats_words(int B, int Hq, int N) {
 size_t pcast_workspace_bytes(int B, int Hkv, int N, int d, float S) {
   if (B <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return 0;
   return (size_t)B * Hkv * N * d * ((S == 0.0f) ? 2 : 1);
+}
+
+size_t pcast_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return 0;
+  return bwd_layout(B, Hq, Hkv, N, d).total;
 }
 
 size_t pcast_decode_workspace_bytes(int B, int Hkv, int Nk, int d, int split_keys) {
@@ -1770,6 +2227,82 @@ int attn_fwd_pcast_rows(const void* Q, const void* K, const void* workspace, con
   if ((rc = check_device()) != PCAST_OK) return rc;
   return enqueue_attn(Q, K, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
                       static_cast<hipStream_t>(stream), false, lse, lost);
+}
+
+int attn_bwd_pcast(const void* Q, const void* K, const void* V, const float* O, const void* dO,
+                   const float* lse, const float* bias, int B, int Hq, int Hkv, int N, int d, int causal,
+                   float* dQ, float* dK, float* dV, void* workspace, void* stream) {
+  g_last_error[0] = '\0';
+  if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !workspace)
+    return fail(PCAST_EINVAL, "Q, K, V, O, dO, lse, dQ, dK, dV and workspace must be non-null");
+  const void* a16[] = {Q, K, V, O, dO, dQ, dK, dV, workspace};
+  for (const void* ptr : a16)
+    if (!aligned(ptr, 16)) return fail(PCAST_EINVAL, "tensors and workspace must be 16-byte aligned");
+  if (!aligned(lse, 4) || (bias && !aligned(bias, 4))) return fail(PCAST_EINVAL, "lse and bias must be 4-byte aligned");
+  if (causal != 0 && causal != 1) return fail(PCAST_EINVAL, "causal must be 0 or 1");
+  int rc = check_shape(B, Hq, Hkv, N, d, 1.0f);
+  if (rc != PCAST_OK) return rc;
+  if ((int64_t)B * Hkv * ((N + kBlockRows - 1) / kBlockRows) > (int64_t)INT32_MAX) return fail(PCAST_ENOTSUP, "grid too large");
+  if ((rc = check_device()) != PCAST_OK) return rc;
+
+  const BwdLayout l = bwd_layout(B, Hq, Hkv, N, d);
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t rows = (int64_t)B * Hq * N;
+  const int64_t qblk = (int64_t)B * Hq * (N / kKvBlock), kblk = (int64_t)B * Hkv * (N / kKvBlock);
+  const uint16_t* Qb = static_cast<const uint16_t*>(Q);
+  const uint16_t* Kb = static_cast<const uint16_t*>(K);
+  const uint16_t* dOb = static_cast<const uint16_t*>(dO);
+  if (d == 64) {
+    launch_prep<64, false>(Kb, base + l.kt, kblk, st);
+    launch_prep<64, false>(Qb, base + l.qt, qblk, st);
+    launch_prep<64, false>(dOb, base + l.dot, qblk, st);
+    hipLaunchKernelGGL(pcast_bwd_rowdot<64>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, st, dOb, O,
+                       reinterpret_cast<float*>(base + l.dvec), rows);
+  } else {
+    launch_prep<128, false>(Kb, base + l.kt, kblk, st);
+    launch_prep<128, false>(Qb, base + l.qt, qblk, st);
+    launch_prep<128, false>(dOb, base + l.dot, qblk, st);
+    hipLaunchKernelGGL(pcast_bwd_rowdot<128>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, st, dOb, O,
+                       reinterpret_cast<float*>(base + l.dvec), rows);
+  }
+  Params p{};
+  p.q = Qb;
+  p.k = Kb;
+  p.v = static_cast<const uint16_t*>(V);
+  p.dout = dOb;
+  p.lse_in = lse;
+  p.dvec = reinterpret_cast<const float*>(base + l.dvec);
+  p.kt = base + l.kt;
+  p.qt = base + l.qt;
+  p.dot = base + l.dot;
+  p.bias = bias;
+  p.dq = dQ;
+  p.dk = dK;
+  p.dv = dV;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N;
+  p.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)d));
+  const int n_rb = (N + kBlockRows - 1) / kBlockRows;
+  const dim3 gq((unsigned)(n_rb * Hq * B)), gk((unsigned)(n_rb * Hkv * B));
+  if (d == 64) {
+    if (causal) {
+      hipLaunchKernelGGL((pcast_attn_bwd_dq<64, true>), gq, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((pcast_attn_bwd_dkv<64, true>), gk, dim3(kThreads), 0, st, p);
+    } else {
+      hipLaunchKernelGGL((pcast_attn_bwd_dq<64, false>), gq, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((pcast_attn_bwd_dkv<64, false>), gk, dim3(kThreads), 0, st, p);
+    }
+  } else {
+    if (causal) {
+      hipLaunchKernelGGL((pcast_attn_bwd_dq<128, true>), gq, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((pcast_attn_bwd_dkv<128, true>), gk, dim3(kThreads), 0, st, p);
+    } else {
+      hipLaunchKernelGGL((pcast_attn_bwd_dq<128, false>), gq, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((pcast_attn_bwd_dkv<128, false>), gk, dim3(kThreads), 0, st, p);
+    }
+  }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PCAST_OK : hip_fail(e, "backward launch");
 }
 
 int attn_decode_pcast(const void* Q, const void* K, const void* vop, const float* bias, int B, int Hq,

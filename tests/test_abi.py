@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_sizes(lib):
-    assert lib.pcast_abi_version() == 4
+    assert lib.pcast_abi_version() == 5
     assert sna.stats_words(4, 32, 8192) == 4 * 32 * 128 * 2
     assert sna.stats_words(1, 1, 100) == 4
     assert sna.workspace_bytes(4, 32, 8192, 128, 256.0) == 4 * 32 * 8192 * 128
@@ -186,6 +186,30 @@ def test_decode_argument_errors(lib, kw, code):
              split_keys=256, out=FAKE, stats=0, workspace=FAKE, stream=0)
     a.update(kw)
     assert sna.attn_decode_pcast(**a) == code
+
+
+def test_bwd_workspace_layout(lib):
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for B, Hq, Hkv, N, d in ((4, 32, 32, 8192, 128), (1, 3, 1, 64, 64)):
+        want = up(up(up(up(2 * B * Hkv * N * d) + 2 * B * Hq * N * d) + 2 * B * Hq * N * d) + 4 * B * Hq * N)
+        assert sna.bwd_workspace_bytes(B, Hq, Hkv, N, d) == want
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(O=0), sna.PCAST_EINVAL),
+    (dict(dO=FAKE + 2), sna.PCAST_EINVAL),
+    (dict(lse=FAKE + 1), sna.PCAST_EINVAL),
+    (dict(dV=0), sna.PCAST_EINVAL),
+    (dict(causal=5), sna.PCAST_EINVAL),
+    (dict(Hq=3, Hkv=2), sna.PCAST_EINVAL),
+    (dict(N=96), sna.PCAST_ENOTSUP),
+    (dict(d=96), sna.PCAST_ENOTSUP),
+])
+def test_bwd_argument_errors(lib, kw, code):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, lse=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128,
+             causal=1, dQ=FAKE, dK=FAKE, dV=FAKE, workspace=FAKE, stream=0)
+    a.update(kw)
+    assert sna.attn_bwd_pcast(**a) == code
 
 
 def test_strerror_texts(lib):

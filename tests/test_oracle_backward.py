@@ -97,3 +97,24 @@ def test_planted_missing_d_is_caught():
     dq0, _, _ = backward.grads(qb, kb, vb, np.zeros_like(o), dob, lse, None, False)
     aq, _, _ = _autograd(qb, kb, vb, dob, None, False)
     assert np.max(np.abs(dq0 - aq)) > 1e-3
+
+
+def test_sampled_equals_full():
+    qb, kb, vb = synthetic.qkv_bf16(1, 4, 2, 128, 32, 105)
+    dob = synthetic.gaussian_bf16(105, 3, qb.shape)
+    bias = synthetic.sink_bias(128, 4.0)
+    o, lse = backward.forward_exact(qb, kb, vb, bias, True)
+    dq, dk, dv, bnd = backward.grads(qb, kb, vb, o, dob, lse, bias, True, with_bounds=True)
+    rows = [(0, 0, 0), (0, 3, 127), (0, 2, 64)]
+    keys = [(0, 0, 0), (0, 1, 127), (0, 1, 5)]
+    sq, sk, sv, sb = backward.grads_sampled(qb, kb, vb, o, dob, lse, bias, True, rows, keys)
+    for n, (b, h, i) in enumerate(rows):
+        assert np.allclose(sq[n], dq[b, h, i], rtol=1e-10, atol=1e-12)
+        assert np.allclose(sb["dq"][n], bnd["dq"][b, h, i], rtol=1e-10, atol=1e-12)
+        assert np.allclose(sb["dq2"][n], bnd["dq2"][b, h, i], rtol=1e-10, atol=1e-12)
+    for n, (b, g, j) in enumerate(keys):
+        assert np.allclose(sk[n], dk[b, g, j], rtol=1e-10, atol=1e-12)
+        assert np.allclose(sv[n], dv[b, g, j], rtol=1e-10, atol=1e-12)
+        assert np.allclose(sb["dk"][n], bnd["dk"][b, g, j], rtol=1e-10, atol=1e-12)
+        assert np.allclose(sb["dk2"][n], bnd["dk2"][b, g, j], rtol=1e-10, atol=1e-12)
+        assert np.allclose(sb["dv"][n], bnd["dv"][b, g, j], rtol=1e-10, atol=1e-12)
