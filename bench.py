@@ -17,7 +17,9 @@ forward.  The "qk_fp8" object times the variant with FP8 logits
 MSE against the same fp64 attention of the unquantised Q and K.  The "decode"
 object times attn_decode_pcast (split KV) on the decode workload (16 sequences of
 16384 cached keys, one new token each, GQA 32/8) against the HBM roofline; its V
-copy is prepared once, outside the timed calls, as a cache would be.
+copy is prepared once, outside the timed calls, as a cache would be.  The
+"backward" object times attn_bwd_pcast on the same workload (its pre-passes
+included), with the forward's O and lse as inputs.
 """
 from __future__ import annotations
 
@@ -110,6 +112,53 @@ def cpu_baseline(w, qb, kb, vb, bias, out_rev, out_fwd1, target_s: float, seed: 
     return base, mse
 
 
+def bench_backward(sna, torch, np, synthetic, w, q, k, v, ws, bias_t, dev, stream, steps, warmup):
+    sh = stream.cuda_stream
+    S, order = 256.0, 1
+    B, Hq, Hkv, N, d = w.B, w.Hq, w.Hkv, w.N, w.d
+    o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    rc = sna.prepare_v(v.data_ptr(), B, Hkv, N, d, S, ws.data_ptr(), sh)
+    rc = rc or sna.attn_fwd_pcast_rows(q.data_ptr(), k.data_ptr(), ws.data_ptr(), bias_t.data_ptr(), B, Hq, Hkv, N,
+                                       d, int(w.causal), S, order, o.data_ptr(), 0, lse.data_ptr(), 0, sh)
+    if rc != sna.PCAST_OK:
+        raise sna.PcastError(rc, sna.strerror(rc))
+    dob = synthetic.gaussian_bf16(w.seed, 3, (B, Hq, N, d))
+    do = torch.from_numpy(dob.view(np.int16)).view(torch.bfloat16).to(dev)
+    dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    wb = torch.empty(sna.bwd_workspace_bytes(B, Hq, Hkv, N, d), dtype=torch.uint8, device=dev)
+
+    def call():
+        r = sna.attn_bwd_pcast(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                               bias_t.data_ptr(), B, Hq, Hkv, N, d, int(w.causal), dq.data_ptr(), dk.data_ptr(),
+                               dv.data_ptr(), wb.data_ptr(), sh)
+        if r != sna.PCAST_OK:
+            raise sna.PcastError(r, sna.strerror(r))
+
+    for _ in range(warmup):
+        call()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    flops = 2.5 * w.flops   # five products of the forward's two (FlashAttention convention)
+    tf = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] backward: {ms:.4f} ms per call ({tf:.0f} TFLOP/s)", file=sys.stderr, flush=True)
+    return {"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal, sink bias 7 on keys 0..3, "
+                        f"gradients of the S={S:g} {'reverse' if order else 'forward'} forward",
+            "ms_per_call": round(ms, 5), "steps": steps,
+            "kernels": "3 x pcast_prep_v (bf16 transposes) + pcast_bwd_rowdot + pcast_attn_bwd_dq + pcast_attn_bwd_dkv",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16, 4), "algorithmic_flops": flops,
+                         "flops_rule": "2.5 x the forward's 2*B*H*N^2*d (causal)"}}
+
+
 def bench_decode(sna, torch, np, synthetic, dev, stream, steps, warmup):
     w = synthetic.DECODE_WORKLOADS["decode"]
     delta, S, order = w.cases[0]
@@ -166,6 +215,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-qk8", action="store_true", help="skip the FP8-logit variant")
     ap.add_argument("--no-decode", action="store_true", help="skip the split-KV decode measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes, 3 times (scale for "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
@@ -310,6 +360,9 @@ def main() -> int:
                             "traffic": measured_traffic(w.name, TRAFFIC_FILE_QK8)}
         out_qk8 = out.cpu().numpy()
 
+    if not args.no_backward:
+        result["backward"] = bench_backward(sna, torch, np, synthetic, w, q, k, v, ws, bias_t, dev, stream,
+                                            min(args.steps, 10), min(args.warmup, 2))
     if not args.no_decode:
         result["decode"] = bench_decode(sna, torch, np, synthetic, dev, stream, args.steps, args.warmup)
 
