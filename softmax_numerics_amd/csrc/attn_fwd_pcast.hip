@@ -1175,13 +1175,13 @@ __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
   using SV = Swizzle<kVRow>;
   constexpr int kKLoads = kKTile / 1024;  // 1 KB direct loads per block (one wave)
   constexpr int kVLoads = kVTile / 1024;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[kKTile];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[kKTile];
+  // one K buffer, reloaded once the block's logits have read it; V and bias double
+  // buffered (32.5 KiB: four workgroups per CU)
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kKTile];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v0[kVTile];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v1[kVTile];
   __shared__ __attribute__((aligned(16))) float lds_b0[kKvBlock];
   __shared__ __attribute__((aligned(16))) float lds_b1[kKvBlock];
-  auto kbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_k1 : lds_k0; };
   auto vbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_v1 : lds_v0; };
   auto bbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_b1 : lds_b0; };
 
@@ -1215,12 +1215,12 @@ __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
   const uint8_t* vbase = static_cast<const uint8_t*>(p.vop) + ((int64_t)b * p.Hkv + hk) * (int64_t)n_blk * kVTile;
   auto tile_of = [&](int it) __attribute__((always_inline)) { return p.order ? (t_end - 1 - it) : (t_first + it); };
   // load i fills LDS chunk position i * 64 + lane, which holds logical chunk position ^ key(row)
-  auto load_k = [&](int t, int buf) __attribute__((always_inline)) {
+  auto load_k = [&](int t) __attribute__((always_inline)) {
     const uint8_t* ks = kbase + (int64_t)t * kKTile;
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
       const int cp = i * 64 + lane, r = cp / SK::kChunks;
-      load_to_lds16(ks + r * kKRow + (((cp % SK::kChunks) ^ SK::key(r)) << 4), kbuf(buf) + i * 1024);
+      load_to_lds16(ks + r * kKRow + (((cp % SK::kChunks) ^ SK::key(r)) << 4), lds_k + i * 1024);
     }
   };
   auto load_v = [&](int t, int buf) __attribute__((always_inline)) {
@@ -1237,8 +1237,8 @@ __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
   auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   const int xk = SK::key(li);
-  auto issue_s = [&](int buf, f32x16_t(&sa)[2]) __attribute__((always_inline)) {
-    const uint8_t* kl = kbuf(buf) + li * kKRow;
+  auto issue_s = [&](f32x16_t(&sa)[2]) __attribute__((always_inline)) {
+    const uint8_t* kl = lds_k + li * kKRow;
 #pragma unroll
     for (int s = 0; s < G::kQSteps; ++s)
 #pragma unroll
@@ -1274,11 +1274,13 @@ __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
     constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
     const int t = tile_of(it);
     if (it + 1 < n_it) {
-      load_k(tile_of(it + 1), nxt);
       load_v(tile_of(it + 1), nxt);
       load_b(tile_of(it + 1), nxt);
     }
-    issue_s(cur, sacc);
+    issue_s(sacc);
+    // the logits have read K (the MFMAs took their operands): reload it with block t+1
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (it + 1 < n_it) load_k(tile_of(it + 1));
     const int key0 = t * kKvBlock;
     const bool mask = key0 + kKvBlock - 1 > p.Nk - p.Nq;  // some row cannot see some key
     const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bbuf(cur)[lane] != 0.0f) != 0;
@@ -1341,7 +1343,7 @@ __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
     __syncthreads();
   };
 
-  load_k(tile_of(0), 0);
+  load_k(tile_of(0));
   load_v(tile_of(0), 0);
   load_b(tile_of(0), 0);
   wait_loads();
