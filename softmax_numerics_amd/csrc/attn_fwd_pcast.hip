@@ -1700,9 +1700,11 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
   const int wave = tid / 64, lane = tid % 64;
   const int g = lane / 32, li = lane % 32;
   const int n_kb = (p.N + kBlockRows - 1) / kBlockRows;
-  const int kb = blockIdx.x % n_kb;  // causal: the lowest keys (the most rows) first
-  const int bhk = blockIdx.x / n_kb;
-  const int hk = bhk % p.Hkv, b = bhk / p.Hkv;
+  // the forward's XCD-aware order over (b, kv head, key block): the key blocks of a kv
+  // head share one XCD's L2; ascending, so with a causal mask the key blocks with the
+  // most rows start first
+  int b, hk, kb;
+  decode_block(blockIdx.x, n_kb * p.Hkv * p.B, n_kb, p.Hkv, false, b, hk, kb);
   const int Gq = p.Hq / p.Hkv;
   const int key0 = kb * kBlockRows;
   const int wkey0 = key0 + wave * kRowsPerWave;
@@ -1738,9 +1740,11 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
     const int pos = (wave * kTLoads + i) * 64 + lane, r = pos / ST::kChunks;
     tsrc[i] = r * kTRow + (((pos % ST::kChunks) ^ ST::key(r)) << 4);
   }
-  // iteration it: query head hk * Gq + it / n_r, row block r_first + it % n_r
+  // iteration it: query head hk * Gq + it / n_r, row blocks from the last one down, so
+  // that the workgroups of a kv head, whatever their first row block, read the same
+  // Q / dO tiles at about the same time
   auto head_of = [&](int it) __attribute__((always_inline)) { return hk * Gq + it / n_r; };
-  auto rblk_of = [&](int it) __attribute__((always_inline)) { return r_first + it % n_r; };
+  auto rblk_of = [&](int it) __attribute__((always_inline)) { return n_rblk - 1 - it % n_r; };
   auto load = [&](int it, int buf) __attribute__((always_inline)) {
     const int64_t hrow = ((int64_t)b * p.Hq + head_of(it)) * p.N;  // first row of the head
     const int r = rblk_of(it);
