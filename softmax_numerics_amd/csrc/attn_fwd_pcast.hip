@@ -1,4 +1,4 @@
-// FP8 "P-cast" attention forward for MI355X (gfx950 / CDNA4).
+// FP8 "P-cast" attention for MI355X (gfx950 / CDNA4): the forward, and around it.
 //
 // What is computed (FlashAttention blog, "L'algoritmo Flash Attention" and
 // "La ricorrenza softmax online"; P-cast summaries, sections 1-2): for every
@@ -30,6 +30,19 @@
 //   1/(S*l) is exact up to the final reciprocal.  Other S use an fp32 multiply
 //   (not exact, as the P-cast summary notes for 448), and S > 448 clamps first
 //   because the conversion does not saturate by itself.
+//
+// Around the forward, in this file:
+// * FP8 logits: a template flag of the FP8 kernel rounds Q to E4M3 per row as
+//   it loads it and reads K as E4M3 codes with one scale per key block
+//   (pcast_prep_kv8 writes them, with the V copy); the logits then run on the
+//   FP8 matrix cores too.
+// * Row diagnostics: a counter level of the FP8 kernel that also accumulates the
+//   non-sink and the zeroed non-sink mass of each row and writes its lse.
+// * Split-KV decode: pcast_decode_split (one wave per key range, GQA rows packed
+//   into the MFMA columns) and pcast_decode_merge.
+// * Backward by recomputation from lse: pcast_bwd_rowdot, pcast_attn_bwd_dq (a
+//   lane per query row) and pcast_attn_bwd_dkv (a lane per key).
+// * The host side: argument checks, workspace layouts and the C entry points.
 
 #include <hip/hip_runtime.h>
 
