@@ -89,3 +89,50 @@ def quantize_q(bits: np.ndarray):
 def quantize_k(bits: np.ndarray):
     """K with one scale per 64-key block: (dequantised bf16 bits, exponents [B, H, N/64])."""
     return quantize_blocks(bits, K_BLOCK_ROWS)
+
+
+# ---------------------------------------------------------------------------
+# Random rotation before the quantisation ("FP8 con elaborazione incoerente" in the
+# FlashAttention blog's FA3 section: Q and K are rotated by a random orthogonal
+# matrix so that an outlier's magnitude spreads over all coordinates).  Reading:
+# the randomised Hadamard transform x -> x diag(sigma) H with H the d x d Sylvester
+# matrix of +-1 and sigma random signs (an input).  It is not normalised: since
+# H H^T = d I, (q diag(sigma) H) . (k diag(sigma) H) = d (q . k), and the factor d
+# (a power of two) is taken out of K exactly.  In fp64 the rotation of bf16 inputs
+# is exact.
+# ---------------------------------------------------------------------------
+def hadamard(d: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order d (a power of two), entries +-1."""
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    if h.shape[0] != d:
+        raise ValueError("d must be a power of two")
+    return h
+
+
+def rotate(bits: np.ndarray, signs) -> np.ndarray:
+    """x diag(signs) H for every row of a bf16 tensor [..., d], fp64."""
+    x = _bf16_bits_to_f64(bits)
+    d = x.shape[-1]
+    return (x * np.asarray(signs, dtype=np.float64)) @ hadamard(d)
+
+
+def quantize_values(x: np.ndarray, rows: int):
+    """quantize_blocks on fp64 values [B, H, N, d]: (E4M3_RNE(x / 2^e) * 2^e, e)."""
+    B, H, N, d = x.shape
+    blocks = x.reshape(B, H, N // rows, rows * d)
+    exps = scale_exps(np.max(np.abs(blocks), axis=3))
+    q = e4m3_rne(np.ldexp(blocks, -exps[..., None]))
+    assert q.size == 0 or np.max(np.abs(q)) <= E4M3_MAX
+    return np.ldexp(q, exps[..., None]).reshape(x.shape), exps
+
+
+def quantize_rotated(q_bits: np.ndarray, k_bits: np.ndarray, signs):
+    """Rotated, then quantised Q (per row) and K (per 64-key block), as bf16 bits whose
+    plain dot products are those of the original logits' inputs: Q~ and K~ / d.
+    Returns (q bits, k bits, q exps [B, H, N], k exps [B, Hkv, N/64])."""
+    d = np.shape(q_bits)[-1]
+    qv, eq = quantize_values(rotate(q_bits, signs), Q_BLOCK_ROWS)
+    kv, ek = quantize_values(rotate(k_bits, signs), K_BLOCK_ROWS)
+    return _f64_to_bf16_bits(qv), _f64_to_bf16_bits(kv / d), eq, ek

@@ -173,3 +173,73 @@ def test_planted_head_scale_is_caught():
     # per row: relative error at most 2^-4 (3 mantissa bits, no subnormals at these maxima)
     assert np.all(err_row <= 2.0 ** -4 * np.abs(x[0, 0, 1::2]) + 1e-300)
     assert np.sum(err_head ** 2) > 100 * np.sum(err_row ** 2)
+
+
+# ---- random rotation (randomised Hadamard transform) ----
+
+@pytest.mark.parametrize("d", [1, 2, 8, 64, 128])
+def test_hadamard_is_orthogonal_up_to_d(d):
+    h = qk8.hadamard(d)
+    assert np.array_equal(h @ h.T, d * np.eye(d))
+    assert set(np.unique(h)) <= {-1.0, 1.0}
+
+
+def test_rotation_keeps_dot_products_exactly():
+    q, k, _ = synthetic.qkv_bf16(1, 1, 1, 16, 128, 48)
+    signs = np.random.default_rng(3).choice([-1.0, 1.0], size=128)
+    rq, rk = qk8.rotate(q, signs)[0, 0], qk8.rotate(k, signs)[0, 0]
+    x, y = reference.bf16_to_f64(q)[0, 0], reference.bf16_to_f64(k)[0, 0]
+    assert np.array_equal(rq @ rk.T, 128 * (x @ y.T))
+
+
+def test_rotation_spreads_an_outlier():
+    """One large channel becomes +-A on every coordinate (the point of the rotation)."""
+    x = np.zeros((1, 1, 1, 64), dtype=np.float32)
+    x[..., 5] = 96.0
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    signs = np.ones(64)
+    r = qk8.rotate(bits, signs)
+    assert np.array_equal(np.abs(r), np.full((1, 1, 1, 64), 96.0))
+
+
+def test_rotated_quantisation_gives_scaled_logits():
+    q, k, _ = synthetic.qkv_bf16(1, 1, 1, 128, 64, 49)
+    signs = np.random.default_rng(4).choice([-1.0, 1.0], size=64)
+    qb, kb, eq, ek = qk8.quantize_rotated(q, k, signs)
+    rq, rk = qk8.rotate(q, signs)[0, 0], qk8.rotate(k, signs)[0, 0]
+    dq = reference.bf16_to_f64(qb)[0, 0]
+    dk = reference.bf16_to_f64(kb)[0, 0] * 64
+    # each value is its rotated input rounded to E4M3 at its block's scale
+    for i in (0, 17, 127):
+        e = int(eq[0, 0, i])
+        assert np.array_equal(dq[i], np.ldexp(e4m3.e4m3_rne(np.ldexp(rq[i], -e)), e))
+        e = int(ek[0, 0, i // 64])
+        assert np.array_equal(dk[i], np.ldexp(e4m3.e4m3_rne(np.ldexp(rk[i], -e)), e))
+    # and the plain dot product of the returned tensors approximates the original one
+    x, y = reference.bf16_to_f64(q)[0, 0], reference.bf16_to_f64(k)[0, 0]
+    got = reference.bf16_to_f64(qb)[0, 0] @ reference.bf16_to_f64(kb)[0, 0].T
+    assert np.max(np.abs(got - x @ y.T)) < 0.2 * np.max(np.abs(x @ y.T))
+
+
+def test_rotation_lowers_the_error_with_outlier_channels():
+    """Gaussian Q, K with four channels 30x larger: without rotation the outliers set
+    every row's scale and the small channels lose precision; rotated, the error of
+    the logits drops (the FA3 section reports 2.6x on its data)."""
+    rng = np.random.default_rng(5)
+    q, k, _ = synthetic.qkv_bf16(1, 1, 1, 256, 128, 50)
+    x = reference.bf16_to_f64(q).copy()
+    y = reference.bf16_to_f64(k).copy()
+    for t in (x, y):
+        t[..., [3, 40, 77, 100]] *= 30.0
+    qbits = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    kbits = (y.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    exact = reference.bf16_to_f64(qbits)[0, 0] @ reference.bf16_to_f64(kbits)[0, 0].T
+    qa, _ = qk8.quantize_q(qbits)
+    ka, _ = qk8.quantize_k(kbits)
+    plain = reference.bf16_to_f64(qa)[0, 0] @ reference.bf16_to_f64(ka)[0, 0].T
+    signs = rng.choice([-1.0, 1.0], size=128)
+    qr, kr, _, _ = qk8.quantize_rotated(qbits, kbits, signs)
+    rot = reference.bf16_to_f64(qr)[0, 0] @ reference.bf16_to_f64(kr)[0, 0].T
+    e_plain = np.sqrt(np.mean((plain - exact) ** 2))
+    e_rot = np.sqrt(np.mean((rot - exact) ** 2))
+    assert e_rot < e_plain
