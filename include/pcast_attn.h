@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define PCAST_ABI_VERSION 5
+#define PCAST_ABI_VERSION 6
 
 /* Keys per KV block.  The block size is part of the numerics (the running
  * max is updated once per block), so it is fixed. */
@@ -273,6 +273,37 @@ int attn_fwd_pcast_qk8_prepared(const void* Q, const void* workspace, const floa
 int attn_fwd_pcast_qk8(const void* Q, const void* K, const void* V, const float* bias, int B, int Hq,
                        int Hkv, int N, int d, int causal, float S, int order, float* out,
                        unsigned long long* stats, void* stream);
+
+/*
+ * The FP8-logit forward with a random rotation of Q and K before the rounding
+ * (FlashAttention blog, section "FA3: Meccanica della tramoggia", item 3: the
+ * vectors are rotated at random before the block quantisation so that an
+ * outlier's magnitude spreads over all coordinates).  Each row x of Q and K
+ * becomes x diag(sigma) H, H the d x d Sylvester Hadamard matrix of +-1 and
+ * sigma the caller's signs; since H H^T = d I the logits are those of the
+ * unrotated inputs times d, which the kernel divides out exactly.  The rotation
+ * is computed in fp64 (exact for bf16 inputs) and rounded to E4M3 with one
+ * power-of-two scale per query row and per 64-key block, as in
+ * attn_fwd_pcast_qk8.
+ *
+ * pcast_workspace_bytes_qk8_rot -- bytes of the workspace: that of the
+ * unrotated variant plus the codes of Q and one exponent per query row.
+ * pcast_prepare_qk8_rot -- enqueue the V copy and the rotation pre-passes of K
+ * and Q.  signs: device, int8 [d], the signs sigma (a negative entry is -1,
+ * any other +1; the caller draws them).  Other arguments as for
+ * pcast_prepare_qk8, plus Q and Hq.
+ * attn_fwd_pcast_qk8_rot_prepared -- the attention kernel on that workspace;
+ * arguments and errors as for attn_fwd_pcast_qk8_prepared (no Q: its codes are
+ * in the workspace).  Allocates nothing.
+ */
+size_t pcast_workspace_bytes_qk8_rot(int B, int Hq, int Hkv, int N, int d);
+
+int pcast_prepare_qk8_rot(const void* Q, const void* K, const void* V, const signed char* signs, int B, int Hq,
+                          int Hkv, int N, int d, void* workspace, void* stream);
+
+int attn_fwd_pcast_qk8_rot_prepared(const void* workspace, const float* bias, int B, int Hq, int Hkv, int N, int d,
+                                    int causal, float S, int order, float* out, unsigned long long* stats,
+                                    void* stream);
 
 /* Number of uint64 words the stats buffer needs: B * Hq * ceil(N / 64) * 2. */
 size_t pcast_stats_words(int B, int Hq, int N);

@@ -24,7 +24,8 @@ EXPORTS = ("attn_fwd_pcast", "pcast_prepare_v", "attn_fwd_pcast_prepared", "pcas
            "pcast_prepare_qk8", "attn_fwd_pcast_qk8_prepared", "attn_fwd_pcast_qk8",
            "attn_fwd_pcast_rows", "pcast_sink_max_mean", "pcast_delta_critical",
            "pcast_underflow_model", "pcast_lost_mass_model", "attn_decode_pcast",
-           "pcast_decode_workspace_bytes", "attn_bwd_pcast", "pcast_bwd_workspace_bytes")
+           "pcast_decode_workspace_bytes", "attn_bwd_pcast", "pcast_bwd_workspace_bytes",
+           "pcast_workspace_bytes_qk8_rot", "pcast_prepare_qk8_rot", "attn_fwd_pcast_qk8_rot_prepared")
 
 _lock = threading.Lock()
 _lib = None
@@ -80,6 +81,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_bwd_pcast.restype = I
             lib.pcast_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
             lib.pcast_bwd_workspace_bytes.restype = ctypes.c_size_t
+            lib.pcast_workspace_bytes_qk8_rot.argtypes = [I, I, I, I, I]
+            lib.pcast_workspace_bytes_qk8_rot.restype = ctypes.c_size_t
+            lib.pcast_prepare_qk8_rot.argtypes = [P, P, P, P, I, I, I, I, I, P, P]
+            lib.pcast_prepare_qk8_rot.restype = I
+            lib.attn_fwd_pcast_qk8_rot_prepared.argtypes = [P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P]
+            lib.attn_fwd_pcast_qk8_rot_prepared.restype = I
             D = ctypes.c_double
             lib.pcast_sink_max_mean.argtypes = [I]
             lib.pcast_sink_max_mean.restype = D
@@ -180,6 +187,23 @@ def underflow_model(delta: float, S: float, k: int = 4) -> float:
 
 def lost_mass_model(delta: float, S: float, k: int = 4) -> float:
     return float(load_library().pcast_lost_mass_model(float(delta), float(S), int(k)))
+
+
+def workspace_bytes_qk8_rot(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
+    return int(load_library().pcast_workspace_bytes_qk8_rot(B, Hq, Hkv, N, d))
+
+
+def prepare_qk8_rot(Q, K, V, signs, B, Hq, Hkv, N, d, workspace, stream) -> int:
+    """Raw pcast_prepare_qk8_rot with integer device addresses; returns the C return code."""
+    return int(load_library().pcast_prepare_qk8_rot(Q, K, V, signs, B, Hq, Hkv, N, d, workspace, stream or None))
+
+
+def attn_fwd_pcast_qk8_rot_prepared(workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
+                                    stream) -> int:
+    """Raw attn_fwd_pcast_qk8_rot_prepared with integer device addresses; returns the C return code."""
+    return int(load_library().attn_fwd_pcast_qk8_rot_prepared(
+        workspace, bias or None, B, Hq, Hkv, N, d, int(causal), float(S), int(order), out, stats or None,
+        stream or None))
 
 
 def workspace_bytes_qk8(B: int, Hkv: int, N: int, d: int) -> int:

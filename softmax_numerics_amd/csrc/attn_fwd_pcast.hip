@@ -220,6 +220,88 @@ __global__ __launch_bounds__(256) void pcast_prep_kv8(const uint16_t* __restrict
   prep_v_block<D, true>(V, vop, blk);
 }
 
+// Rotated FP8 logits: x -> x diag(sigma) H (H the Sylvester matrix of +-1, sigma the
+// caller's signs), in fp64, where the rotation of bf16 inputs is exact; then the
+// E4M3 codes of x * 2^-e with one scale per row (kPerRow, for Q) or per 64-row block
+// (for K).  One workgroup per 64 rows of one head.  The rounding to the E4M3 grid is
+// done in fp64 (round to nearest even at the grid step of the value's binade), so
+// that no intermediate fp32 rounding can move a value onto a midpoint; the result is
+// on the grid, which the fp32 conversion then encodes exactly.
+__device__ inline double e4m3_rne_f64(double y) {
+  const double a = fabs(y);
+  if (a == 0.0) return y;
+  int E;
+  frexp(a, &E);                                   // a in [2^(E-1), 2^E)
+  const int step = a < 0x1.0p-6 ? -9 : (E - 1) - 3;  // grid step 2^step (subnormal below 2^-6)
+  return copysign(ldexp(rint(ldexp(a, -step)), step), y);
+}
+
+__device__ inline int scale_exp_f64(double amax) {
+  if (amax == 0.0) return 0;
+  int E;
+  const double m = frexp(amax, &E);
+  return m <= 0.875 ? E - 9 : E - 8;
+}
+
+template <int D, bool kPerRow>
+__global__ __launch_bounds__(256) void pcast_prep_rot8(const uint16_t* __restrict__ x,
+                                                       const signed char* __restrict__ signs,
+                                                       uint8_t* __restrict__ codes, int* __restrict__ exps) {
+  __shared__ double tile[kKvBlock][D];
+  __shared__ double rmax[kKvBlock];
+  const int tid = threadIdx.x;
+  const int64_t blk = blockIdx.x;  // flat 64-row block
+  const uint16_t* src = x + blk * kKvBlock * D;
+  for (int i = tid; i < kKvBlock * D; i += 256) {
+    const int col = i % D;
+    const double v = (double)__builtin_bit_cast(float, (uint32_t)src[i] << 16);
+    tile[i / D][col] = signs[col] < 0 ? -v : v;
+  }
+  __syncthreads();
+  // in-place fast Walsh-Hadamard transform of every row (natural, Sylvester order)
+  for (int h = 1; h < D; h *= 2) {
+    for (int pi = tid; pi < kKvBlock * D / 2; pi += 256) {
+      const int r = pi / (D / 2), j = pi % (D / 2);
+      const int i = (j / h) * 2 * h + (j % h);
+      const double a = tile[r][i], b = tile[r][i + h];
+      tile[r][i] = a + b;
+      tile[r][i + h] = a - b;
+    }
+    __syncthreads();
+  }
+  __shared__ int erow[kKvBlock];
+  if (tid < kKvBlock) {
+    double m = 0.0;
+    for (int c = 0; c < D; ++c) m = fmax(m, fabs(tile[tid][c]));
+    rmax[tid] = m;
+  }
+  __syncthreads();
+  // scale exponents: per row, or the block's from the max over its rows
+  if (tid < kKvBlock) {
+    double m = rmax[tid];
+    if constexpr (!kPerRow)
+      for (int i = 0; i < kKvBlock; ++i) m = fmax(m, rmax[i]);
+    erow[tid] = scale_exp_f64(m);
+  }
+  __syncthreads();
+  uint32_t* dst = reinterpret_cast<uint32_t*>(codes + blk * kKvBlock * D);
+  for (int w = tid; w < kKvBlock * D / 4; w += 256) {
+    const int r = (w * 4) / D, c = (w * 4) % D;
+    const int e = erow[r];
+    float f[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) f[t] = (float)e4m3_rne_f64(ldexp(tile[r][c + t], -e));
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], word, true);
+    dst[w] = (uint32_t)word;
+  }
+  if constexpr (kPerRow) {
+    if (tid < kKvBlock) exps[blk * kKvBlock + tid] = erow[tid];
+  } else {
+    if (tid == 0) exps[blk] = erow[0];
+  }
+}
+
 struct Params {
   const uint16_t* q;
   const uint16_t* k;
@@ -233,9 +315,12 @@ struct Params {
   float S;            // P-cast scale (1 in the bf16 path)
   float inv_S;        // 1/S: the conversion scale when S is a power of two
   float p_clamp;      // largest P kept before conversion when S > 448 (448/S)
-  // FP8 logits: E4M3 codes of K ([B][Hkv][N][d] bytes) and the exponent of each key block
+  // FP8 logits: E4M3 codes of K ([B][Hkv][N][d] bytes) and the exponent of each key block;
+  // with the rotation also the codes of Q ([B][Hq][N][d]) and the exponent of each row
   const uint8_t* k8;
   const int* kexp;
+  const uint8_t* q8;
+  const int* qexp;
   // per-row diagnostics [B][Hq][N], or null
   float* lse;
   float* lost;
@@ -614,7 +699,9 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params 
 // ---------------------------------------------------------------------------
 // kStats: 0 = no counting; 1 = underflow counters; 2 = counters (if p.stats) and the
 // per-row log-sum-exp and lost non-sink mass (every block then takes the sequential step).
-template <int D, int kMode, bool kCausal, int kStats, bool kQ8>
+// kQ8: 0 = bf16 logits; 1 = FP8 logits, Q rounded here per row; 2 = FP8 logits of the
+// rotated Q and K, both as codes from the pre-pass.
+template <int D, int kMode, bool kCausal, int kStats, int kQ8>
 __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p) {
   static_assert(kMode != kBf16, "FP8 modes only");
   constexpr bool kDiag = kStats == 2;
@@ -622,7 +709,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
   // kQ8: Q and K as E4M3 codes, logits on the FP8 MFMA (K = 64 per step), else bf16
   constexpr int kKRow = kQ8 ? D : D * 2;      // bytes per K row
   constexpr int kSSteps = kQ8 ? D / 64 : G::kQSteps;  // logit MFMA k-steps per 32-key half
-  using KFrag = typename Select<kQ8, i32x8_t, bf16x8_t>::type;  // one operand fragment
+  using KFrag = typename Select<kQ8 != 0, i32x8_t, bf16x8_t>::type;  // one operand fragment
   constexpr int kVRow = kKvBlock;             // bytes per V^T row (64 E4M3 codes)
   constexpr int kKTile = kKvBlock * kKRow;    // bytes of one K block
   constexpr int kVTile = D * kVRow;           // bytes of one V operand block
@@ -675,7 +762,17 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
   float c_row = p.logit_scale;
   if (wave_active) {
     const int64_t row = ((int64_t)b * p.Hq + h) * p.N + myrow;
-    if constexpr (kQ8) {
+    if constexpr (kQ8 == 2) {
+      // the pre-pass's codes of the rotated row; the rotation scales Q K^T by d
+      const uint8_t* qrow = p.q8 + row * D + g * 32;
+#pragma unroll
+      for (int s = 0; s < kSSteps; ++s) {
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(qrow + s * 64);
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(qrow + s * 64 + 16);
+        qf[s] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      c_row = ldexpf(p.logit_scale, p.qexp[row] - (D == 64 ? 6 : 7));
+    } else if constexpr (kQ8 == 1) {
       const uint16_t* qrow = p.q + row * D + g * 32;
       i32x4_t w[kSSteps][4];
       uint32_t m = 0;
@@ -748,7 +845,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
   // K fragment of 32-key half kb and k-step s from K buffer `buf`
   auto kread = [&](int buf, int kb, int s) __attribute__((always_inline)) -> KFrag {
     const uint8_t* kl = kbuf(buf) + (kb * 32 + li) * kKRow;
-    if constexpr (kQ8) {
+    if constexpr (kQ8 != 0) {
       const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kl + (((4 * s + 2 * g) ^ xk) << 4));
       const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(kl + (((4 * s + 2 * g + 1) ^ xk) << 4));
       return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -757,7 +854,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
     }
   };
   auto smma = [&](const KFrag& a, int s, const f32x16_t& acc) __attribute__((always_inline)) -> f32x16_t {
-    if constexpr (kQ8) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[s], acc, 0, 0, 0, 0, 0, 0);
+    if constexpr (kQ8 != 0) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[s], acc, 0, 0, 0, 0, 0, 0);
     else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc, 0, 0, 0);
   };
   auto issue_s = [&](int buf, f32x16_t(&sa)[2]) __attribute__((always_inline)) {
@@ -946,7 +1043,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
   auto step = [&](int it, auto cur_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
     const int t = tile_of(it);
-    if constexpr (kQ8) {
+    if constexpr (kQ8 != 0) {
       c = ldexpf(c_row, ke_next);
       if (it + 1 < n_it) ke_next = kexp_head[tile_of(it + 1)];
     }
@@ -1937,18 +2034,23 @@ void launch_attn3(const Params& p, hipStream_t stream) {
       hipLaunchKernelGGL((pcast_attn_fwd_bf16<D, kCausal, true>), grid, dim3(kThreads), 0, stream, p);
     else
       hipLaunchKernelGGL((pcast_attn_fwd_bf16<D, kCausal, false>), grid, dim3(kThreads), 0, stream, p);
+  } else if (p.k8 && p.q8) {
+    if (p.stats)
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, 2>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, 2>), grid, dim3(kThreads), 0, stream, p);
   } else if (p.k8) {
     if (p.stats)
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, true>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, 1>), grid, dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, true>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, 1>), grid, dim3(kThreads), 0, stream, p);
   } else if (p.lse || p.lost) {
-    hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 2, false>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 2, 0>), grid, dim3(kThreads), 0, stream, p);
   } else {
     if (p.stats)
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, 0>), grid, dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, 0>), grid, dim3(kThreads), 0, stream, p);
   }
 }
 
@@ -2010,14 +2112,18 @@ DecodeLayout decode_layout(int B, int Hkv, int Nk, int d, int split_keys) {
 // layout, and the exponent of each key block's scale (int32).
 struct Qk8Layout {
   size_t k8, kexp, total;
+  size_t q8, qexp, total_rot;  // the rotated variant adds the codes and row exponents of Q
 };
-Qk8Layout qk8_layout(int B, int Hkv, int N, int d) {
+Qk8Layout qk8_layout(int B, int Hkv, int N, int d, int Hq = 0) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t nkv = (size_t)B * Hkv * N * d;
   Qk8Layout l;
   l.k8 = up(nkv);
   l.kexp = up(l.k8 + nkv);
   l.total = up(l.kexp + (size_t)B * Hkv * (N / kKvBlock) * 4);
+  l.q8 = l.total;
+  l.qexp = up(l.q8 + (size_t)B * Hq * N * d);
+  l.total_rot = up(l.qexp + (size_t)B * Hq * N * 4);
   return l;
 }
 
@@ -2043,6 +2149,11 @@ size_t pcast_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
 size_t pcast_decode_workspace_bytes(int B, int Hkv, int Nk, int d, int split_keys) {
   if (B <= 0 || Hkv <= 0 || Nk <= 0 || d <= 0 || split_keys <= 0) return 0;
   return decode_layout(B, Hkv, Nk, d, split_keys).total;
+}
+
+size_t pcast_workspace_bytes_qk8_rot(int B, int Hq, int Hkv, int N, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return 0;
+  return qk8_layout(B, Hkv, N, d, Hq).total_rot;
 }
 
 size_t pcast_workspace_bytes_qk8(int B, int Hkv, int N, int d) {
@@ -2145,16 +2256,20 @@ int check_qk8(float S) {
 int enqueue_attn(const void* Q, const void* K, const void* ws, const float* bias, int B, int Hq,
                  int Hkv, int N, int d, int causal, float S, int order, float* out,
                  unsigned long long* stats, hipStream_t st, bool qk8 = false, float* lse = nullptr,
-                 float* lost = nullptr) {
+                 float* lost = nullptr, bool rot = false) {
   const bool fp8 = S != 0.0f;
   Params p{};
   p.lse = lse;
   p.lost = lost;
   if (qk8) {
-    const Qk8Layout l = qk8_layout(B, Hkv, N, d);
+    const Qk8Layout l = qk8_layout(B, Hkv, N, d, Hq);
     const uint8_t* base = static_cast<const uint8_t*>(ws);
     p.k8 = base + l.k8;
     p.kexp = reinterpret_cast<const int*>(base + l.kexp);
+    if (rot) {
+      p.q8 = base + l.q8;
+      p.qexp = reinterpret_cast<const int*>(base + l.qexp);
+    }
   }
   p.q = static_cast<const uint16_t*>(Q);
   p.k = static_cast<const uint16_t*>(K);
@@ -2397,6 +2512,50 @@ int attn_decode_pcast(const void* Q, const void* K, const void* vop, const float
 #undef PCAST_DECODE
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? PCAST_OK : hip_fail(e, "decode kernel launch");
+}
+
+int pcast_prepare_qk8_rot(const void* Q, const void* K, const void* V, const signed char* signs, int B, int Hq,
+                          int Hkv, int N, int d, void* workspace, void* stream) {
+  g_last_error[0] = '\0';
+  if (!Q || !K || !V || !signs || !workspace) return fail(PCAST_EINVAL, "Q, K, V, signs and workspace must be non-null");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(workspace, 16))
+    return fail(PCAST_EINVAL, "Q, K, V and workspace must be 16-byte aligned");
+  int rc = check_shape(B, Hq, Hkv, N, d, 1.0f);
+  if (rc != PCAST_OK) return rc;
+  if ((rc = check_device()) != PCAST_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Qk8Layout l = qk8_layout(B, Hkv, N, d, Hq);
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  const uint16_t* Qb = static_cast<const uint16_t*>(Q);
+  const uint16_t* Kb = static_cast<const uint16_t*>(K);
+  const int64_t qblk = (int64_t)B * Hq * (N / kKvBlock), kblk = (int64_t)B * Hkv * (N / kKvBlock);
+  if ((rc = enqueue_prep(V, B, Hkv, N, d, 1.0f, workspace, st)) != PCAST_OK) return rc;
+  int* kexp = reinterpret_cast<int*>(base + l.kexp);
+  int* qexp = reinterpret_cast<int*>(base + l.qexp);
+  if (d == 64) {
+    hipLaunchKernelGGL((pcast_prep_rot8<64, false>), dim3((unsigned)kblk), dim3(256), 0, st, Kb, signs, base + l.k8, kexp);
+    hipLaunchKernelGGL((pcast_prep_rot8<64, true>), dim3((unsigned)qblk), dim3(256), 0, st, Qb, signs, base + l.q8, qexp);
+  } else {
+    hipLaunchKernelGGL((pcast_prep_rot8<128, false>), dim3((unsigned)kblk), dim3(256), 0, st, Kb, signs, base + l.k8, kexp);
+    hipLaunchKernelGGL((pcast_prep_rot8<128, true>), dim3((unsigned)qblk), dim3(256), 0, st, Qb, signs, base + l.q8, qexp);
+  }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PCAST_OK : hip_fail(e, "rotation pre-pass launch");
+}
+
+int attn_fwd_pcast_qk8_rot_prepared(const void* workspace, const float* bias, int B, int Hq, int Hkv, int N, int d,
+                                    int causal, float S, int order, float* out, unsigned long long* stats,
+                                    void* stream) {
+  g_last_error[0] = '\0';
+  if (!workspace) return fail(PCAST_EINVAL, "workspace must be non-null");
+  if (!aligned(workspace, 16)) return fail(PCAST_EINVAL, "workspace must be 16-byte aligned");
+  int rc = check_attn_args(workspace, workspace, bias, causal, order, out, stats);
+  if (rc != PCAST_OK) return rc;
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  if ((rc = check_qk8(S)) != PCAST_OK) return rc;
+  if ((rc = check_device()) != PCAST_OK) return rc;
+  return enqueue_attn(nullptr, nullptr, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
+                      static_cast<hipStream_t>(stream), true, nullptr, nullptr, true);
 }
 
 int pcast_prepare_qk8(const void* K, const void* V, int B, int Hkv, int N, int d, void* workspace,

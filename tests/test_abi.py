@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_sizes(lib):
-    assert lib.pcast_abi_version() == 5
+    assert lib.pcast_abi_version() == 6
     assert sna.stats_words(4, 32, 8192) == 4 * 32 * 128 * 2
     assert sna.stats_words(1, 1, 100) == 4
     assert sna.workspace_bytes(4, 32, 8192, 128, 256.0) == 4 * 32 * 8192 * 128
@@ -210,6 +210,38 @@ def test_bwd_argument_errors(lib, kw, code):
              causal=1, dQ=FAKE, dK=FAKE, dV=FAKE, workspace=FAKE, stream=0)
     a.update(kw)
     assert sna.attn_bwd_pcast(**a) == code
+
+
+def test_qk8_rot_workspace_layout(lib):
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for B, Hq, Hkv, N, d in ((4, 32, 32, 8192, 128), (1, 3, 1, 64, 64)):
+        nkv, nq = B * Hkv * N * d, B * Hq * N * d
+        base = up(up(up(nkv) + nkv) + 4 * B * Hkv * (N // 64))
+        assert sna.workspace_bytes_qk8_rot(B, Hq, Hkv, N, d) == up(up(base + nq) + 4 * B * Hq * N)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(signs=0), sna.PCAST_EINVAL),
+    (dict(Q=FAKE + 4), sna.PCAST_EINVAL),
+    (dict(workspace=0), sna.PCAST_EINVAL),
+    (dict(d=96), sna.PCAST_ENOTSUP),
+])
+def test_prepare_qk8_rot_argument_errors(lib, kw, code):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, signs=FAKE, B=1, Hq=2, Hkv=1, N=128, d=128, workspace=FAKE, stream=0)
+    a.update(kw)
+    assert sna.prepare_qk8_rot(**a) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(workspace=0), sna.PCAST_EINVAL),
+    (dict(out=0), sna.PCAST_EINVAL),
+    (dict(S=0.0), sna.PCAST_ENOTSUP),
+])
+def test_qk8_rot_prepared_argument_errors(lib, kw, code):
+    a = dict(workspace=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128, causal=1, S=256.0, order=1, out=FAKE,
+             stats=0, stream=0)
+    a.update(kw)
+    assert sna.attn_fwd_pcast_qk8_rot_prepared(**a) == code
 
 
 def test_strerror_texts(lib):

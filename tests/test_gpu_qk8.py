@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import synthetic
-from oracle import e4m3, qk8
+from oracle import core, e4m3, qk8
 from tests import _parity
 
 torch = pytest.importorskip("torch")
@@ -121,6 +121,15 @@ def _run_qk8(sna, qb, kb, vb, bias, causal, S, order, stats=True):
     return out.cpu().numpy(), (None if st is None else st.cpu().numpy())
 
 
+def _run(sna, qb, kb, vb, bias, causal, S, order):
+    """The P-cast forward with bf16 logits, for comparison."""
+    q, k, v = (_parity.to_gpu_bf16(x) for x in (qb, kb, vb))
+    bt = None if bias is None else torch.from_numpy(bias).cuda()
+    out, st = sna.forward(q, k, v, bt, causal=causal, S=S, order=order, stats=True)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), st.cpu().numpy()
+
+
 def _case(sna, name, B, Hq, Hkv, N, d, causal, bias, S, order, seed, blocks=None, qkv=None):
     print(f"\n[case] qk8 {name}: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal} S={S} "
           f"order={order} seed={seed}", flush=True)
@@ -225,3 +234,112 @@ def test_gqa_full_size(sna):
     w = W["gqa"]
     _case(sna, "gqa", w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, synthetic.sink_bias(w.N, 7.0), 256.0, 1,
           w.seed, blocks=6)
+
+
+# ---- FP8 logits with the random Hadamard rotation ----
+
+def _signs(d, seed):
+    return np.random.default_rng(seed).choice(np.array([-1, 1], dtype=np.int8), size=d)
+
+
+def _prepare_rot(sna, qb, kb, vb, signs):
+    B, Hq, N, d = qb.shape
+    Hkv = kb.shape[1]
+    q, k, v = (_parity.to_gpu_bf16(x) for x in (qb, kb, vb))
+    sg = torch.from_numpy(signs).cuda()
+    ws = torch.zeros(sna.workspace_bytes_qk8_rot(B, Hq, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    rc = sna.prepare_qk8_rot(q.data_ptr(), k.data_ptr(), v.data_ptr(), sg.data_ptr(), B, Hq, Hkv, N, d,
+                             ws.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc == sna.PCAST_OK, sna.strerror(rc)
+    torch.cuda.synchronize()
+    return ws
+
+
+def _rot_run(sna, qb, kb, vb, bias, causal, S, order, signs):
+    B, Hq, N, d = qb.shape
+    Hkv = kb.shape[1]
+    ws = _prepare_rot(sna, qb, kb, vb, signs)
+    out = torch.empty((B, Hq, N, d), device="cuda")
+    st = torch.empty(sna.stats_words(B, Hq, N), dtype=torch.int64, device="cuda")
+    bt = None if bias is None else torch.from_numpy(bias).cuda()
+    rc = sna.attn_fwd_pcast_qk8_rot_prepared(ws.data_ptr(), 0 if bt is None else bt.data_ptr(), B, Hq, Hkv, N, d,
+                                             causal, S, order, out.data_ptr(), st.data_ptr(),
+                                             torch.cuda.current_stream().cuda_stream)
+    assert rc == sna.PCAST_OK, sna.strerror(rc)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), st.cpu().numpy().reshape(B, Hq, -1, 2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rotation_prepass_bit_exact(sna, d):
+    print(f"\n[case] qk8 rotation pre-pass d={d}", flush=True)
+    B, Hq, Hkv, N = 2, 4, 2, 192
+    qb = _scaled_heads(B, Hq, N, d, 51, 0)
+    kb = _scaled_heads(B, Hkv, N, d, 51, 1)
+    vb = synthetic.gaussian_bf16(51, 2, kb.shape)
+    signs = _signs(d, 51)
+    w = _prepare_rot(sna, qb, kb, vb, signs).cpu().numpy()
+    nkv, nq = B * Hkv * N * d, B * Hq * N * d
+    off_k = _up(nkv)
+    off_ke = _up(off_k + nkv)
+    off_q = _up(off_ke + 4 * B * Hkv * (N // 64))
+    off_qe = _up(off_q + nq)
+    k8 = w[off_k:off_k + nkv].reshape(kb.shape)
+    ke = w[off_ke:off_ke + 4 * B * Hkv * (N // 64)].view(np.int32).reshape(B, Hkv, N // 64)
+    q8 = w[off_q:off_q + nq].reshape(qb.shape)
+    qe = w[off_qe:off_qe + 4 * B * Hq * N].view(np.int32).reshape(B, Hq, N)
+    sg = signs.astype(np.float64)
+    for codes, exps, bits, rows in ((q8, qe, qb, 1), (k8, ke, kb, 64)):
+        x = qk8.rotate(bits, sg)
+        _, want_e = qk8.quantize_values(x, rows)
+        assert np.array_equal(exps, want_e), "exponents"
+        e = np.repeat(want_e, rows, axis=2)[..., None]
+        want = e4m3.e4m3_encode(np.ldexp(x, -e))
+        assert np.array_equal(e4m3.DECODE_TABLE[codes], e4m3.DECODE_TABLE[want]), "codes"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S,order", [(256.0, 1), (1.0, 0)])
+def test_rotation_parity(sna, d, causal, S, order):
+    print(f"\n[case] qk8 rotation parity d={d} causal={causal} S={S} order={order}", flush=True)
+    qb, kb, vb = synthetic.qkv_bf16(2, 4, 2, 320, d, 52)
+    bias = synthetic.sink_bias(320, 7.0)
+    signs = _signs(d, 52)
+    out, st = _rot_run(sna, qb, kb, vb, bias, causal, S, order, signs)
+    qd, kd, _, _ = qk8.quantize_rotated(qb, kb, signs.astype(np.float64))
+    rep = _parity.compare_qk8(out, st, qd, kd, vb, bias, causal, S, order)
+    print(f"[case] qk8 rotation parity: {rep}", flush=True)
+
+
+def _outlier_inputs(B, Hq, Hkv, N, d, seed, mult):
+    qb, kb, vb = synthetic.qkv_bf16(B, Hq, Hkv, N, d, seed)
+    chans = [3, 40, 77, 100][: 4 if d == 128 else 2]
+    out = []
+    for bits in (qb, kb):
+        x = ((bits.astype(np.uint32)) << 16).view(np.float32).copy()
+        x[..., chans] *= np.float32(mult)
+        u = x.view(np.uint32).astype(np.uint64)
+        out.append(((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16))
+    return out[0], out[1], vb
+
+
+def test_rotation_helps_with_outlier_channels(sna):
+    """Four channels of Q and K 30x larger (with the scale of Q lowered so the logits
+    stay moderate): the output error against exact attention of the unrounded inputs
+    drops with the rotation."""
+    B, Hq, Hkv, N, d = 1, 4, 4, 1024, 128
+    qb, kb, vb = _outlier_inputs(B, Hq, Hkv, N, d, 53, 30.0)
+    x = ((qb.astype(np.uint32)) << 16).view(np.float32) * np.float32(2.0 ** -5)
+    qb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    bias = synthetic.sink_bias(N, 7.0)
+    print("\n[case] qk8 rotation with outlier channels", flush=True)
+    plain, _ = _run_qk8(sna, qb, kb, vb, bias, True, 256.0, 1)
+    rot, _ = _rot_run(sna, qb, kb, vb, bias, True, 256.0, 1, _signs(d, 53))
+    base, _ = _run(sna, qb, kb, vb, bias, True, 256.0, 1)
+    ex = core.rows(qb, kb, vb, bias, True, 256.0, 1, "kernel", want_exact=True)["o1"]
+    mse = {name: float(np.mean((o.reshape(-1, d) - ex) ** 2)) for name, o in
+           (("bf16 logits", base), ("fp8 logits", plain), ("fp8 logits rotated", rot))}
+    print(f"[case] qk8 rotation with outliers: MSE {mse}, plain / rotated {mse['fp8 logits'] / mse['fp8 logits rotated']:.2f}",
+          flush=True)
+    assert mse["fp8 logits rotated"] < mse["fp8 logits"]
