@@ -353,11 +353,44 @@ def main() -> int:
         ach8 = flops / (attn8 * 1e-3) / 1e12
         print(f"[bench] FP8 logits: {wall8 * 1e3 / args.steps:.4f} ms/step (wall), attention kernel "
               f"{attn8:.4f} ms, K/V pre-pass {prep8:.4f} ms", file=sys.stderr, flush=True)
+        # the same with Q and K rotated by diag(sigma) H before the rounding
+        signs = torch.from_numpy(np.random.default_rng(w.seed).choice(np.array([-1, 1], dtype=np.int8), size=w.d)).to(dev)
+        wsr = torch.empty(sna.workspace_bytes_qk8_rot(w.B, w.Hq, w.Hkv, w.N, w.d), dtype=torch.uint8, device=dev)
+
+        def step_rot(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            rc = sna.prepare_qk8_rot(q.data_ptr(), k.data_ptr(), v.data_ptr(), signs.data_ptr(), w.B, w.Hq, w.Hkv,
+                                     w.N, w.d, wsr.data_ptr(), sh)
+            if ev is not None:
+                ev[1].record(stream)
+            rc = rc or sna.attn_fwd_pcast_qk8_rot_prepared(
+                wsr.data_ptr(), bias_t.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), S, order,
+                out.data_ptr(), 0 if stats is None else stats.data_ptr(), sh)
+            if ev is not None:
+                ev[2].record(stream)
+            if rc != sna.PCAST_OK:
+                raise sna.PcastError(rc, sna.strerror(rc))
+
+        for _ in range(2):
+            step_rot()
+        evr = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(min(args.steps, 10))]
+        torch.cuda.synchronize()
+        for e in evr:
+            step_rot(ev=e)
+        torch.cuda.synchronize()
+        rot = {"prepass_ms": round(float(np.mean([e[0].elapsed_time(e[1]) for e in evr])), 5),
+               "attention_kernel_ms": round(float(np.mean([e[1].elapsed_time(e[2]) for e in evr])), 5)}
+        print(f"[bench] FP8 logits, rotated: attention kernel {rot['attention_kernel_ms']:.4f} ms, "
+              f"pre-pass {rot['prepass_ms']:.4f} ms", file=sys.stderr, flush=True)
+        del wsr
         result["qk_fp8"] = {"ms_per_step": round(wall8 * 1e3 / args.steps, 5),
                             "value": round(flops / wall8 * args.steps / 1e12, 2),
                             "attention_kernel_ms": round(attn8, 5), "prepass_ms": round(prep8, 5),
                             "achieved": round(ach8, 2), "peak": PEAK_FP8, "frac": round(ach8 / PEAK_FP8, 4),
-                            "traffic": measured_traffic(w.name, TRAFFIC_FILE_QK8)}
+                            "traffic": measured_traffic(w.name, TRAFFIC_FILE_QK8), "rotated": rot}
+        step_qk8()                                   # the output of the unrotated variant
+        torch.cuda.synchronize()
         out_qk8 = out.cpu().numpy()
 
     if not args.no_backward:

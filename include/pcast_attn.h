@@ -289,8 +289,8 @@ int attn_fwd_pcast_qk8(const void* Q, const void* K, const void* V, const float*
  * pcast_workspace_bytes_qk8_rot -- bytes of the workspace: that of the
  * unrotated variant plus the codes of Q and one exponent per query row.
  * pcast_prepare_qk8_rot -- enqueue the V copy and the rotation pre-passes of K
- * and Q.  signs: device, int8 [d], the signs sigma (a negative entry is -1,
- * any other +1; the caller draws them).  Other arguments as for
+ * and Q.  signs: device, int8 [d], 16-byte aligned, the signs sigma (a negative
+ * entry is -1, any other +1; the caller draws them).  Other arguments as for
  * pcast_prepare_qk8, plus Q and Hq.
  * attn_fwd_pcast_qk8_rot_prepared -- the attention kernel on that workspace;
  * arguments and errors as for attn_fwd_pcast_qk8_prepared (no Q: its codes are

@@ -247,58 +247,75 @@ template <int D, bool kPerRow>
 __global__ __launch_bounds__(256) void pcast_prep_rot8(const uint16_t* __restrict__ x,
                                                        const signed char* __restrict__ signs,
                                                        uint8_t* __restrict__ codes, int* __restrict__ exps) {
-  __shared__ double tile[kKvBlock][D];
-  __shared__ double rmax[kKvBlock];
+  // four lanes per row, each with V contiguous values: the transform's stages of
+  // stride below V run in registers, the strides V and 2V across lanes (xor 1, 2)
+  constexpr int V = D / 4;
   const int tid = threadIdx.x;
-  const int64_t blk = blockIdx.x;  // flat 64-row block
-  const uint16_t* src = x + blk * kKvBlock * D;
-  for (int i = tid; i < kKvBlock * D; i += 256) {
-    const int col = i % D;
-    const double v = (double)__builtin_bit_cast(float, (uint32_t)src[i] << 16);
-    tile[i / D][col] = signs[col] < 0 ? -v : v;
+  const int r = tid / 4, part = tid % 4;
+  const int64_t row = (int64_t)blockIdx.x * kKvBlock + r;  // 64 rows per workgroup
+  const uint16_t* src = x + row * D + part * V;
+  // the lane's V signs (16-byte aligned, V a multiple of 16) and values, all loads first
+  i32x4_t sw[V / 16], xw[V / 8];
+#pragma unroll
+  for (int k = 0; k < V / 16; ++k) sw[k] = *reinterpret_cast<const i32x4_t*>(signs + part * V + k * 16);
+#pragma unroll
+  for (int k = 0; k < V / 8; ++k) xw[k] = *reinterpret_cast<const i32x4_t*>(src + k * 8);
+  double v[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const uint32_t u = (uint32_t)xw[i / 8][(i % 8) / 2];
+    const double f = (double)__builtin_bit_cast(float, (i & 1) ? (u & 0xFFFF0000u) : (u << 16));
+    const int sgn = (int)(signed char)(((uint32_t)sw[i / 16][(i % 16) / 4] >> (8 * (i % 4))) & 0xFFu);
+    v[i] = sgn < 0 ? -f : f;
   }
-  __syncthreads();
-  // in-place fast Walsh-Hadamard transform of every row (natural, Sylvester order)
-  for (int h = 1; h < D; h *= 2) {
-    for (int pi = tid; pi < kKvBlock * D / 2; pi += 256) {
-      const int r = pi / (D / 2), j = pi % (D / 2);
-      const int i = (j / h) * 2 * h + (j % h);
-      const double a = tile[r][i], b = tile[r][i + h];
-      tile[r][i] = a + b;
-      tile[r][i + h] = a - b;
+  // in-lane stages (natural, Sylvester order)
+#pragma unroll
+  for (int h = 1; h < V; h *= 2)
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if ((i & h) == 0) {
+        const double a = v[i], c = v[i + h];
+        v[i] = a + c;
+        v[i + h] = a - c;
+      }
+  // cross-lane stages: the lower partner keeps the sum, the upper the difference
+#pragma unroll
+  for (int m = 1; m <= 2; m *= 2) {
+    const bool upper = (part & m) != 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const double o = __shfl_xor(v[i], m);
+      v[i] = upper ? o - v[i] : v[i] + o;
     }
+  }
+  double mx = 0.0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) mx = fmax(mx, fabs(v[i]));
+  mx = fmax(mx, __shfl_xor(mx, 1));
+  mx = fmax(mx, __shfl_xor(mx, 2));
+  int e;
+  if constexpr (kPerRow) {
+    e = scale_exp_f64(mx);
+    if (part == 0) exps[row] = e;
+  } else {
+    // the block's exponent from the max over its 64 rows
+    __shared__ double rmax[kKvBlock];
+    if (part == 0) rmax[r] = mx;
     __syncthreads();
+    double bm = 0.0;
+    for (int i = 0; i < kKvBlock; ++i) bm = fmax(bm, rmax[i]);
+    e = scale_exp_f64(bm);
+    if (tid == 0) exps[blockIdx.x] = e;
   }
-  __shared__ int erow[kKvBlock];
-  if (tid < kKvBlock) {
-    double m = 0.0;
-    for (int c = 0; c < D; ++c) m = fmax(m, fabs(tile[tid][c]));
-    rmax[tid] = m;
-  }
-  __syncthreads();
-  // scale exponents: per row, or the block's from the max over its rows
-  if (tid < kKvBlock) {
-    double m = rmax[tid];
-    if constexpr (!kPerRow)
-      for (int i = 0; i < kKvBlock; ++i) m = fmax(m, rmax[i]);
-    erow[tid] = scale_exp_f64(m);
-  }
-  __syncthreads();
-  uint32_t* dst = reinterpret_cast<uint32_t*>(codes + blk * kKvBlock * D);
-  for (int w = tid; w < kKvBlock * D / 4; w += 256) {
-    const int r = (w * 4) / D, c = (w * 4) % D;
-    const int e = erow[r];
+  uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * D + part * V);
+#pragma unroll
+  for (int k = 0; k < V / 4; ++k) {
     float f[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) f[t] = (float)e4m3_rne_f64(ldexp(tile[r][c + t], -e));
+    for (int t = 0; t < 4; ++t) f[t] = (float)e4m3_rne_f64(ldexp(v[4 * k + t], -e));
     int word = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
     word = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], word, true);
-    dst[w] = (uint32_t)word;
-  }
-  if constexpr (kPerRow) {
-    if (tid < kKvBlock) exps[blk * kKvBlock + tid] = erow[tid];
-  } else {
-    if (tid == 0) exps[blk] = erow[0];
+    dst[k] = (uint32_t)word;
   }
 }
 
@@ -2518,8 +2535,8 @@ int pcast_prepare_qk8_rot(const void* Q, const void* K, const void* V, const sig
                           int Hkv, int N, int d, void* workspace, void* stream) {
   g_last_error[0] = '\0';
   if (!Q || !K || !V || !signs || !workspace) return fail(PCAST_EINVAL, "Q, K, V, signs and workspace must be non-null");
-  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(workspace, 16))
-    return fail(PCAST_EINVAL, "Q, K, V and workspace must be 16-byte aligned");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(signs, 16) || !aligned(workspace, 16))
+    return fail(PCAST_EINVAL, "Q, K, V, signs and workspace must be 16-byte aligned");
   int rc = check_shape(B, Hq, Hkv, N, d, 1.0f);
   if (rc != PCAST_OK) return rc;
   if ((rc = check_device()) != PCAST_OK) return rc;

@@ -222,6 +222,7 @@ def test_qk8_rot_workspace_layout(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(signs=0), sna.PCAST_EINVAL),
+    (dict(signs=FAKE + 8), sna.PCAST_EINVAL),
     (dict(Q=FAKE + 4), sna.PCAST_EINVAL),
     (dict(workspace=0), sna.PCAST_EINVAL),
     (dict(d=96), sna.PCAST_ENOTSUP),
