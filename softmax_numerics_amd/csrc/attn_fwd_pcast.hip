@@ -1607,12 +1607,15 @@ __global__ __launch_bounds__(256) void pcast_bwd_rowdot(const uint16_t* __restri
   if (row < rows && part == 0) dvec[row] = acc;
 }
 
-// dQ: a workgroup of 4 waves takes 128 query rows of one (b, h), a lane one row,
-// and walks the key blocks: S^T = K Q^T and dP^T = V dO^T (keys x rows, the
-// forward's layout), dS in registers, dQ^T += K^T dS^T with K^T from its
-// slot-order copy.
+// dQ: a workgroup of 8 waves (two per SIMD) takes 256 query rows of one (b, h),
+// a lane one row, and walks the key blocks: S^T = K Q^T and dP^T = V dO^T (keys x
+// rows, the forward's layout), dS in registers, dQ^T += K^T dS^T with K^T from its
+// slot-order copy.  Each block is taken in its two 32-key halves (products, dS,
+// then that half's k-steps of dQ), which keeps the wave within 256 registers.
+constexpr int kDqWaves = 8;
+constexpr int kDqRows = kDqWaves * kRowsPerWave;
 template <int D, bool kCausal>
-__global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dq(const Params p) {
+__global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Params p) {
   using G = Geometry<D>;
   constexpr int kKRow = D * 2;
   constexpr int kTRow = kKvBlock * 2;
@@ -1620,9 +1623,9 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dq(const Params p)
   constexpr int kTTile = D * kTRow;
   using SK = Swizzle<kKRow>;
   using ST = Swizzle<kTRow>;
-  constexpr int kKLoads = kKTile / (1024 * kWaves);
-  constexpr int kTLoads = kTTile / (1024 * kWaves);
-  static_assert(kKTile % (1024 * kWaves) == 0 && kTTile % (1024 * kWaves) == 0, "staging split");
+  constexpr int kKLoads = kKTile / (1024 * kDqWaves);
+  constexpr int kTLoads = kTTile / (1024 * kDqWaves);
+  static_assert(kKTile % (1024 * kDqWaves) == 0 && kTTile % (1024 * kDqWaves) == 0, "staging split");
   __shared__ __attribute__((aligned(16))) uint8_t lds_k0[kKTile];
   __shared__ __attribute__((aligned(16))) uint8_t lds_k1[kKTile];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v0[kKTile];
@@ -1639,16 +1642,16 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dq(const Params p)
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
   const int g = lane / 32, li = lane % 32;
-  const int n_rb = (p.N + kBlockRows - 1) / kBlockRows;
+  const int n_rb = (p.N + kDqRows - 1) / kDqRows;
   int b, h, rb;
   decode_block(blockIdx.x, n_rb * p.Hq * p.B, n_rb, p.Hq, kCausal, b, h, rb);
   const int hk = h / (p.Hq / p.Hkv);
   const int n_tiles = p.N / kKvBlock;
-  const int row0 = rb * kBlockRows;
+  const int row0 = rb * kDqRows;
   const int wrow0 = row0 + wave * kRowsPerWave;
   const int myrow = wrow0 + li;
   const bool wave_active = wrow0 < p.N;
-  const int t_last = kCausal ? min((row0 + kBlockRows - 1) / kKvBlock, n_tiles - 1) : n_tiles - 1;
+  const int t_last = kCausal ? min((row0 + kDqRows - 1) / kKvBlock, n_tiles - 1) : n_tiles - 1;
   const int n_it = t_last + 1;
   const float c = p.logit_scale;
   const int64_t row = ((int64_t)b * p.Hq + h) * p.N + myrow;
@@ -1703,61 +1706,63 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dq(const Params p)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqacc[dt][r] = 0.0f;
   const int xk = SK::key(li);
+  const int xt = ST::key(li);
 
   auto step = [&](int it, auto cur_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
     if (it + 1 < n_it) load(it + 1, nxt);
     if (visible(it)) {
-      // S^T = K Q^T and dP^T = V dO^T, two 32-key halves each
-      f32x16_t sacc[2], pacc[2];
-      const uint8_t* kl = kbuf(cur) + li * kKRow;
-      const uint8_t* vl = vbuf(cur) + li * kKRow;
-#pragma unroll
-      for (int s = 0; s < G::kQSteps; ++s)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int off = kb * 32 * kKRow + (((2 * s + g) ^ xk) << 4);
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + off);
-          const bf16x8_t e = *reinterpret_cast<const bf16x8_t*>(vl + off);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16_t{} : sacc[kb], 0, 0, 0);
-          pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e, df[s], s == 0 ? f32x16_t{} : pacc[kb], 0, 0, 0);
-        }
       const int key0 = it * kKvBlock;
       const bool diag = kCausal && (key0 + kKvBlock - 1 > wrow0);
       const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bbuf(cur)[lane] != 0.0f) != 0;
-      float bk[32];
-      if (has_bias) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float4 v = *reinterpret_cast<const float4*>(bbuf(cur) + slot_key(g, 4 * q));
-          bk[4 * q] = v.x; bk[4 * q + 1] = v.y; bk[4 * q + 2] = v.z; bk[4 * q + 3] = v.w;
-        }
-      }
-      uint32_t pw[16];
-#pragma unroll
-      for (int w = 0; w < 16; ++w) {
-        float ds2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int j = 2 * w + e;
-          const float x = has_bias ? fmaf(sacc[j / 16][j % 16], c, bk[j] * kLog2e) : sacc[j / 16][j % 16] * c;
-          float pj = __builtin_amdgcn_exp2f(x - lse2);
-          if (diag && key0 + slot_key(g, j) > myrow) pj = 0.0f;
-          ds2[e] = pj * (pacc[j / 16][j % 16] - drow);
-        }
-        pw[w] = cast2_bf16(ds2[0], ds2[1]);
-      }
-      // dQ^T += K^T dS^T: four k-steps of 16 keys per 32-column tile
+      const uint8_t* kl = kbuf(cur) + li * kKRow;
+      const uint8_t* vl = vbuf(cur) + li * kKRow;
       const uint8_t* tl = tbuf(cur) + li * kTRow;
-      const int xt = ST::key(li);
 #pragma unroll
-      for (int dt = 0; dt < G::kDTiles; ++dt)
+      for (int kb = 0; kb < 2; ++kb) {
+        // S^T and dP^T of the half's 32 keys
+        f32x16_t sacc, pacc;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(tl + dt * 32 * kTRow + (((4 * g + s) ^ xt) << 4));
-          const i32x4_t bw = {(int)pw[4 * s], (int)pw[4 * s + 1], (int)pw[4 * s + 2], (int)pw[4 * s + 3]};
-          dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bw), dqacc[dt], 0, 0, 0);
+        for (int s = 0; s < G::kQSteps; ++s) {
+          const int off = kb * 32 * kKRow + (((2 * s + g) ^ xk) << 4);
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + off);
+          const bf16x8_t e = *reinterpret_cast<const bf16x8_t*>(vl + off);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16_t{} : sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e, df[s], s == 0 ? f32x16_t{} : pacc, 0, 0, 0);
         }
+        float bk[16];
+        if (has_bias) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(bbuf(cur) + slot_key(g, 16 * kb + 4 * q));
+            bk[4 * q] = v.x; bk[4 * q + 1] = v.y; bk[4 * q + 2] = v.z; bk[4 * q + 3] = v.w;
+          }
+        }
+        uint32_t pw[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          float ds2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int jj = 2 * w + e, j = 16 * kb + jj;
+            const float x = has_bias ? fmaf(sacc[jj], c, bk[jj] * kLog2e) : sacc[jj] * c;
+            float pj = __builtin_amdgcn_exp2f(x - lse2);
+            if (diag && key0 + slot_key(g, j) > myrow) pj = 0.0f;
+            ds2[e] = pj * (pacc[jj] - drow);
+          }
+          pw[w] = cast2_bf16(ds2[0], ds2[1]);
+        }
+        // dQ^T += K^T dS^T over the half's two k-steps of 16 keys
+#pragma unroll
+        for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int s = 2 * kb + s2;
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(tl + dt * 32 * kTRow + (((4 * g + s) ^ xt) << 4));
+            const i32x4_t bw = {(int)pw[4 * s2], (int)pw[4 * s2 + 1], (int)pw[4 * s2 + 2], (int)pw[4 * s2 + 3]};
+            dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bw), dqacc[dt], 0, 0, 0);
+          }
+      }
     }
     wait_loads();
     __syncthreads();
@@ -2433,22 +2438,22 @@ int attn_bwd_pcast(const void* Q, const void* K, const void* V, const float* O, 
   p.dv = dV;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N;
   p.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)d));
-  const int n_rb = (N + kBlockRows - 1) / kBlockRows;
-  const dim3 gq((unsigned)(n_rb * Hq * B)), gk((unsigned)(n_rb * Hkv * B));
+  const int n_rb = (N + kBlockRows - 1) / kBlockRows, n_qb = (N + kDqRows - 1) / kDqRows;
+  const dim3 gq((unsigned)(n_qb * Hq * B)), gk((unsigned)(n_rb * Hkv * B));
   if (d == 64) {
     if (causal) {
-      hipLaunchKernelGGL((pcast_attn_bwd_dq<64, true>), gq, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((pcast_attn_bwd_dq<64, true>), gq, dim3(kDqWaves * 64), 0, st, p);
       hipLaunchKernelGGL((pcast_attn_bwd_dkv<64, true>), gk, dim3(kThreads), 0, st, p);
     } else {
-      hipLaunchKernelGGL((pcast_attn_bwd_dq<64, false>), gq, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((pcast_attn_bwd_dq<64, false>), gq, dim3(kDqWaves * 64), 0, st, p);
       hipLaunchKernelGGL((pcast_attn_bwd_dkv<64, false>), gk, dim3(kThreads), 0, st, p);
     }
   } else {
     if (causal) {
-      hipLaunchKernelGGL((pcast_attn_bwd_dq<128, true>), gq, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((pcast_attn_bwd_dq<128, true>), gq, dim3(kDqWaves * 64), 0, st, p);
       hipLaunchKernelGGL((pcast_attn_bwd_dkv<128, true>), gk, dim3(kThreads), 0, st, p);
     } else {
-      hipLaunchKernelGGL((pcast_attn_bwd_dq<128, false>), gq, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((pcast_attn_bwd_dq<128, false>), gq, dim3(kDqWaves * 64), 0, st, p);
       hipLaunchKernelGGL((pcast_attn_bwd_dkv<128, false>), gk, dim3(kThreads), 0, st, p);
     }
   }
