@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define PCAST_ABI_VERSION 6
+#define PCAST_ABI_VERSION 7
 
 /* Keys per KV block.  The block size is part of the numerics (the running
  * max is updated once per block), so it is fixed. */
@@ -177,7 +177,7 @@ double pcast_lost_mass_model(double delta, double S, int k);
  * dQ       device, float32 [B][Hq][N][d]; dK, dV device, float32 [B][Hkv][N][d];
  *          written completely.
  * workspace  device, pcast_bwd_workspace_bytes(B, Hq, Hkv, N, d) bytes, 16-byte
- *          aligned, owned by the caller (transposed copies of K, Q, dO and D).
+ *          aligned, owned by the caller (the row dots D = dO . O, fp32 [B][Hq][N]).
  * All products run on bf16 matrix cores with fp32 accumulation; P and dS are
  * rounded to bf16 where they are operands.  Allocates nothing; errors as for
  * attn_fwd_pcast.

@@ -41,7 +41,8 @@
 // * Split-KV decode: pcast_decode_split (one wave per key range, GQA rows packed
 //   into the MFMA columns) and pcast_decode_merge.
 // * Backward by recomputation from lse: pcast_bwd_rowdot, pcast_attn_bwd_dq (a
-//   lane per query row) and pcast_attn_bwd_dkv (a lane per key).
+//   lane per query row) and pcast_attn_bwd_dkv (a lane per key); the transposed
+//   operands come from ds_read_b64_tr_b16 reads of the row-major tiles.
 // * The host side: argument checks, workspace layouts and the C entry points.
 
 #include <hip/hip_runtime.h>
@@ -52,6 +53,8 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
+#include <utility>
 
 #include "pcast_attn.h"
 
@@ -348,14 +351,11 @@ struct Params {
   float* part_ml;         // [..][32][2] running max (log2 units) and row sum
   unsigned int* part_cnt; // [..][32][2] non-sink pairs, zero codes
   // backward: raw V (bf16), dO (bf16), the forward's lse (natural units) and the row
-  // dots D = dO . O; slot-order transposes of K, Q and dO; gradients (fp32)
+  // dots D = dO . O; gradients (fp32)
   const uint16_t* v;
   const uint16_t* dout;
   const float* lse_in;
   const float* dvec;
-  const uint8_t* kt;
-  const uint8_t* qt;
-  const uint8_t* dot;
   float* dq;
   float* dk;
   float* dv;
@@ -390,9 +390,14 @@ __device__ inline uint32_t cast4(const Params& p, float a, float b, float c, flo
   }
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// a in the low half, b in the high half, each rounded to nearest even (one
+// v_cvt_pk_bf16_f32)
 __device__ inline uint32_t cast2_bf16(float a, float b) {
-  const __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 typedef __attribute__((address_space(1))) const void global_cvoid;
@@ -404,9 +409,40 @@ __device__ inline void load_to_lds16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)lds, 16, 0, 0);
 }
 
+// The same through a buffer resource (buffer_load_dword* ... lds): base is
+// wave-uniform, voff the lane's byte offset (below 2^31).  Unlike the global form,
+// which the compiler must treat as a possible LDS access in flight (every later LDS
+// read then waits for lgkmcnt(0)), this keeps its LDS waits exact.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ inline void buffer_to_lds16(__amdgpu_buffer_rsrc_t rs, int voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ inline void buffer_to_lds4(__amdgpu_buffer_rsrc_t rs, int voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 4, voff, 0, 0, 0);
+}
+
 // 4 bytes per lane from global memory straight into LDS (lane i writes lds + 4*i).
 __device__ inline void load_to_lds4(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)lds, 4, 0, 0);
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+
+// An MFMA operand fragment of 8 bf16 read across the rows of a row-major LDS tile
+// with two transposing reads (ds_read_b64_tr_b16): within each 16-lane group, lane
+// i receives element (i % 4) of the 8-byte pieces addressed by lanes 4e + i / 4,
+// e = 0..3, of its group.  Elements 0..3 come from the pieces at lo, 4..7 from hi.
+__device__ inline bf16x8_t tr_frag(const uint8_t* lo, const uint8_t* hi) {
+  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lo);
+  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)hi);
+  const i32x4_t w = {__builtin_bit_cast(int, __builtin_shufflevector(a, a, 0, 1)),
+                     __builtin_bit_cast(int, __builtin_shufflevector(a, a, 2, 3)),
+                     __builtin_bit_cast(int, __builtin_shufflevector(b, b, 0, 1)),
+                     __builtin_bit_cast(int, __builtin_shufflevector(b, b, 2, 3))};
+  return __builtin_bit_cast(bf16x8_t, w);
 }
 
 // max over the two 32-lane halves (lane l and lane l ^ 32 hold the same query row)
@@ -450,6 +486,19 @@ template <int V>
 struct BufIndex {
   static constexpr int value = V;
 };
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time so
+// that every register array index in f is a constant
+template <class F, int... I>
+__device__ __attribute__((always_inline)) inline void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 // ---------------------------------------------------------------------------
 // Attention kernel for the path without the P-cast (S = 0): P and V in bf16, P.V
@@ -1609,38 +1658,32 @@ __global__ __launch_bounds__(256) void pcast_bwd_rowdot(const uint16_t* __restri
 
 // dQ: a workgroup of 8 waves (two per SIMD) takes 256 query rows of one (b, h),
 // a lane one row, and walks the key blocks: S^T = K Q^T and dP^T = V dO^T (keys x
-// rows, the forward's layout), dS in registers, dQ^T += K^T dS^T with K^T from its
-// slot-order copy.  Each block is taken in its two 32-key halves (products, dS,
-// then that half's k-steps of dQ), which keeps the wave within 256 registers.
+// rows, the forward's layout), dS in registers, dQ^T += K^T dS^T with K^T read
+// from the K tile by transposing LDS reads.  Each block is taken in its two 32-key
+// halves (products, dS, then that half's k-steps of dQ), which keeps the wave
+// within 256 registers.
 constexpr int kDqWaves = 8;
 constexpr int kDqRows = kDqWaves * kRowsPerWave;
 template <int D, bool kCausal>
 __global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Params p) {
   using G = Geometry<D>;
   constexpr int kKRow = D * 2;
-  constexpr int kTRow = kKvBlock * 2;
   constexpr int kKTile = kKvBlock * kKRow;
-  constexpr int kTTile = D * kTRow;
   using SK = Swizzle<kKRow>;
-  using ST = Swizzle<kTRow>;
   constexpr int kKLoads = kKTile / (1024 * kDqWaves);
-  constexpr int kTLoads = kTTile / (1024 * kDqWaves);
-  static_assert(kKTile % (1024 * kDqWaves) == 0 && kTTile % (1024 * kDqWaves) == 0, "staging split");
+  static_assert(kKTile % (1024 * kDqWaves) == 0, "staging split");
   __shared__ __attribute__((aligned(16))) uint8_t lds_k0[kKTile];
   __shared__ __attribute__((aligned(16))) uint8_t lds_k1[kKTile];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v0[kKTile];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v1[kKTile];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_t0[kTTile];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_t1[kTTile];
   __shared__ __attribute__((aligned(16))) float lds_b0[kKvBlock];
   __shared__ __attribute__((aligned(16))) float lds_b1[kKvBlock];
   auto kbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_k1 : lds_k0; };
   auto vbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_v1 : lds_v0; };
-  auto tbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_t1 : lds_t0; };
   auto bbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_b1 : lds_b0; };
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int g = lane / 32, li = lane % 32;
   const int n_rb = (p.N + kDqRows - 1) / kDqRows;
   int b, h, rb;
@@ -1669,19 +1712,30 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Para
     lse2 = p.lse_in[row] * kLog2e;
     drow = p.dvec[row];
   }
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k + ((int64_t)b * p.Hkv + hk) * p.N * D);
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v + ((int64_t)b * p.Hkv + hk) * p.N * D);
-  const uint8_t* tbase = p.kt + ((int64_t)b * p.Hkv + hk) * (int64_t)n_tiles * kTTile;
-  int ksrc[kKLoads], tsrc[kTLoads];
+  const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(p.k + ((int64_t)b * p.Hkv + hk) * p.N * D);
+  const __amdgpu_buffer_rsrc_t vres = buffer_rsrc(p.v + ((int64_t)b * p.Hkv + hk) * p.N * D);
+  const __amdgpu_buffer_rsrc_t bres = buffer_rsrc(p.bias);
+  int ksrc[kKLoads];
 #pragma unroll
   for (int i = 0; i < kKLoads; ++i) {
     const int pos = (wave * kKLoads + i) * 64 + lane, r = pos / SK::kChunks;
     ksrc[i] = r * kKRow + (((pos % SK::kChunks) ^ SK::key(r)) << 4);
   }
+  // Transposing reads of the K tile for the A operand of dQ^T += K^T dS^T: k-step s
+  // of tile dt takes element e of lane (d row li, g) from key 16 s + 8 (e / 4) +
+  // 4 g + e % 4, the slot order of dS; lane (group G, a) of a read addresses key
+  // 16 s + 4 (G / 2) + a / 4 (+ 8 for elements 4..7) at column 32 dt + 16 (G % 2) +
+  // 4 (a % 4).
+  int tr_lo[G::kDTiles], tr_hi[G::kDTiles];
+  {
+    const int grp = lane / 16, a = lane % 16;
+    const int r_lo = 4 * (grp / 2) + a / 4, r_hi = r_lo + 8;
 #pragma unroll
-  for (int i = 0; i < kTLoads; ++i) {
-    const int pos = (wave * kTLoads + i) * 64 + lane, r = pos / ST::kChunks;
-    tsrc[i] = r * kTRow + (((pos % ST::kChunks) ^ ST::key(r)) << 4);
+    for (int dt = 0; dt < G::kDTiles; ++dt) {
+      const int col = 32 * dt + 16 * (grp % 2) + 4 * (a % 4);
+      tr_lo[dt] = r_lo * kKRow + ((((col >> 3) ^ SK::key(r_lo)) << 4) | ((col & 7) << 1));
+      tr_hi[dt] = r_hi * kKRow + ((((col >> 3) ^ SK::key(r_hi)) << 4) | ((col & 7) << 1));
+    }
   }
   const bool with_bias = p.bias != nullptr;
   auto visible = [&](int t) __attribute__((always_inline)) {
@@ -1690,13 +1744,10 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Para
   auto load = [&](int t, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
-      load_to_lds16(kbase + (int64_t)t * kKTile + ksrc[i], kbuf(buf) + (wave * kKLoads + i) * 1024);
-      load_to_lds16(vbase + (int64_t)t * kKTile + ksrc[i], vbuf(buf) + (wave * kKLoads + i) * 1024);
+      buffer_to_lds16(kres, t * kKTile + ksrc[i], kbuf(buf) + (wave * kKLoads + i) * 1024);
+      buffer_to_lds16(vres, t * kKTile + ksrc[i], vbuf(buf) + (wave * kKLoads + i) * 1024);
     }
-#pragma unroll
-    for (int i = 0; i < kTLoads; ++i)
-      load_to_lds16(tbase + (int64_t)t * kTTile + tsrc[i], tbuf(buf) + (wave * kTLoads + i) * 1024);
-    if (with_bias && wave == 0) load_to_lds4(p.bias + t * kKvBlock + lane, bbuf(buf));
+    if (with_bias && wave == 0) buffer_to_lds4(bres, (t * kKvBlock + lane) * 4, bbuf(buf));
   };
   auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -1706,7 +1757,6 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Para
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqacc[dt][r] = 0.0f;
   const int xk = SK::key(li);
-  const int xt = ST::key(li);
 
   auto step = [&](int it, auto cur_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
@@ -1717,7 +1767,6 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Para
       const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bbuf(cur)[lane] != 0.0f) != 0;
       const uint8_t* kl = kbuf(cur) + li * kKRow;
       const uint8_t* vl = vbuf(cur) + li * kKRow;
-      const uint8_t* tl = tbuf(cur) + li * kTRow;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // S^T and dP^T of the half's 32 keys
@@ -1730,27 +1779,32 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Para
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16_t{} : sacc, 0, 0, 0);
           pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e, df[s], s == 0 ? f32x16_t{} : pacc, 0, 0, 0);
         }
-        float bk[16];
-        if (has_bias) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 v = *reinterpret_cast<const float4*>(bbuf(cur) + slot_key(g, 16 * kb + 4 * q));
-            bk[4 * q] = v.x; bk[4 * q + 1] = v.y; bk[4 * q + 2] = v.z; bk[4 * q + 3] = v.w;
-          }
-        }
         uint32_t pw[8];
+        if (!diag && !has_bias) {
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          float ds2[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int jj = 2 * w + e, j = 16 * kb + jj;
-            const float x = has_bias ? fmaf(sacc[jj], c, bk[jj] * kLog2e) : sacc[jj] * c;
-            float pj = __builtin_amdgcn_exp2f(x - lse2);
-            if (diag && key0 + slot_key(g, j) > myrow) pj = 0.0f;
-            ds2[e] = pj * (pacc[jj] - drow);
+          for (int w = 0; w < 8; ++w) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * w], c, -lse2));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * w + 1], c, -lse2));
+            pw[w] = cast2_bf16(p0 * (pacc[2 * w] - drow), p1 * (pacc[2 * w + 1] - drow));
           }
-          pw[w] = cast2_bf16(ds2[0], ds2[1]);
+        } else {
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            // the bias of the pair's two keys (adjacent slots)
+            const float2 bk = has_bias ? *reinterpret_cast<const float2*>(bbuf(cur) + slot_key(g, 16 * kb + 2 * w))
+                                       : float2{0.0f, 0.0f};
+            float ds2[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int jj = 2 * w + e, j = 16 * kb + jj;
+              const float bj = e ? bk.y : bk.x;
+              const float x = has_bias ? fmaf(sacc[jj], c, bj * kLog2e) - lse2 : fmaf(sacc[jj], c, -lse2);
+              float pj = __builtin_amdgcn_exp2f(x);
+              if (diag && key0 + slot_key(g, j) > myrow) pj = 0.0f;
+              ds2[e] = pj * (pacc[jj] - drow);
+            }
+            pw[w] = cast2_bf16(ds2[0], ds2[1]);
+          }
         }
         // dQ^T += K^T dS^T over the half's two k-steps of 16 keys
 #pragma unroll
@@ -1758,7 +1812,8 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Para
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
             const int s = 2 * kb + s2;
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(tl + dt * 32 * kTRow + (((4 * g + s) ^ xt) << 4));
+            const uint8_t* t = kbuf(cur) + s * 16 * kKRow;
+            const bf16x8_t a = tr_frag(t + tr_lo[dt], t + tr_hi[dt]);
             const i32x4_t bw = {(int)pw[4 * s2], (int)pw[4 * s2 + 1], (int)pw[4 * s2 + 2], (int)pw[4 * s2 + 3]};
             dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bw), dqacc[dt], 0, 0, 0);
           }
@@ -1795,41 +1850,31 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Para
 // dK and dV: a workgroup of 4 waves takes 128 keys of one (b, kv head), a lane
 // one key, and walks the 64-row query blocks of every query head that reads the
 // kv head: S = Q K^T and dP = dO V^T (rows x keys: a lane holds its key's column),
-// P and dS in registers, dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T from
-// their slot-order copies.
+// P and dS in registers, dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
+// from the dO and Q tiles by transposing LDS reads.
 template <int D, bool kCausal>
 __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p) {
   using G = Geometry<D>;
   constexpr int kRow = D * 2;
-  constexpr int kTRow = kKvBlock * 2;
   constexpr int kTile = kKvBlock * kRow;
-  constexpr int kTTile = D * kTRow;
   using SR = Swizzle<kRow>;
-  using ST = Swizzle<kTRow>;
   constexpr int kLoads = kTile / (1024 * kWaves);
-  constexpr int kTLoads = kTTile / (1024 * kWaves);
-  static_assert(kTile % (1024 * kWaves) == 0 && kTTile % (1024 * kWaves) == 0, "staging split");
+  static_assert(kTile % (1024 * kWaves) == 0, "staging split");
   __shared__ __attribute__((aligned(16))) uint8_t lds_q0[kTile];
   __shared__ __attribute__((aligned(16))) uint8_t lds_q1[kTile];
   __shared__ __attribute__((aligned(16))) uint8_t lds_o0[kTile];
   __shared__ __attribute__((aligned(16))) uint8_t lds_o1[kTile];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_qt0[kTTile];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_qt1[kTTile];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_ot0[kTTile];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_ot1[kTTile];
   __shared__ __attribute__((aligned(16))) float lds_l0[kKvBlock];
   __shared__ __attribute__((aligned(16))) float lds_l1[kKvBlock];
   __shared__ __attribute__((aligned(16))) float lds_d0[kKvBlock];
   __shared__ __attribute__((aligned(16))) float lds_d1[kKvBlock];
   auto qbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_q1 : lds_q0; };
   auto obuf = [&](int i) __attribute__((always_inline)) { return i ? lds_o1 : lds_o0; };
-  auto qtbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_qt1 : lds_qt0; };
-  auto otbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_ot1 : lds_ot0; };
   auto lbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_l1 : lds_l0; };
   auto dbuf = [&](int i) __attribute__((always_inline)) { return i ? lds_d1 : lds_d0; };
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int g = lane / 32, li = lane % 32;
   const int n_kb = (p.N + kBlockRows - 1) / kBlockRows;
   // the forward's XCD-aware order over (b, kv head, key block): the key blocks of a kv
@@ -1861,16 +1906,28 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
     }
     if (p.bias) bkl = p.bias[mykey] * kLog2e;
   }
-  int rsrc[kLoads], tsrc[kTLoads];
+  int rsrc[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int pos = (wave * kLoads + i) * 64 + lane, r = pos / SR::kChunks;
     rsrc[i] = r * kRow + (((pos % SR::kChunks) ^ SR::key(r)) << 4);
   }
+  // Transposing reads of the Q and dO tiles for the A operands of dV^T += dO^T P and
+  // dK^T += Q^T dS: k-step st of tile dt takes element e of lane (d row li, g) from
+  // query row 16 st + 8 (e / 4) + 4 g + e % 4, the slot order of P and dS.  Lane
+  // (group G, a) of a read addresses row 16 st + 4 (G / 2) + a / 4 (+ 8 for elements
+  // 4..7) at column 32 dt + 16 (G % 2) + 4 (a % 4); the row's swizzle key does not
+  // depend on st.
+  int tr_lo[G::kDTiles], tr_hi[G::kDTiles];
+  {
+    const int grp = lane / 16, a = lane % 16;
+    const int r_lo = 4 * (grp / 2) + a / 4, r_hi = r_lo + 8;
 #pragma unroll
-  for (int i = 0; i < kTLoads; ++i) {
-    const int pos = (wave * kTLoads + i) * 64 + lane, r = pos / ST::kChunks;
-    tsrc[i] = r * kTRow + (((pos % ST::kChunks) ^ ST::key(r)) << 4);
+    for (int dt = 0; dt < G::kDTiles; ++dt) {
+      const int col = 32 * dt + 16 * (grp % 2) + 4 * (a % 4);
+      tr_lo[dt] = r_lo * kRow + ((((col >> 3) ^ SR::key(r_lo)) << 4) | ((col & 7) << 1));
+      tr_hi[dt] = r_hi * kRow + ((((col >> 3) ^ SR::key(r_hi)) << 4) | ((col & 7) << 1));
+    }
   }
   // iteration it: query head hk * Gq + it / n_r, row blocks from the last one down, so
   // that the workgroups of a kv head, whatever their first row block, read the same
@@ -1880,22 +1937,16 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
   auto load = [&](int it, int buf) __attribute__((always_inline)) {
     const int64_t hrow = ((int64_t)b * p.Hq + head_of(it)) * p.N;  // first row of the head
     const int r = rblk_of(it);
-    const uint8_t* qs = reinterpret_cast<const uint8_t*>(p.q + (hrow + (int64_t)r * kKvBlock) * D);
-    const uint8_t* os = reinterpret_cast<const uint8_t*>(p.dout + (hrow + (int64_t)r * kKvBlock) * D);
-    const int64_t tblk = hrow / kKvBlock + r;  // flat 64-row block of Q^T / dO^T
+    const __amdgpu_buffer_rsrc_t qs = buffer_rsrc(p.q + hrow * D), os = buffer_rsrc(p.dout + hrow * D);
+    const int toff = r * kTile;  // the block's byte offset within the head
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      load_to_lds16(qs + rsrc[i], qbuf(buf) + (wave * kLoads + i) * 1024);
-      load_to_lds16(os + rsrc[i], obuf(buf) + (wave * kLoads + i) * 1024);
-    }
-#pragma unroll
-    for (int i = 0; i < kTLoads; ++i) {
-      load_to_lds16(p.qt + tblk * kTTile + tsrc[i], qtbuf(buf) + (wave * kTLoads + i) * 1024);
-      load_to_lds16(p.dot + tblk * kTTile + tsrc[i], otbuf(buf) + (wave * kTLoads + i) * 1024);
+      buffer_to_lds16(qs, toff + rsrc[i], qbuf(buf) + (wave * kLoads + i) * 1024);
+      buffer_to_lds16(os, toff + rsrc[i], obuf(buf) + (wave * kLoads + i) * 1024);
     }
     if (wave == 0) {
-      load_to_lds4(p.lse_in + hrow + r * kKvBlock + lane, lbuf(buf));
-      load_to_lds4(p.dvec + hrow + r * kKvBlock + lane, dbuf(buf));
+      buffer_to_lds4(buffer_rsrc(p.lse_in + hrow), (r * kKvBlock + lane) * 4, lbuf(buf));
+      buffer_to_lds4(buffer_rsrc(p.dvec + hrow), (r * kKvBlock + lane) * 4, dbuf(buf));
     }
   };
   auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
@@ -1909,66 +1960,113 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
       dvacc[dt][r] = 0.0f;
     }
   const int xr = SR::key(li);
+  // One block of 64 query rows, in two 32-row halves hh: the S and dP products of
+  // half 0, then of half 1 while half 0's P and dS are formed, then half 0's dV and
+  // dK k-steps while half 1's are formed, then half 1's.  Each MFMA sits in a chunk
+  // of its own with the operand fragment of the MFMA kAhead later and a slice of
+  // the VALU work; sched_barrier fences keep the chunks in order.
+  auto block = [&](auto cur_c, auto diag_c, int rrow0) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr bool kDiag = decltype(diag_c)::value;
+    constexpr int kA = 2 * G::kQSteps;   // S and dP MFMAs of one half
+    constexpr int kC = 4 * G::kDTiles;   // dV and dK MFMAs of one half (two k-steps)
+    constexpr int kM = 2 * kA + 2 * kC;  // the block's MFMAs
+    constexpr int kAhead = 3, kRing = kAhead + 1;
+    const uint8_t* ql = qbuf(cur) + li * kRow;
+    const uint8_t* ol = obuf(cur) + li * kRow;
+    f32x16_t sacc[2], pacc[2];
+    uint32_t pp[2][8], ps[2][8];
+    bf16x8_t ring[kRing];
+    float2 lq2[2], dq2[2];
+    // MFMA i: i < 2 kA: half i / kA, k-step (i % kA) / 2, S (even) or dP (odd);
+    // then half hh = (i - 2 kA) / kC and q = (i - 2 kA) % kC: k-step 2 hh + q / (2 kDTiles),
+    // tile (q / 2) % kDTiles, dV (even) or dK (odd)
+    auto fetch = [&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < 2 * kA) {
+        constexpr int hh = i / kA, r = i % kA, st = r / 2;
+        const int off = hh * 32 * kRow + (((2 * st + g) ^ xr) << 4);
+        ring[i % kRing] = *reinterpret_cast<const bf16x8_t*>((r % 2 ? ol : ql) + off);
+      } else if constexpr (i < kM) {
+        constexpr int r = i - 2 * kA, hh = r / kC, q = r % kC, dt = (q / 2) % G::kDTiles;
+        constexpr int st = 2 * hh + q / (2 * G::kDTiles);
+        const uint8_t* t = (q % 2 ? qbuf(cur) : obuf(cur)) + st * 16 * kRow;
+        ring[i % kRing] = tr_frag(t + tr_lo[dt], t + tr_hi[dt]);
+      }
+    };
+    auto mfma = [&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      const bf16x8_t& a = ring[i % kRing];
+      if constexpr (i < 2 * kA) {
+        constexpr int hh = i / kA, r = i % kA, st = r / 2;
+        if constexpr (r % 2 == 0)
+          sacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[st], st == 0 ? f32x16_t{} : sacc[hh], 0, 0, 0);
+        else
+          pacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[st], st == 0 ? f32x16_t{} : pacc[hh], 0, 0, 0);
+      } else {
+        constexpr int r = i - 2 * kA, hh = r / kC, q = r % kC, s2 = q / (2 * G::kDTiles), dt = (q / 2) % G::kDTiles;
+        const uint32_t* src = q % 2 == 0 ? pp[hh] : ps[hh];
+        const i32x4_t bw = {(int)src[4 * s2], (int)src[4 * s2 + 1], (int)src[4 * s2 + 2], (int)src[4 * s2 + 3]};
+        if constexpr (q % 2 == 0)
+          dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bw), dvacc[dt], 0, 0, 0);
+        else
+          dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bw), dkacc[dt], 0, 0, 0);
+      }
+    };
+    // lse and D of rows 2w, 2w + 1 of half hh (adjacent slots) for unit n = 8 hh + w,
+    // read one unit ahead
+    auto rowstats = [&](auto nc) __attribute__((always_inline)) {
+      constexpr int n = decltype(nc)::value;
+      if constexpr (n < 16) {
+        const int k = slot_key(g, 2 * n);
+        lq2[n % 2] = *reinterpret_cast<const float2*>(lbuf(cur) + k);
+        dq2[n % 2] = *reinterpret_cast<const float2*>(dbuf(cur) + k);
+      }
+    };
+    auto unit = [&](auto nc) __attribute__((always_inline)) {  // P and dS of rows 2w, 2w + 1
+      constexpr int n = decltype(nc)::value, hh = n / 8, w = n % 8;
+      const float2 lr = lq2[n % 2], dr = dq2[n % 2];
+      rowstats(IC<n + 1>{});
+      float pj0 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][2 * w], c, bkl) - lr.x * kLog2e);
+      float pj1 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][2 * w + 1], c, bkl) - lr.y * kLog2e);
+      if constexpr (kDiag) {
+        if (rrow0 + slot_key(g, 16 * hh + 2 * w) < mykey) pj0 = 0.0f;
+        if (rrow0 + slot_key(g, 16 * hh + 2 * w + 1) < mykey) pj1 = 0.0f;
+      }
+      pp[hh][w] = cast2_bf16(pj0, pj1);
+      ps[hh][w] = cast2_bf16(pj0 * (pacc[hh][2 * w] - dr.x), pj1 * (pacc[hh][2 * w + 1] - dr.y));
+    };
+#define PCAST_FENCE __builtin_amdgcn_sched_barrier(0)
+    static_for<kAhead>([&](auto ic) __attribute__((always_inline)) { fetch(ic); });
+    rowstats(IC<0>{});
+    PCAST_FENCE;
+    static_for<kM>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      mfma(ic);
+      fetch(IC<i + kAhead>{});
+      // half 0's units over the S / dP MFMAs of half 1, half 1's over the dV / dK
+      // MFMAs of half 0
+      if constexpr (i >= kA && i < 2 * kA) {
+        constexpr int c0 = i - kA, u0 = c0 * 8 / kA, u1 = (c0 + 1) * 8 / kA;
+        static_for<u1 - u0>([&](auto uc) __attribute__((always_inline)) { unit(IC<u0 + decltype(uc)::value>{}); });
+      } else if constexpr (i >= 2 * kA && i < 2 * kA + kC) {
+        constexpr int c0 = i - 2 * kA, u0 = c0 * 8 / kC, u1 = (c0 + 1) * 8 / kC;
+        static_for<u1 - u0>([&](auto uc) __attribute__((always_inline)) { unit(IC<8 + u0 + decltype(uc)::value>{}); });
+      }
+      PCAST_FENCE;
+    });
+#undef PCAST_FENCE
+  };
 
   auto step = [&](int it, auto cur_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
     if (it + 1 < n_it) load(it + 1, nxt);
     const int rrow0 = rblk_of(it) * kKvBlock;
     if (wave_active && (!kCausal || rrow0 + kKvBlock - 1 >= wkey0)) {
-      // S = Q K^T and dP = dO V^T, two 32-row halves each (rows in slots, keys in lanes)
-      f32x16_t sacc[2], pacc[2];
-      const uint8_t* ql = qbuf(cur) + li * kRow;
-      const uint8_t* ol = obuf(cur) + li * kRow;
-#pragma unroll
-      for (int s = 0; s < G::kQSteps; ++s)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int off = hh * 32 * kRow + (((2 * s + g) ^ xr) << 4);
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ql + off);
-          const bf16x8_t e = *reinterpret_cast<const bf16x8_t*>(ol + off);
-          sacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[s], s == 0 ? f32x16_t{} : sacc[hh], 0, 0, 0);
-          pacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e, vf[s], s == 0 ? f32x16_t{} : pacc[hh], 0, 0, 0);
-        }
-      const bool diag = kCausal && (rrow0 < wkey0 + kRowsPerWave - 1);
-      float lq[32], dq4[32];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float4 a = *reinterpret_cast<const float4*>(lbuf(cur) + slot_key(g, 4 * q));
-        const float4 e = *reinterpret_cast<const float4*>(dbuf(cur) + slot_key(g, 4 * q));
-        lq[4 * q] = a.x; lq[4 * q + 1] = a.y; lq[4 * q + 2] = a.z; lq[4 * q + 3] = a.w;
-        dq4[4 * q] = e.x; dq4[4 * q + 1] = e.y; dq4[4 * q + 2] = e.z; dq4[4 * q + 3] = e.w;
-      }
-      uint32_t pp[16], ps[16];
-#pragma unroll
-      for (int w = 0; w < 16; ++w) {
-        float p2[2], d2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int j = 2 * w + e;
-          float pj = __builtin_amdgcn_exp2f(fmaf(sacc[j / 16][j % 16], c, bkl) - lq[j] * kLog2e);
-          if (diag && rrow0 + slot_key(g, j) < mykey) pj = 0.0f;
-          p2[e] = pj;
-          d2[e] = pj * (pacc[j / 16][j % 16] - dq4[j]);
-        }
-        pp[w] = cast2_bf16(p2[0], p2[1]);
-        ps[w] = cast2_bf16(d2[0], d2[1]);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS: four k-steps of 16 rows per 32-column tile
-      const uint8_t* otl = otbuf(cur) + li * kTRow;
-      const uint8_t* qtl = qtbuf(cur) + li * kTRow;
-      const int xt = ST::key(li);
-#pragma unroll
-      for (int dt = 0; dt < G::kDTiles; ++dt)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int off = dt * 32 * kTRow + (((4 * g + s) ^ xt) << 4);
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(otl + off);
-          const bf16x8_t e = *reinterpret_cast<const bf16x8_t*>(qtl + off);
-          const i32x4_t bp = {(int)pp[4 * s], (int)pp[4 * s + 1], (int)pp[4 * s + 2], (int)pp[4 * s + 3]};
-          const i32x4_t bs = {(int)ps[4 * s], (int)ps[4 * s + 1], (int)ps[4 * s + 2], (int)ps[4 * s + 3]};
-          dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bp), dvacc[dt], 0, 0, 0);
-          dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e, __builtin_bit_cast(bf16x8_t, bs), dkacc[dt], 0, 0, 0);
-        }
+      if (kCausal && rrow0 < wkey0 + kRowsPerWave - 1)
+        block(cur_c, std::true_type{}, rrow0);
+      else
+        block(cur_c, std::false_type{}, rrow0);
     }
     wait_loads();
     __syncthreads();
@@ -2098,16 +2196,13 @@ bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(pt
 // Workspace of the backward: slot-order transposes of K, Q and dO (bf16, the
 // layout pcast_prep_v writes for V), then the row dots D (fp32); 256-aligned parts.
 struct BwdLayout {
-  size_t kt, qt, dot, dvec, total;
+  size_t dvec, total;
 };
-BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int d) {
+BwdLayout bwd_layout(int B, int Hq, int /*Hkv*/, int N, int /*d*/) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   BwdLayout l;
-  l.kt = 0;
-  l.qt = up((size_t)B * Hkv * N * d * 2);
-  l.dot = up(l.qt + (size_t)B * Hq * N * d * 2);
-  l.dvec = up(l.dot + (size_t)B * Hq * N * d * 2);
-  l.total = up(l.dvec + (size_t)B * Hq * N * 4);
+  l.dvec = 0;
+  l.total = up((size_t)B * Hq * N * 4);
   return l;
 }
 
@@ -2405,23 +2500,15 @@ int attn_bwd_pcast(const void* Q, const void* K, const void* V, const float* O, 
   uint8_t* base = static_cast<uint8_t*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t rows = (int64_t)B * Hq * N;
-  const int64_t qblk = (int64_t)B * Hq * (N / kKvBlock), kblk = (int64_t)B * Hkv * (N / kKvBlock);
   const uint16_t* Qb = static_cast<const uint16_t*>(Q);
   const uint16_t* Kb = static_cast<const uint16_t*>(K);
   const uint16_t* dOb = static_cast<const uint16_t*>(dO);
-  if (d == 64) {
-    launch_prep<64, false>(Kb, base + l.kt, kblk, st);
-    launch_prep<64, false>(Qb, base + l.qt, qblk, st);
-    launch_prep<64, false>(dOb, base + l.dot, qblk, st);
+  if (d == 64)
     hipLaunchKernelGGL(pcast_bwd_rowdot<64>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, st, dOb, O,
                        reinterpret_cast<float*>(base + l.dvec), rows);
-  } else {
-    launch_prep<128, false>(Kb, base + l.kt, kblk, st);
-    launch_prep<128, false>(Qb, base + l.qt, qblk, st);
-    launch_prep<128, false>(dOb, base + l.dot, qblk, st);
+  else
     hipLaunchKernelGGL(pcast_bwd_rowdot<128>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, st, dOb, O,
                        reinterpret_cast<float*>(base + l.dvec), rows);
-  }
   Params p{};
   p.q = Qb;
   p.k = Kb;
@@ -2429,9 +2516,6 @@ int attn_bwd_pcast(const void* Q, const void* K, const void* V, const float* O, 
   p.dout = dOb;
   p.lse_in = lse;
   p.dvec = reinterpret_cast<const float*>(base + l.dvec);
-  p.kt = base + l.kt;
-  p.qt = base + l.qt;
-  p.dot = base + l.dot;
   p.bias = bias;
   p.dq = dQ;
   p.dk = dK;
