@@ -98,6 +98,20 @@ struct Swizzle {
   __device__ static int key(int row) { return (row / kRowsPerWindow) % kChunks; }
 };
 
+// The backward's row-major tiles use another key: 16 consecutive rows take distinct
+// keys (row reads of one 16-byte chunk per lane stay conflict-free), and 4
+// consecutive rows fall in 4 different 64-byte windows of the 256-byte bank row
+// (the transposing reads take 4 rows x 64 bytes per half wave).
+template <int kRowBytes>
+struct SwizzleT {
+  static_assert(kRowBytes == 256 || kRowBytes == 128, "d = 128 or 64");
+  static constexpr int kChunks = kRowBytes / 16;
+  __device__ static int key(int row) {
+    if constexpr (kChunks == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Pre-pass: V (bf16, [B][Hkv][N][D]) -> operand copy [B][Hkv][N/64][D][64]
 // in slot order, E4M3 (RNE, saturating) or bf16.
@@ -1669,7 +1683,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Para
   using G = Geometry<D>;
   constexpr int kKRow = D * 2;
   constexpr int kKTile = kKvBlock * kKRow;
-  using SK = Swizzle<kKRow>;
+  using SK = SwizzleT<kKRow>;
   constexpr int kKLoads = kKTile / (1024 * kDqWaves);
   static_assert(kKTile % (1024 * kDqWaves) == 0, "staging split");
   __shared__ __attribute__((aligned(16))) uint8_t lds_k0[kKTile];
@@ -1857,7 +1871,7 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
   using G = Geometry<D>;
   constexpr int kRow = D * 2;
   constexpr int kTile = kKvBlock * kRow;
-  using SR = Swizzle<kRow>;
+  using SR = SwizzleT<kRow>;
   constexpr int kLoads = kTile / (1024 * kWaves);
   static_assert(kTile % (1024 * kWaves) == 0, "staging split");
   __shared__ __attribute__((aligned(16))) uint8_t lds_q0[kTile];
