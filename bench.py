@@ -153,7 +153,7 @@ def bench_backward(sna, torch, np, synthetic, w, q, k, v, ws, bias_t, dev, strea
     return {"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal, sink bias 7 on keys 0..3, "
                         f"gradients of the S={S:g} {'reverse' if order else 'forward'} forward",
             "ms_per_call": round(ms, 5), "steps": steps,
-            "kernels": "3 x pcast_prep_v (bf16 transposes) + pcast_bwd_rowdot + pcast_attn_bwd_dq + pcast_attn_bwd_dkv",
+            "kernels": "pcast_bwd_rowdot + pcast_attn_bwd_dq + pcast_attn_bwd_dkv",
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_BF16, 4), "algorithmic_flops": flops,
                          "flops_rule": "2.5 x the forward's 2*B*H*N^2*d (causal)"}}
