@@ -180,7 +180,8 @@ double pcast_lost_mass_model(double delta, double S, int k);
  *          aligned, owned by the caller (the row dots D = dO . O, fp32 [B][Hq][N]).
  * All products run on bf16 matrix cores with fp32 accumulation; P and dS are
  * rounded to bf16 where they are operands.  Allocates nothing; errors as for
- * attn_fwd_pcast.
+ * attn_fwd_pcast, plus PCAST_ENOTSUP when one head's rows (N * d * 2 bytes)
+ * reach 2 GiB.
  */
 size_t pcast_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 

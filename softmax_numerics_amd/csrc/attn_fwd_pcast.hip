@@ -2508,6 +2508,8 @@ int attn_bwd_pcast(const void* Q, const void* K, const void* V, const float* O, 
   int rc = check_shape(B, Hq, Hkv, N, d, 1.0f);
   if (rc != PCAST_OK) return rc;
   if ((int64_t)B * Hkv * ((N + kBlockRows - 1) / kBlockRows) > (int64_t)INT32_MAX) return fail(PCAST_ENOTSUP, "grid too large");
+  if ((int64_t)N * d * 2 > (int64_t)INT32_MAX)
+    return fail(PCAST_ENOTSUP, "N = %d, d = %d: the backward addresses one head's rows with 32-bit byte offsets", N, d);
   if ((rc = check_device()) != PCAST_OK) return rc;
 
   const BwdLayout l = bwd_layout(B, Hq, Hkv, N, d);

@@ -204,6 +204,7 @@ def test_bwd_workspace_layout(lib):
     (dict(Hq=3, Hkv=2), sna.PCAST_EINVAL),
     (dict(N=96), sna.PCAST_ENOTSUP),
     (dict(d=96), sna.PCAST_ENOTSUP),
+    (dict(N=1 << 23), sna.PCAST_ENOTSUP),  # one head's rows reach 2 GiB
 ])
 def test_bwd_argument_errors(lib, kw, code):
     a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, lse=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128,
