@@ -87,6 +87,16 @@ def test_small(sna, d, causal):
     _case(sna, "small", 2, 4, 2, 320, d, causal, synthetic.sink_bias(320, 7.0), 111)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", [
+    (2, 4, 1, 64, 64, True),      # one key block: most waves of both kernels idle
+    (1, 8, 1, 192, 64, False),    # eight query heads per kv head, a partial 256-row block
+    (1, 2, 2, 448, 128, True),    # seven key blocks, diagonal blocks at both parities
+    (1, 16, 2, 384, 128, False),  # the dK/dV walk over eight query heads
+])
+def test_shapes(sna, B, Hq, Hkv, N, d, causal):
+    _case(sna, "shape", B, Hq, Hkv, N, d, causal, synthetic.sink_bias(N, 7.0), 116 + N + d)
+
+
 @pytest.mark.parametrize("bias_kind", ["none", "random"])
 def test_bias_kinds(sna, bias_kind):
     bias = None if bias_kind == "none" else synthetic.random_bias(256, 112)
