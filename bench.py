@@ -17,8 +17,9 @@ forward.  The "qk_fp8" object times the variant with FP8 logits
 MSE against the same fp64 attention of the unquantised Q and K.  The "decode"
 object times attn_decode_pcast (split KV) on the decode workload (16 sequences of
 16384 cached keys, one new token each, GQA 32/8) against the HBM roofline; its V
-copy is prepared once, outside the timed calls, as a cache would be.  The
-"backward" object times attn_bwd_pcast on the same workload (its pre-passes
+copy is prepared once, outside the timed calls, as a cache would be; its "qk_fp8"
+object times attn_decode_pcast_qk8 on an FP8 K cache prepared the same way.  The
+"backward" object times attn_bwd_pcast on the same workload (its row-dot pre-pass
 included), with the forward's O and lse as inputs.
 """
 from __future__ import annotations
@@ -195,13 +196,41 @@ def bench_decode(sna, torch, np, synthetic, dev, stream, steps, warmup):
     ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     gbs = w.bytes / (ms * 1e-3) / 1e9
     print(f"[bench] decode {w.name}: {ms:.4f} ms per call ({gbs:.0f} GB/s)", file=sys.stderr, flush=True)
+
+    # the same decode with FP8 logits (K as E4M3 codes from pcast_prepare_qk8)
+    ws8 = torch.empty(sna.workspace_bytes_qk8(w.B, w.Hkv, w.Nk, w.d), dtype=torch.uint8, device=dev)
+    rc = sna.prepare_qk8(k.data_ptr(), v.data_ptr(), w.B, w.Hkv, w.Nk, w.d, ws8.data_ptr(), sh)
+    if rc != sna.PCAST_OK:
+        raise sna.PcastError(rc, sna.strerror(rc))
+
+    def call8():
+        r = sna.attn_decode_pcast_qk8(q.data_ptr(), ws8.data_ptr(), bias.data_ptr(), w.B, w.Hq, w.Hkv, w.Nq, w.Nk,
+                                      w.d, S, order, w.split_keys, out.data_ptr(), st.data_ptr(), ws.data_ptr(), sh)
+        if r != sna.PCAST_OK:
+            raise sna.PcastError(r, sna.strerror(r))
+
+    for _ in range(warmup):
+        call8()
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        call8()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms8 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    gbs8 = w.bytes_qk8 / (ms8 * 1e-3) / 1e9
+    print(f"[bench] decode {w.name}, FP8 logits: {ms8:.4f} ms per call ({gbs8:.0f} GB/s)", file=sys.stderr,
+          flush=True)
     return {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} d={w.d}, "
                         f"split_keys={w.split_keys}, sink bias {delta} on keys 0..3, S={S:g}, "
                         f"{'reverse' if order else 'forward'} order, counters on",
             "ms_per_call": round(ms, 5), "kernels": "pcast_decode_split + pcast_decode_merge",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
                          "frac": round(gbs / 8000.0, 4), "algorithmic_bytes": w.bytes},
-            "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
+            "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2),
+            "qk_fp8": {"ms_per_call": round(ms8, 5), "kernels": "attn_decode_pcast_qk8 (K pre-pass not timed)",
+                       "roofline": {"bound": "hbm", "achieved": round(gbs8, 1), "peak": 8000.0, "unit": "GB/s",
+                                    "frac": round(gbs8 / 8000.0, 4), "algorithmic_bytes": w.bytes_qk8}}}
 
 
 def main() -> int:

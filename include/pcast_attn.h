@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define PCAST_ABI_VERSION 7
+#define PCAST_ABI_VERSION 8
 
 /* Keys per KV block.  The block size is part of the numerics (the running
  * max is updated once per block), so it is fixed. */
@@ -274,6 +274,24 @@ int attn_fwd_pcast_qk8_prepared(const void* Q, const void* workspace, const floa
 int attn_fwd_pcast_qk8(const void* Q, const void* K, const void* V, const float* bias, int B, int Hq,
                        int Hkv, int N, int d, int causal, float S, int order, float* out,
                        unsigned long long* stats, void* stream);
+
+/*
+ * attn_decode_pcast_qk8 -- the split-KV decode of attn_decode_pcast with FP8
+ * logits, as the forward above: each query row of Q rounded to E4M3 with its
+ * own power-of-two scale inside the kernel, K read as the E4M3 codes and
+ * per-64-key-block exponents of a workspace that pcast_prepare_qk8(K, V, B,
+ * Hkv, Nk, d, ...) filled (its V operand copy serves the P.V product), so a
+ * decode step reads one byte per element of K instead of two.
+ *
+ * qk8_workspace  device, pcast_workspace_bytes_qk8(B, Hkv, Nk, d) bytes,
+ *        16-byte aligned, filled by pcast_prepare_qk8 with the same B, Hkv,
+ *        Nk, d (stream order, or other synchronisation, must complete it first).
+ * Every other argument, the results and the errors as for attn_decode_pcast.
+ * Allocates nothing.
+ */
+int attn_decode_pcast_qk8(const void* Q, const void* qk8_workspace, const float* bias, int B, int Hq, int Hkv,
+                          int Nq, int Nk, int d, float S, int order, int split_keys, float* out,
+                          unsigned long long* stats, void* workspace, void* stream);
 
 /*
  * The FP8-logit forward with a random rotation of Q and K before the rounding

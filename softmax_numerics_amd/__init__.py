@@ -25,7 +25,8 @@ EXPORTS = ("attn_fwd_pcast", "pcast_prepare_v", "attn_fwd_pcast_prepared", "pcas
            "attn_fwd_pcast_rows", "pcast_sink_max_mean", "pcast_delta_critical",
            "pcast_underflow_model", "pcast_lost_mass_model", "attn_decode_pcast",
            "pcast_decode_workspace_bytes", "attn_bwd_pcast", "pcast_bwd_workspace_bytes",
-           "pcast_workspace_bytes_qk8_rot", "pcast_prepare_qk8_rot", "attn_fwd_pcast_qk8_rot_prepared")
+           "pcast_workspace_bytes_qk8_rot", "pcast_prepare_qk8_rot", "attn_fwd_pcast_qk8_rot_prepared",
+           "attn_decode_pcast_qk8")
 
 _lock = threading.Lock()
 _lib = None
@@ -75,6 +76,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_fwd_pcast_rows.restype = I
             lib.attn_decode_pcast.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I, I, P, P, P, P]
             lib.attn_decode_pcast.restype = I
+            lib.attn_decode_pcast_qk8.argtypes = [P, P, P, I, I, I, I, I, I, ctypes.c_float, I, I, P, P, P, P]
+            lib.attn_decode_pcast_qk8.restype = I
             lib.pcast_decode_workspace_bytes.argtypes = [I, I, I, I, I]
             lib.pcast_decode_workspace_bytes.restype = ctypes.c_size_t
             lib.attn_bwd_pcast.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P]
@@ -155,6 +158,14 @@ def attn_decode_pcast(Q, K, vop, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_ke
     """Raw attn_decode_pcast with integer device addresses (0 for NULL); returns the C return code."""
     return int(load_library().attn_decode_pcast(
         Q, K, vop, bias or None, B, Hq, Hkv, Nq, Nk, d, float(S), int(order), int(split_keys), out,
+        stats or None, workspace, stream or None))
+
+
+def attn_decode_pcast_qk8(Q, qk8_workspace, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out, stats,
+                          workspace, stream) -> int:
+    """Raw attn_decode_pcast_qk8 with integer device addresses (0 for NULL); returns the C return code."""
+    return int(load_library().attn_decode_pcast_qk8(
+        Q, qk8_workspace, bias or None, B, Hq, Hkv, Nq, Nk, d, float(S), int(order), int(split_keys), out,
         stats or None, workspace, stream or None))
 
 

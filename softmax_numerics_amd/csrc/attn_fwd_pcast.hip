@@ -1353,11 +1353,15 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
 // their common max and adds them.  Rows sit at the last Nq positions: row i sees
 // keys j <= Nk - Nq + i.
 // ---------------------------------------------------------------------------
-template <int D, int kMode, bool kStats>
+template <int D, int kMode, bool kStats, bool kQ8>
 __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
   static_assert(kMode != kBf16, "FP8 modes only");
   using G = Geometry<D>;
-  constexpr int kKRow = D * 2;
+  // kQ8: Q rounded here per row and K read as E4M3 codes with one scale per key block
+  // (pcast_prepare_qk8's layout); the logits then run on the FP8 matrix cores
+  constexpr int kKRow = kQ8 ? D : D * 2;
+  constexpr int kSSteps = kQ8 ? D / 64 : G::kQSteps;  // logit MFMA k-steps per 32-key half
+  using KFrag = typename Select<kQ8, i32x8_t, bf16x8_t>::type;
   constexpr int kVRow = kKvBlock;
   constexpr int kKTile = kKvBlock * kKRow;
   constexpr int kVTile = D * kVRow;
@@ -1389,19 +1393,47 @@ __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
   const int t_first = split * p.split_blocks;
   const int t_end = min(t_first + p.split_blocks, n_blk);
   const int n_it = t_end - t_first;
-  const float c = p.logit_scale;
   const bool with_bias = p.bias != nullptr;
 
-  bf16x8_t qf[G::kQSteps];
-  {
+  // Q operand as in the forward: bf16 Q[row][s*16 + g*8 .. +8), or the E4M3 codes of
+  // Q[row][s*64 + g*32 .. +32) * 2^-e_row with the row's scale (padding rows are 0)
+  KFrag qf[kSSteps];
+  float c_row = p.logit_scale;  // log2(e)/sqrt(d), times 2^e_row with FP8 logits
+  if constexpr (kQ8) {
+    const uint16_t* qrow = p.q + (((int64_t)b * p.Hq + h) * p.Nq + qi) * D + g * 32;
+    i32x4_t w[kSSteps][4];
+    uint32_t m = 0;
+#pragma unroll
+    for (int s = 0; s < kSSteps; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const i32x4_t z = {};
+        w[s][t] = row_ok ? *reinterpret_cast<const i32x4_t*>(qrow + s * 64 + t * 8) : z;
+        m = max(m, absmax8(w[s][t]));
+      }
+    m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+    const int e = scale_exp(m);
+#pragma unroll
+    for (int s = 0; s < kSSteps; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        int lo, hi;
+        codes8(w[s][t], e, lo, hi);
+        qf[s][2 * t] = lo;
+        qf[s][2 * t + 1] = hi;
+      }
+    c_row = ldexpf(p.logit_scale, e);
+  } else {
     const uint16_t* qrow = p.q + (((int64_t)b * p.Hq + h) * p.Nq + qi) * D + g * 8;
 #pragma unroll
-    for (int s = 0; s < G::kQSteps; ++s) {
+    for (int s = 0; s < kSSteps; ++s) {
       bf16x8_t z = {};
       qf[s] = row_ok ? *reinterpret_cast<const bf16x8_t*>(qrow + s * 16) : z;
     }
   }
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k + ((int64_t)b * p.Hkv + hk) * p.Nk * D);
+  const uint8_t* kbase = kQ8 ? p.k8 + ((int64_t)b * p.Hkv + hk) * p.Nk * D
+                             : reinterpret_cast<const uint8_t*>(p.k + ((int64_t)b * p.Hkv + hk) * p.Nk * D);
+  const int* kexp_head = kQ8 ? p.kexp + ((int64_t)b * p.Hkv + hk) * n_blk : nullptr;
   const uint8_t* vbase = static_cast<const uint8_t*>(p.vop) + ((int64_t)b * p.Hkv + hk) * (int64_t)n_blk * kVTile;
   auto tile_of = [&](int it) __attribute__((always_inline)) { return p.order ? (t_end - 1 - it) : (t_first + it); };
   // load i fills LDS chunk position i * 64 + lane, which holds logical chunk position ^ key(row)
@@ -1430,11 +1462,20 @@ __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
   auto issue_s = [&](f32x16_t(&sa)[2]) __attribute__((always_inline)) {
     const uint8_t* kl = lds_k + li * kKRow;
 #pragma unroll
-    for (int s = 0; s < G::kQSteps; ++s)
+    for (int s = 0; s < kSSteps; ++s)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + kb * 32 * kKRow + (((2 * s + g) ^ xk) << 4));
-        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16_t{} : sa[kb], 0, 0, 0);
+        const uint8_t* kr = kl + kb * 32 * kKRow;
+        if constexpr (kQ8) {
+          const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kr + (((4 * s + 2 * g) ^ xk) << 4));
+          const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(kr + (((4 * s + 2 * g + 1) ^ xk) << 4));
+          const i32x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          sa[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[s], s == 0 ? f32x16_t{} : sa[kb], 0, 0, 0, 0,
+                                                                   0, 0);
+        } else {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kr + (((2 * s + g) ^ xk) << 4));
+          sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16_t{} : sa[kb], 0, 0, 0);
+        }
       }
   };
   f32x16_t oacc[G::kDTiles];
@@ -1463,6 +1504,8 @@ __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
   auto step = [&](int it, auto cur_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
     const int t = tile_of(it);
+    // the logit scale of this block: times 2^e_block of K's scale with FP8 logits
+    const float c = kQ8 ? ldexpf(c_row, kexp_head[t]) : c_row;
     if (it + 1 < n_it) {
       load_v(tile_of(it + 1), nxt);
       load_b(tile_of(it + 1), nxt);
@@ -2423,6 +2466,85 @@ int enqueue_attn(const void* Q, const void* K, const void* ws, const float* bias
   return e == hipSuccess ? PCAST_OK : hip_fail(e, "attention kernel launch");
 }
 
+// Argument checks shared by the decode entry points (Q, out, workspace; shapes).
+int check_decode(const void* Q, const float* bias, int B, int Hq, int Hkv, int Nq, int Nk, int d, float S,
+                 int order, int split_keys, const float* out, const unsigned long long* stats,
+                 const void* workspace) {
+  if (!aligned(Q, 16) || !aligned(out, 16) || !aligned(workspace, 16))
+    return fail(PCAST_EINVAL, "Q, out and workspace must be 16-byte aligned");
+  if (bias && !aligned(bias, 4)) return fail(PCAST_EINVAL, "bias must be 4-byte aligned");
+  if (stats && !aligned(stats, 8)) return fail(PCAST_EINVAL, "stats must be 8-byte aligned");
+  if (order != PCAST_ORDER_FORWARD && order != PCAST_ORDER_REVERSE)
+    return fail(PCAST_EINVAL, "order must be 0 (forward) or 1 (reverse)");
+  if (Nq <= 0) return fail(PCAST_EINVAL, "Nq must be positive");
+  if (split_keys <= 0 || split_keys % kKvBlock != 0)
+    return fail(PCAST_EINVAL, "split_keys must be a positive multiple of %d", kKvBlock);
+  int rc = check_shape(B, Hq, Hkv, Nk, d, S);
+  if (rc != PCAST_OK) return rc;
+  if (S == 0.0f) return fail(PCAST_ENOTSUP, "decode needs S > 0 (the FP8 P.V path)");
+  if ((int64_t)(Hq / Hkv) * Nq > 32)
+    return fail(PCAST_ENOTSUP, "(Hq / Hkv) * Nq = %lld: at most 32 rows per kv head", (long long)(Hq / Hkv) * Nq);
+  const DecodeLayout l = decode_layout(B, Hkv, Nk, d, split_keys);
+  if ((int64_t)B * Hkv * l.n_split > (int64_t)INT32_MAX) return fail(PCAST_ENOTSUP, "grid too large");
+  return check_device();
+}
+
+// The decode's two kernels; K as bf16 (K) or as E4M3 codes with block exponents (k8, kexp).
+int enqueue_decode(const void* Q, const void* K, const void* vop, const uint8_t* k8, const int* kexp,
+                   const float* bias, int B, int Hq, int Hkv, int Nq, int Nk, int d, float S, int order,
+                   int split_keys, float* out, unsigned long long* stats, void* workspace, hipStream_t st) {
+  const DecodeLayout l = decode_layout(B, Hkv, Nk, d, split_keys);
+  Params p{};
+  p.q = static_cast<const uint16_t*>(Q);
+  p.k = static_cast<const uint16_t*>(K);
+  p.k8 = k8;
+  p.kexp = kexp;
+  p.vop = vop;
+  p.bias = bias;
+  p.out = out;
+  p.stats = stats;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = Nk;
+  p.order = order;
+  p.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)d));
+  p.S = S;
+  p.inv_S = 1.0f / S;
+  p.p_clamp = 448.0f / S;
+  p.Nq = Nq; p.Nk = Nk; p.n_split = l.n_split; p.split_blocks = split_keys / kKvBlock;
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  p.part_a = reinterpret_cast<float*>(base + l.a);
+  p.part_ml = reinterpret_cast<float*>(base + l.ml);
+  p.part_cnt = reinterpret_cast<unsigned int*>(base + l.cnt);
+  const int mode = (is_pow2(S) ? kPow2 : kMul) + (S > 448.0f ? 1 : 0);
+  const bool qk8 = k8 != nullptr;
+  const dim3 grid((unsigned)(B * Hkv * l.n_split)), mgrid((unsigned)(B * Hkv));
+#define PCAST_DECODE(DD, MM, Q8)                                                                    \
+  do {                                                                                              \
+    if (stats) {                                                                                    \
+      hipLaunchKernelGGL((pcast_decode_split<DD, MM, true, Q8>), grid, dim3(64), 0, st, p);         \
+      hipLaunchKernelGGL((pcast_decode_merge<DD, true>), mgrid, dim3(256), 0, st, p);               \
+    } else {                                                                                        \
+      hipLaunchKernelGGL((pcast_decode_split<DD, MM, false, Q8>), grid, dim3(64), 0, st, p);        \
+      hipLaunchKernelGGL((pcast_decode_merge<DD, false>), mgrid, dim3(256), 0, st, p);              \
+    }                                                                                               \
+  } while (0)
+#define PCAST_DECODE_MODES(DD, Q8)                              \
+  switch (mode) {                                               \
+    case kPow2: PCAST_DECODE(DD, kPow2, Q8); break;             \
+    case kPow2Clamp: PCAST_DECODE(DD, kPow2Clamp, Q8); break;   \
+    case kMul: PCAST_DECODE(DD, kMul, Q8); break;               \
+    default: PCAST_DECODE(DD, kMulClamp, Q8); break;            \
+  }
+  if (d == 64) {
+    if (qk8) PCAST_DECODE_MODES(64, true) else PCAST_DECODE_MODES(64, false)
+  } else {
+    if (qk8) PCAST_DECODE_MODES(128, true) else PCAST_DECODE_MODES(128, false)
+  }
+#undef PCAST_DECODE_MODES
+#undef PCAST_DECODE
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PCAST_OK : hip_fail(e, "decode kernel launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -2567,73 +2689,29 @@ int attn_decode_pcast(const void* Q, const void* K, const void* vop, const float
   g_last_error[0] = '\0';
   if (!Q || !K || !vop || !out || !workspace)
     return fail(PCAST_EINVAL, "Q, K, vop, out and workspace must be non-null");
-  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(vop, 16) || !aligned(out, 16) || !aligned(workspace, 16))
+  if (!aligned(K, 16) || !aligned(vop, 16))
     return fail(PCAST_EINVAL, "Q, K, vop, out and workspace must be 16-byte aligned");
-  if (bias && !aligned(bias, 4)) return fail(PCAST_EINVAL, "bias must be 4-byte aligned");
-  if (stats && !aligned(stats, 8)) return fail(PCAST_EINVAL, "stats must be 8-byte aligned");
-  if (order != PCAST_ORDER_FORWARD && order != PCAST_ORDER_REVERSE)
-    return fail(PCAST_EINVAL, "order must be 0 (forward) or 1 (reverse)");
-  if (Nq <= 0) return fail(PCAST_EINVAL, "Nq must be positive");
-  if (split_keys <= 0 || split_keys % kKvBlock != 0)
-    return fail(PCAST_EINVAL, "split_keys must be a positive multiple of %d", kKvBlock);
-  int rc = check_shape(B, Hq, Hkv, Nk, d, S);
+  const int rc = check_decode(Q, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out, stats, workspace);
   if (rc != PCAST_OK) return rc;
-  if (S == 0.0f) return fail(PCAST_ENOTSUP, "decode needs S > 0 (the FP8 P.V path)");
-  if ((int64_t)(Hq / Hkv) * Nq > 32)
-    return fail(PCAST_ENOTSUP, "(Hq / Hkv) * Nq = %lld: at most 32 rows per kv head", (long long)(Hq / Hkv) * Nq);
-  const DecodeLayout l = decode_layout(B, Hkv, Nk, d, split_keys);
-  if ((int64_t)B * Hkv * l.n_split > (int64_t)INT32_MAX) return fail(PCAST_ENOTSUP, "grid too large");
-  if ((rc = check_device()) != PCAST_OK) return rc;
+  return enqueue_decode(Q, K, vop, nullptr, nullptr, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out,
+                        stats, workspace, static_cast<hipStream_t>(stream));
+}
 
-  Params p{};
-  p.q = static_cast<const uint16_t*>(Q);
-  p.k = static_cast<const uint16_t*>(K);
-  p.vop = vop;
-  p.bias = bias;
-  p.out = out;
-  p.stats = stats;
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = Nk;
-  p.order = order;
-  p.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)d));
-  p.S = S;
-  p.inv_S = 1.0f / S;
-  p.p_clamp = 448.0f / S;
-  p.Nq = Nq; p.Nk = Nk; p.n_split = l.n_split; p.split_blocks = split_keys / kKvBlock;
-  uint8_t* base = static_cast<uint8_t*>(workspace);
-  p.part_a = reinterpret_cast<float*>(base + l.a);
-  p.part_ml = reinterpret_cast<float*>(base + l.ml);
-  p.part_cnt = reinterpret_cast<unsigned int*>(base + l.cnt);
-  const int mode = (is_pow2(S) ? kPow2 : kMul) + (S > 448.0f ? 1 : 0);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)(B * Hkv * l.n_split)), mgrid((unsigned)(B * Hkv));
-#define PCAST_DECODE(DD, MM)                                                                        \
-  do {                                                                                              \
-    if (stats) {                                                                                    \
-      hipLaunchKernelGGL((pcast_decode_split<DD, MM, true>), grid, dim3(64), 0, st, p);             \
-      hipLaunchKernelGGL((pcast_decode_merge<DD, true>), mgrid, dim3(256), 0, st, p);               \
-    } else {                                                                                        \
-      hipLaunchKernelGGL((pcast_decode_split<DD, MM, false>), grid, dim3(64), 0, st, p);            \
-      hipLaunchKernelGGL((pcast_decode_merge<DD, false>), mgrid, dim3(256), 0, st, p);              \
-    }                                                                                               \
-  } while (0)
-  if (d == 64) {
-    switch (mode) {
-      case kPow2: PCAST_DECODE(64, kPow2); break;
-      case kPow2Clamp: PCAST_DECODE(64, kPow2Clamp); break;
-      case kMul: PCAST_DECODE(64, kMul); break;
-      default: PCAST_DECODE(64, kMulClamp); break;
-    }
-  } else {
-    switch (mode) {
-      case kPow2: PCAST_DECODE(128, kPow2); break;
-      case kPow2Clamp: PCAST_DECODE(128, kPow2Clamp); break;
-      case kMul: PCAST_DECODE(128, kMul); break;
-      default: PCAST_DECODE(128, kMulClamp); break;
-    }
-  }
-#undef PCAST_DECODE
-  const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? PCAST_OK : hip_fail(e, "decode kernel launch");
+int attn_decode_pcast_qk8(const void* Q, const void* qk8_workspace, const float* bias, int B, int Hq, int Hkv,
+                          int Nq, int Nk, int d, float S, int order, int split_keys, float* out,
+                          unsigned long long* stats, void* workspace, void* stream) {
+  g_last_error[0] = '\0';
+  if (!Q || !qk8_workspace || !out || !workspace)
+    return fail(PCAST_EINVAL, "Q, qk8_workspace, out and workspace must be non-null");
+  if (!aligned(qk8_workspace, 16))
+    return fail(PCAST_EINVAL, "Q, qk8_workspace, out and workspace must be 16-byte aligned");
+  const int rc = check_decode(Q, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out, stats, workspace);
+  if (rc != PCAST_OK) return rc;
+  const Qk8Layout l = qk8_layout(B, Hkv, Nk, d);
+  const uint8_t* base = static_cast<const uint8_t*>(qk8_workspace);
+  return enqueue_decode(Q, nullptr, qk8_workspace, base + l.k8, reinterpret_cast<const int*>(base + l.kexp), bias,
+                        B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out, stats, workspace,
+                        static_cast<hipStream_t>(stream));
 }
 
 int pcast_prepare_qk8_rot(const void* Q, const void* K, const void* V, const signed char* signs, int B, int Hq,

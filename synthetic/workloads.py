@@ -80,6 +80,13 @@ class DecodeWorkload:
         once, out (fp32) written once."""
         return self.B * (self.Hq * self.Nq * self.d * (2 + 4) + self.Hkv * self.Nk * self.d * (2 + 1))
 
+    @property
+    def bytes_qk8(self) -> int:
+        """The same with FP8 logits: K read as E4M3 codes (1 byte) plus one exponent
+        (4 bytes) per 64-key block."""
+        return self.B * (self.Hq * self.Nq * self.d * (2 + 4) + self.Hkv * self.Nk * self.d * (1 + 1)
+                         + self.Hkv * (self.Nk // 64) * 4)
+
 
 DECODE_WORKLOADS = {
     # one new token for each of 16 sequences of 16k cached keys, GQA 32 / 8

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_sizes(lib):
-    assert lib.pcast_abi_version() == 7
+    assert lib.pcast_abi_version() == 8
     assert sna.stats_words(4, 32, 8192) == 4 * 32 * 128 * 2
     assert sna.stats_words(1, 1, 100) == 4
     assert sna.workspace_bytes(4, 32, 8192, 128, 256.0) == 4 * 32 * 8192 * 128
@@ -186,6 +186,24 @@ def test_decode_argument_errors(lib, kw, code):
              split_keys=256, out=FAKE, stats=0, workspace=FAKE, stream=0)
     a.update(kw)
     assert sna.attn_decode_pcast(**a) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=0), sna.PCAST_EINVAL),
+    (dict(qk8_workspace=0), sna.PCAST_EINVAL),
+    (dict(qk8_workspace=FAKE + 8), sna.PCAST_EINVAL),
+    (dict(out=FAKE + 4), sna.PCAST_EINVAL),
+    (dict(split_keys=100), sna.PCAST_EINVAL),
+    (dict(order=3), sna.PCAST_EINVAL),
+    (dict(S=0.0), sna.PCAST_ENOTSUP),
+    (dict(Hq=32, Hkv=8, Nq=9), sna.PCAST_ENOTSUP),
+    (dict(d=80), sna.PCAST_ENOTSUP),
+])
+def test_decode_qk8_argument_errors(lib, kw, code):
+    a = dict(Q=FAKE, qk8_workspace=FAKE, bias=0, B=1, Hq=8, Hkv=2, Nq=1, Nk=1024, d=128, S=256.0, order=1,
+             split_keys=256, out=FAKE, stats=0, workspace=FAKE, stream=0)
+    a.update(kw)
+    assert sna.attn_decode_pcast_qk8(**a) == code
 
 
 def test_bwd_workspace_layout(lib):
