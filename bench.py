@@ -262,7 +262,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the P-cast forward needs no collective, and multi-GPU runs are not part of this build",
+              "the measured path runs on one GPU and needs no collective (sharding is by batch and kv head)",
               file=sys.stderr)
         return 2
 

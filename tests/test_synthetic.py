@@ -38,3 +38,15 @@ def test_workload_sizes():
     assert w["throughput"].flops == 2 * 4 * 32 * 8192 ** 2 * 128
     assert w["tiny"].flops == 4 * 1024 ** 2 * 64
     assert len(w["sweep"].cases) == 11 * 11 * 2
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus 2 ends with a message and exit code 2, before any device use."""
+    import subprocess
+    import sys
+    from pathlib import Path
+    root = Path(__file__).resolve().parents[1]
+    r = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
