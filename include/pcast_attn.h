@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define PCAST_ABI_VERSION 8
+#define PCAST_ABI_VERSION 9
 
 /* Keys per KV block.  The block size is part of the numerics (the running
  * max is updated once per block), so it is fixed. */
@@ -72,6 +72,13 @@ extern "C" {
  *        not accumulated.  In the bf16 path the second word counts P values
  *        that round to zero in bf16.
  * stream hipStream_t, or NULL for the default stream.
+ *
+ * Non-finite inputs: Q, K, V and bias must be finite.  The device code has no
+ * NaN semantics for max and min, so no NaN is guaranteed to propagate: a NaN
+ * or infinity in row i of Q leaves row i of out, and the two counters of its
+ * 64-row block, undefined (possibly finite and wrong), and every other row and
+ * block exactly as without it; a non-finite value in row j of K or V, or in
+ * bias[j], leaves undefined every row that sees key j.
  *
  * Ownership: the caller owns every buffer; the library keeps no pointer after
  * returning.  The call takes pcast_workspace_bytes() of temporary device
@@ -157,6 +164,29 @@ double pcast_sink_max_mean(int k);
 double pcast_delta_critical(double S, int k);
 double pcast_underflow_model(double delta, double S, int k);
 double pcast_lost_mass_model(double delta, double S, int k);
+
+/*
+ * pcast_collapse_check -- the run-time warning of the collapse model: reads a
+ * host copy of an attention call's bias and reports whether forward order at
+ * scale S is predicted to zero most non-sink probabilities (P-cast summary on
+ * gist.science, "Contributi Chiave" point 1: collapse once the sink strength
+ * exceeds Delta_c(S); "Ottimizzazione 1": reverse order defers the sink block
+ * to the last step, so only the non-sink keys of that block can be zeroed).
+ *   bias       host, float32 [N] (the bias passed to the attention call), or NULL.
+ *   N          number of keys, >= 1.
+ *   S, order   as for attn_fwd_pcast (S > 0 and finite).
+ * Outputs (each may be NULL):
+ *   delta      the sink strength: the largest bias value (0 if none is positive);
+ *   k          the number of keys carrying it (0 without a positive bias);
+ *   delta_c    pcast_delta_critical(S, k), NaN when k is 0 or above 1024;
+ *   underflow  pcast_underflow_model(delta, S, k), the forward-order fraction of
+ *              non-sink codes expected at zero (0 when k is 0);
+ *   collapse   1 when order is forward and delta > delta_c, else 0.
+ * Returns PCAST_OK, or PCAST_EINVAL for N <= 0, a bad S or order, or a
+ * non-finite bias value.  Host code only; touches no device.
+ */
+int pcast_collapse_check(const float* bias, int N, double S, int order, double* delta, int* k,
+                         double* delta_c, double* underflow, int* collapse);
 
 /*
  * attn_bwd_pcast -- gradients of the forward by recomputation from its
@@ -323,6 +353,25 @@ int pcast_prepare_qk8_rot(const void* Q, const void* K, const void* V, const sig
 int attn_fwd_pcast_qk8_rot_prepared(const void* workspace, const float* bias, int B, int Hq, int Hkv, int N, int d,
                                     int causal, float S, int order, float* out, unsigned long long* stats,
                                     void* stream);
+
+/*
+ * pcast_cast_e4m3 -- enqueue the P-cast conversion alone: codes[i] = the E4M3
+ * code (OCP e4m3fn) of S * P[i], computed by the same device code that every
+ * attention kernel above applies to its probability tile (P-cast summary on
+ * gist.science, section "Ottimizzazione 2": for S = 2^k the product is formed
+ * inside the conversion and is exact, so the code is that of the exact S*P
+ * rounded to nearest even; for any other S the product is rounded to fp32
+ * first and then converted; above 448 every code saturates at 448, 0x7E).  It
+ * lets a caller check the kernels' rounding bit for bit.
+ *
+ * P      device, float32 [n], 16-byte aligned: probabilities in [0, 1] (the
+ *        kernels convert nothing else; codes of other values are unspecified).
+ * codes  device, uint8 [n], 4-byte aligned, overwritten.
+ * n      a non-negative multiple of 4 (PCAST_EINVAL otherwise).
+ * S      finite and > 0 (PCAST_EINVAL otherwise).
+ * Allocates nothing; errors as for attn_fwd_pcast.
+ */
+int pcast_cast_e4m3(const float* P, unsigned char* codes, long long n, float S, void* stream);
 
 /* Number of uint64 words the stats buffer needs: B * Hq * ceil(N / 64) * 2. */
 size_t pcast_stats_words(int B, int Hq, int N);

@@ -26,7 +26,7 @@ EXPORTS = ("attn_fwd_pcast", "pcast_prepare_v", "attn_fwd_pcast_prepared", "pcas
            "pcast_underflow_model", "pcast_lost_mass_model", "attn_decode_pcast",
            "pcast_decode_workspace_bytes", "attn_bwd_pcast", "pcast_bwd_workspace_bytes",
            "pcast_workspace_bytes_qk8_rot", "pcast_prepare_qk8_rot", "attn_fwd_pcast_qk8_rot_prepared",
-           "attn_decode_pcast_qk8")
+           "attn_decode_pcast_qk8", "pcast_cast_e4m3", "pcast_collapse_check")
 
 _lock = threading.Lock()
 _lib = None
@@ -90,6 +90,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.pcast_prepare_qk8_rot.restype = I
             lib.attn_fwd_pcast_qk8_rot_prepared.argtypes = [P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P]
             lib.attn_fwd_pcast_qk8_rot_prepared.restype = I
+            lib.pcast_cast_e4m3.argtypes = [P, P, ctypes.c_longlong, ctypes.c_float, P]
+            lib.pcast_cast_e4m3.restype = I
             D = ctypes.c_double
             lib.pcast_sink_max_mean.argtypes = [I]
             lib.pcast_sink_max_mean.restype = D
@@ -99,6 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.pcast_underflow_model.restype = D
             lib.pcast_lost_mass_model.argtypes = [D, D, I]
             lib.pcast_lost_mass_model.restype = D
+            lib.pcast_collapse_check.argtypes = [P, I, D, I, P, P, P, P, P]
+            lib.pcast_collapse_check.restype = I
             _lib = lib
     return _lib
 
@@ -200,6 +204,28 @@ def lost_mass_model(delta: float, S: float, k: int = 4) -> float:
     return float(load_library().pcast_lost_mass_model(float(delta), float(S), int(k)))
 
 
+def collapse_check(bias, S: float, order="forward") -> dict:
+    """The collapse model's verdict for a bias (numpy array or torch tensor, copied to
+    the host): keys delta, k, delta_c, underflow, collapse (see pcast_collapse_check)."""
+    import numpy as np
+
+    if bias is not None and hasattr(bias, "detach"):
+        bias = bias.detach().cpu().numpy()
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    if b is not None and b.ndim != 1:
+        raise ValueError("bias must be 1-D")
+    N = 1 if b is None else b.size
+    delta, dc, under = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    k, col = ctypes.c_int(), ctypes.c_int()
+    rc = load_library().pcast_collapse_check(None if b is None else b.ctypes.data, N, float(S), ORDERS[order],
+                                             ctypes.byref(delta), ctypes.byref(k), ctypes.byref(dc),
+                                             ctypes.byref(under), ctypes.byref(col))
+    if rc != PCAST_OK:
+        raise PcastError(rc, "pcast_collapse_check: bad arguments")
+    return {"delta": delta.value, "k": k.value, "delta_c": dc.value, "underflow": under.value,
+            "collapse": bool(col.value)}
+
+
 def workspace_bytes_qk8_rot(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
     return int(load_library().pcast_workspace_bytes_qk8_rot(B, Hq, Hkv, N, d))
 
@@ -217,6 +243,11 @@ def attn_fwd_pcast_qk8_rot_prepared(workspace, bias, B, Hq, Hkv, N, d, causal, S
         stream or None))
 
 
+def cast_e4m3(P, codes, n, S, stream) -> int:
+    """Raw pcast_cast_e4m3 with integer device addresses; returns the C return code."""
+    return int(load_library().pcast_cast_e4m3(P, codes, int(n), float(S), stream or None))
+
+
 def workspace_bytes_qk8(B: int, Hkv: int, N: int, d: int) -> int:
     return int(load_library().pcast_workspace_bytes_qk8(B, Hkv, N, d))
 
@@ -230,15 +261,21 @@ def workspace_bytes(B: int, Hkv: int, N: int, d: int, S: float) -> int:
 
 
 def forward(q, k, v, bias=None, causal: bool = True, S: float = 256.0, order="reverse",
-            stats: bool = False, out=None, qk_fp8: bool = False):
+            stats: bool = False, out=None, qk_fp8: bool = False, check_collapse: bool = False):
     """O = softmax(q k^T / sqrt(d) + bias) v with the P-cast, on the current stream.
 
     q: bf16 [B, Hq, N, d]; k, v: bf16 [B, Hkv, N, d]; bias: fp32 [N] or None.
     S > 0: P*S cast to E4M3; S = 0: the bf16 reference path.  qk_fp8: Q and K
     rounded to E4M3 with power-of-two scales per query row and per 64-key
-    block, logits on the FP8 matrix cores (needs S > 0).  Returns (out fp32 [B, Hq, N, d], stats int64
+    block, logits on the FP8 matrix cores (needs S > 0).  out: an fp32
+    [B, Hq, N, d] contiguous tensor on q's device to write into, or None.
+    check_collapse: copy the bias to the host (a synchronisation) and warn when
+    pcast_collapse_check predicts that the cast zeroes most non-sink
+    probabilities.  Returns (out fp32 [B, Hq, N, d], stats int64
     [B, Hq, N/64, 2] or None).
     """
+    import warnings
+
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -253,6 +290,15 @@ def forward(q, k, v, bias=None, causal: bool = True, S: float = 256.0, order="re
         raise ValueError("bias must be a contiguous float32 [N] tensor on the GPU")
     if out is None:
         out = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+    elif (out.dtype != torch.float32 or out.device != q.device or tuple(out.shape) != (B, Hq, N, d)
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous float32 [B, Hq, N, d] tensor on q's device")
+    if check_collapse and S > 0:
+        r = collapse_check(bias, S, order)
+        if r["collapse"]:
+            warnings.warn(f"P-cast collapse predicted: sink strength {r['delta']:g} on {r['k']} keys exceeds "
+                          f"Delta_c({S:g}) = {r['delta_c']:.3f} in forward order; about "
+                          f"{100 * r['underflow']:.0f} % of the non-sink codes will be zero", RuntimeWarning)
     st = None
     if stats:
         st = torch.empty(stats_words(B, Hq, N), dtype=torch.int64, device=q.device)

@@ -30,7 +30,8 @@ def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory() as td:
         # the host-only part is plain C++ (no device pass)
         obj = os.path.join(td, "collapse_model.o")
-        host = subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-c", SRC_HOST, "-o", obj],
+        host = subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-c",
+                               SRC_HOST, "-o", obj],
                               capture_output=True, text=True)
         if host.returncode != 0:
             raise RuntimeError(f"g++ failed ({host.returncode}):\n{host.stderr}")

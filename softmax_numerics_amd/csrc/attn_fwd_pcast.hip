@@ -47,6 +47,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -401,6 +402,18 @@ __device__ inline uint32_t cast4(const Params& p, float a, float b, float c, flo
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(a * S, b * S, __builtin_bit_cast(int, a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c * S, d * S, w, true);
     return (uint32_t)w;
+  }
+}
+
+// The P-cast conversion on its own, over a caller array of probabilities: four
+// per lane through cast4<kMode>, the device code every attention kernel runs on P.
+template <int kMode>
+__global__ __launch_bounds__(256) void pcast_cast_probs(const Params p, const float4* __restrict__ src,
+                                                         uint32_t* __restrict__ dst, int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    const float4 v = src[i];
+    dst[i] = cast4<kMode>(p, v.x, v.y, v.z, v.w);
   }
 }
 
@@ -2712,6 +2725,35 @@ int attn_decode_pcast_qk8(const void* Q, const void* qk8_workspace, const float*
   return enqueue_decode(Q, nullptr, qk8_workspace, base + l.k8, reinterpret_cast<const int*>(base + l.kexp), bias,
                         B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out, stats, workspace,
                         static_cast<hipStream_t>(stream));
+}
+
+int pcast_cast_e4m3(const float* P, unsigned char* codes, long long n, float S, void* stream) {
+  g_last_error[0] = '\0';
+  if (!P || !codes) return fail(PCAST_EINVAL, "P and codes must be non-null");
+  if (!aligned(P, 16) || !aligned(codes, 4)) return fail(PCAST_EINVAL, "P must be 16-byte and codes 4-byte aligned");
+  if (n < 0 || n % 4 != 0) return fail(PCAST_EINVAL, "n = %lld: must be a non-negative multiple of 4", n);
+  if (!std::isfinite(S) || !(S > 0.0f)) return fail(PCAST_EINVAL, "S must be finite and > 0");
+  int rc = check_device();
+  if (rc != PCAST_OK) return rc;
+  if (n == 0) return PCAST_OK;
+  Params p{};
+  p.S = S;
+  p.inv_S = 1.0f / S;
+  p.p_clamp = 448.0f / S;
+  const int mode = (is_pow2(S) ? kPow2 : kMul) + (S > 448.0f ? 1 : 0);
+  const int64_t n4 = n / 4;
+  const unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 1 << 16);
+  const float4* src = reinterpret_cast<const float4*>(P);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(codes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (mode) {
+    case kPow2: hipLaunchKernelGGL(pcast_cast_probs<kPow2>, dim3(blocks), dim3(256), 0, st, p, src, dst, n4); break;
+    case kPow2Clamp: hipLaunchKernelGGL(pcast_cast_probs<kPow2Clamp>, dim3(blocks), dim3(256), 0, st, p, src, dst, n4); break;
+    case kMul: hipLaunchKernelGGL(pcast_cast_probs<kMul>, dim3(blocks), dim3(256), 0, st, p, src, dst, n4); break;
+    default: hipLaunchKernelGGL(pcast_cast_probs<kMulClamp>, dim3(blocks), dim3(256), 0, st, p, src, dst, n4); break;
+  }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PCAST_OK : hip_fail(e, "cast kernel launch");
 }
 
 int pcast_prepare_qk8_rot(const void* Q, const void* K, const void* V, const signed char* signs, int B, int Hq,

@@ -21,6 +21,8 @@
 // by composite Simpson's rule on [-12, 12] (the density is below 1e-30 outside).
 #include <cmath>
 
+#include "pcast_attn.h"
+
 namespace {
 
 constexpr double kPi = 3.14159265358979323846;
@@ -66,6 +68,34 @@ double pcast_underflow_model(double delta, double S, int k) {
 double pcast_lost_mass_model(double delta, double S, int k) {
   if (bad(S, k) || !std::isfinite(delta)) return NAN;
   return pcast_underflow_model(delta - 1.0, S, k);
+}
+
+int pcast_collapse_check(const float* bias, int N, double S, int order, double* delta, int* k,
+                         double* delta_c, double* underflow, int* collapse) {
+  if (N <= 0 || !(S > 0.0) || !std::isfinite(S) || (order != PCAST_ORDER_FORWARD && order != PCAST_ORDER_REVERSE))
+    return PCAST_EINVAL;
+  // the sink strength is the largest bias; the sinks are the keys that carry it
+  double dmax = 0.0;
+  int nk = 0;
+  if (bias) {
+    for (int j = 0; j < N; ++j) {
+      if (!std::isfinite(bias[j])) return PCAST_EINVAL;
+      if (bias[j] > dmax) {
+        dmax = bias[j];
+        nk = 0;
+      }
+      if (bias[j] == dmax && dmax > 0.0) ++nk;
+    }
+  }
+  const bool sinks = nk > 0 && nk <= 1024;
+  const double dc = sinks ? pcast_delta_critical(S, nk) : NAN;
+  const double f = sinks ? pcast_underflow_model(dmax, S, nk) : 0.0;
+  if (delta) *delta = dmax;
+  if (k) *k = nk;
+  if (delta_c) *delta_c = dc;
+  if (underflow) *underflow = f;
+  if (collapse) *collapse = (sinks && order == PCAST_ORDER_FORWARD && dmax > dc) ? 1 : 0;
+  return PCAST_OK;
 }
 
 }  // extern "C"

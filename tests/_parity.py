@@ -5,7 +5,8 @@ Acceptance (per compared row, 64-row block or case):
   pipeline in kernel mode and slack_row bounds the change of O2 if every E4M3
   (or bf16) rounding decided within a relative 2^-14 of S*p went the other way
   (the GPU's logits and exp2 differ from fp64 by about 1e-6 relative);
-  atol = 1e-3 is ten times tighter than the 1e-2 acceptance bound;
+  atol = 1e-3 is ten times tighter than the 1e-2 acceptance bound; at most
+  0.1 % of the rows (and at least one) may need the slack to pass;
 * relative MSE against exact attention within 5 % of the oracle's;
 * per 64-row block: pair counts equal, underflow counts within the number of
   near-threshold pairs, pooled underflow fraction within 0.5 percentage points;
@@ -21,6 +22,12 @@ ATOL = 1e-3
 EPS = 2.0 ** -14
 
 
+def widened_allowance(rows: int) -> int:
+    """Rows that may exceed atol and pass only through the slack: 0.1 % of the rows
+    compared, and at least one (a single flipped sink code widens its row)."""
+    return max(1, int(1e-3 * rows))
+
+
 def to_gpu_bf16(bits: np.ndarray, device="cuda:0"):
     import torch
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
@@ -33,6 +40,19 @@ def block_rows(B: int, Hq: int, N: int, blocks):
         base = (b * Hq + h) * N + r * 64
         ids.append(np.arange(base, base + 64, dtype=np.int64))
     return np.concatenate(ids) if ids else np.zeros(0, dtype=np.int64)
+
+
+def stride_blocks(B: int, Hq: int, N: int, stride: int):
+    """Every `stride`-th 64-row block of every head, at an offset that moves from head to
+    head (so that together the heads cover every residue), plus each head's last block."""
+    nb = N // 64
+    out = set()
+    for b in range(B):
+        for h in range(Hq):
+            off = ((b * Hq + h) * 7) % stride
+            out.update((b, h, r) for r in range(off, nb, stride))
+            out.add((b, h, nb - 1))
+    return sorted(out)
 
 
 def sample_blocks(B: int, Hq: int, N: int, n: int, seed: int):
@@ -136,6 +156,8 @@ def compare(out_gpu: np.ndarray, stats_gpu, qb, kb, vb, bias, causal, S, order, 
     assert not np.any(bad), (f"{int(bad.sum())} rows beyond atol+slack; worst dev "
                              f"{dev[bad].max():.3g} slack {ref['slack'][bad][np.argmax(dev[bad])]:.3g} "
                              f"extra {tol_extra[bad][np.argmax(dev[bad])]:.3g}")
+    if extra is None:
+        assert widened <= widened_allowance(ids.size), f"{widened} of {ids.size} rows needed the slack"
     e1 = np.sum(ref["o1"] ** 2)
     rel_gpu = np.sum((got - ref["o1"]) ** 2) / e1
     rel_o2 = np.sum((ref["o2"] - ref["o1"]) ** 2) / e1

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_sizes(lib):
-    assert lib.pcast_abi_version() == 8
+    assert lib.pcast_abi_version() == 9
     assert sna.stats_words(4, 32, 8192) == 4 * 32 * 128 * 2
     assert sna.stats_words(1, 1, 100) == 4
     assert sna.workspace_bytes(4, 32, 8192, 128, 256.0) == 4 * 32 * 8192 * 128
@@ -285,3 +285,20 @@ def test_forward_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         sna.forward(q, q, q)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(P=0), sna.PCAST_EINVAL),
+    (dict(codes=0), sna.PCAST_EINVAL),
+    (dict(P=FAKE + 4), sna.PCAST_EINVAL),
+    (dict(codes=FAKE + 2), sna.PCAST_EINVAL),
+    (dict(n=6), sna.PCAST_EINVAL),
+    (dict(n=-4), sna.PCAST_EINVAL),
+    (dict(S=0.0), sna.PCAST_EINVAL),
+    (dict(S=-256.0), sna.PCAST_EINVAL),
+    (dict(S=float("inf")), sna.PCAST_EINVAL),
+])
+def test_cast_argument_errors(lib, kw, code):
+    a = dict(P=FAKE, codes=FAKE, n=1024, S=256.0, stream=0)
+    a.update(kw)
+    assert sna.cast_e4m3(**a) == code

@@ -54,3 +54,27 @@ def test_bad_arguments_give_nan(lib):
               sna.underflow_model(float("nan"), 1.0), sna.lost_mass_model(7.0, 1.0, 0),
               sna.sink_max_mean(0), sna.sink_max_mean(2000)):
         assert np.isnan(v)
+
+
+def test_collapse_check(lib):
+    """The run-time warning: forward order at S = 1 with the configs' sink (delta 7 on
+    keys 0..3) is past Delta_c(1) = 5.90; S = 256 (Delta_c = 11.45) and reverse order
+    are not; delta 5 at S = 1 is below the threshold; no bias, no sink."""
+    N = 1024
+    bias = np.zeros(N, dtype=np.float32)
+    bias[:4] = 7.0
+    r = sna.collapse_check(bias, 1.0, "forward")
+    assert r["collapse"] and r["k"] == 4 and r["delta"] == 7.0
+    assert abs(r["delta_c"] - sna.delta_critical(1.0)) < 1e-12
+    assert abs(r["underflow"] - sna.underflow_model(7.0, 1.0)) < 1e-12
+    assert not sna.collapse_check(bias, 256.0, "forward")["collapse"]
+    assert not sna.collapse_check(bias, 1.0, "reverse")["collapse"]
+    bias[:4] = 5.0
+    assert not sna.collapse_check(bias, 1.0, "forward")["collapse"]
+    bias[:4] = 13.0
+    assert sna.collapse_check(bias, 448.0, "forward")["collapse"]      # Delta_c(448) = 12.01
+    r = sna.collapse_check(None, 1.0, "forward")
+    assert not r["collapse"] and r["k"] == 0 and np.isnan(r["delta_c"])
+    bias[7] = float("nan")
+    with pytest.raises(sna.PcastError):
+        sna.collapse_check(bias, 1.0, "forward")

@@ -61,6 +61,7 @@ def _compare(out, st, ref, atol=1e-3):
     assert abs(rel_gpu - rel_o2) <= 0.05 * rel_o2 + 1e-15, f"relMSE {rel_gpu:.4g} vs {rel_o2:.4g}"
     rep = {"max_dev": float(dev.max()), "rows_widened": int(np.sum(dev > atol)),
            "relmse_gpu": float(rel_gpu), "relmse_oracle": float(rel_o2)}
+    assert rep["rows_widened"] <= _parity.widened_allowance(dev.size), f"{rep['rows_widened']} rows needed the slack"
     if st is not None:
         tot, zer, amb = (ref[k].sum(axis=2) for k in ("total", "zero", "zero_amb"))
         assert np.array_equal(st[..., 0], tot), "pair counts differ"

@@ -136,33 +136,114 @@ def test_errors_are_reported(sna):
     with pytest.raises(sna.PcastError) as ei:
         sna.forward(q, q, q, None, S=256.0)
     assert ei.value.code == sna.PCAST_ENOTSUP
+    # a caller's out must be a contiguous fp32 [B, Hq, N, d] tensor on the same device
+    q = torch.zeros(1, 2, 128, 64, dtype=torch.bfloat16, device="cuda")
+    for bad in (torch.empty(1, 2, 128, 64, dtype=torch.bfloat16, device="cuda"),
+                torch.empty(1, 2, 64, 64, dtype=torch.float32, device="cuda"),
+                torch.empty(1, 2, 64, 128, dtype=torch.float32, device="cuda").transpose(2, 3),
+                torch.empty(1, 2, 128, 64, dtype=torch.float32)):
+        with pytest.raises(ValueError):
+            sna.forward(q, q, q, None, S=256.0, out=bad)
 
 
-SWEEP_CELLS = [(dl, S, o) for dl in (0.0, 5.0, 7.0, 10.0) for S in (1.0, 16.0, 256.0, 448.0, 512.0)
-               for o in (0, 1)]
-
-
-@pytest.mark.parametrize("delta,S,order", SWEEP_CELLS)
-def test_sweep_cells(sna, delta, S, order):
-    _case(sna, "sweep", 1, 8, 8, 4096, 128, True, delta, S, order, 2, blocks=12)
+def test_collapse_warning(sna):
+    print("\n[case] collapse warning", flush=True)
+    q = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16, device="cuda")
+    bias = torch.from_numpy(synthetic.sink_bias(128, 7.0)).cuda()
+    with pytest.warns(RuntimeWarning, match="collapse"):
+        sna.forward(q, q, q, bias, S=1.0, order="forward", check_collapse=True)
+    import warnings
+    with warnings.catch_warnings():
+        warnings.simplefilter("error")
+        sna.forward(q, q, q, bias, S=256.0, order="forward", check_collapse=True)
+        sna.forward(q, q, q, bias, S=1.0, order="reverse", check_collapse=True)
+    torch.cuda.synchronize()
 
 
 W = synthetic.WORKLOADS
+_INPUTS = {}
+
+
+def _workload_inputs(name):
+    """Q, K, V bits of a workload (generated once per module) and their GPU copies."""
+    if name not in _INPUTS:
+        _INPUTS.clear()                      # keep one full-size workload in memory at a time
+        w = W[name]
+        qb, kb, vb = synthetic.qkv_bf16(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed)
+        _INPUTS[name] = (qb, kb, vb, tuple(_parity.to_gpu_bf16(x) for x in (qb, kb, vb)))
+    return _INPUTS[name]
+
+
+def _workload_case(sna, name, delta, S, order, blocks):
+    w = W[name]
+    print(f"\n[case] {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} causal={w.causal} "
+          f"delta={delta} S={S} order={order} seed={w.seed} blocks={len(blocks)}", flush=True)
+    qb, kb, vb, (q, k, v) = _workload_inputs(name)
+    bias = synthetic.sink_bias(w.N, delta)
+    out, st = sna.forward(q, k, v, torch.from_numpy(bias).cuda(), causal=w.causal, S=S, order=order,
+                          stats=True)
+    torch.cuda.synchronize()
+    out_np = out.cpu().numpy()
+    st_np = st.cpu().numpy()
+    del out, st
+    rep = _parity.compare(out_np, st_np, qb, kb, vb, bias, w.causal, S, order, blocks)
+    print(f"[case] {name}: {rep}", flush=True)
+    return rep
+
+
+def _sweep_blocks(i):
+    """Four 64-row blocks for Sweep cell i: the last block of one head (every key) and three
+    more that move with i across heads and positions."""
+    return sorted({(0, i % 8, 63), (0, (i + 3) % 8, (5 * i + 11) % 63),
+                   (0, (i + 5) % 8, (7 * i + 29) % 63), (0, (i + 6) % 8, (3 * i) % 63)})
+
+
+@pytest.mark.parametrize("i", range(len(W["sweep"].cases)),
+                         ids=[f"d{c[0]:g}-S{c[1]:g}-{'rev' if c[2] else 'fwd'}" for c in W["sweep"].cases])
+def test_sweep_cells(sna, i):
+    """Every cell of the Sweep (delta 0..10, S = 2^0..2^9 and 448, both orders) on the same
+    Q, K, V, four sampled 64-row blocks each."""
+    delta, S, order = W["sweep"].cases[i]
+    _workload_case(sna, "sweep", delta, S, order, _sweep_blocks(i))
 
 
 @pytest.mark.parametrize("delta,S,order", W["throughput"].cases)
 def test_throughput_full_size(sna, delta, S, order):
     w = W["throughput"]
-    _case(sna, "throughput", w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, delta, S, order, w.seed, blocks=8)
+    _workload_case(sna, "throughput", delta, S, order, _parity.stride_blocks(w.B, w.Hq, w.N, 16))
 
 
 @pytest.mark.parametrize("delta,S,order", W["gqa"].cases)
 def test_gqa_full_size(sna, delta, S, order):
     w = W["gqa"]
-    _case(sna, "gqa", w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, delta, S, order, w.seed, blocks=6)
+    _workload_case(sna, "gqa", delta, S, order, _parity.stride_blocks(w.B, w.Hq, w.N, 64))
 
 
-@pytest.mark.parametrize("delta,S,order", [(7.0, 256.0, 1), (9.0, 256.0, 0)])
+@pytest.mark.parametrize("delta,S,order", W["long"].cases)
 def test_long_full_size(sna, delta, S, order):
     w = W["long"]
-    _case(sna, "long", w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, delta, S, order, w.seed, blocks=4)
+    _workload_case(sna, "long", delta, S, order, _parity.stride_blocks(w.B, w.Hq, w.N, 128))
+
+
+@pytest.mark.parametrize("qk_fp8", [False, True])
+def test_nan_in_one_query_row_stays_in_that_row(sna, qk_fp8):
+    """Non-finite inputs give undefined output only where they are seen: a NaN in one row
+    of Q leaves every other row of out, and the counters of every other 64-row block,
+    bit-identical to the run without it."""
+    print(f"\n[case] NaN in one query row, FP8 logits={qk_fp8}", flush=True)
+    B, Hq, Hkv, N, d = 1, 2, 1, 256, 128
+    qb, kb, vb = synthetic.qkv_bf16(B, Hq, Hkv, N, d, 26)
+    bias = torch.from_numpy(synthetic.sink_bias(N, 7.0)).cuda()
+    q, k, v = (_parity.to_gpu_bf16(x) for x in (qb, kb, vb))
+    qn = q.clone()
+    qn[0, 1, 77, 5] = float("nan")
+    a, sa = sna.forward(q, k, v, bias, causal=True, S=256.0, order="reverse", stats=True, qk_fp8=qk_fp8)
+    b, sb = sna.forward(qn, k, v, bias, causal=True, S=256.0, order="reverse", stats=True, qk_fp8=qk_fp8)
+    torch.cuda.synchronize()
+    a, b, sa, sb = (x.cpu().numpy() for x in (a, b, sa, sb))
+    keep = np.ones((B, Hq, N), dtype=bool)
+    keep[0, 1, 77] = False
+    assert np.array_equal(a[keep], b[keep])
+    keep_st = np.ones(sa.shape[:3], dtype=bool)
+    keep_st[0, 1, 77 // 64] = False
+    assert np.array_equal(sa[keep_st], sb[keep_st])
