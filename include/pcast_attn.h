@@ -96,6 +96,26 @@ int attn_fwd_pcast(const void* Q, const void* K, const void* V, const float* bia
                    unsigned long long* stats, void* stream);
 
 /*
+ * attn_fwd_pcast_noalloc -- attn_fwd_pcast for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments, kernels and results (bit for
+ * bit), with the V operand copy in a scratch array of
+ * PCAST_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends.  Calls no allocator.
+ * Limit: pcast_workspace_bytes(B, Hkv, N, d, S) must not exceed
+ * PCAST_NOALLOC_SCRATCH_BYTES (64 MiB: B * Hkv * N * d <= 2^26 for S > 0, half
+ * that for S = 0), else PCAST_ENOTSUP before anything is enqueued.
+ * Every call on one device shares that device's scratch: calls that overlap on
+ * one device (different streams or threads without ordering between them)
+ * race and give undefined results.  Calls ordered on one stream are safe.
+ */
+#define PCAST_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int attn_fwd_pcast_noalloc(const void* Q, const void* K, const void* V, const float* bias, int B, int Hq,
+                           int Hkv, int N, int d, int causal, float S, int order, float* out,
+                           unsigned long long* stats, void* stream);
+
+/*
  * The same forward in two stages, for callers that bring their own temporary
  * memory (and for timing the attention kernel on its own).
  *

@@ -26,7 +26,8 @@ EXPORTS = ("attn_fwd_pcast", "pcast_prepare_v", "attn_fwd_pcast_prepared", "pcas
            "pcast_underflow_model", "pcast_lost_mass_model", "attn_decode_pcast",
            "pcast_decode_workspace_bytes", "attn_bwd_pcast", "pcast_bwd_workspace_bytes",
            "pcast_workspace_bytes_qk8_rot", "pcast_prepare_qk8_rot", "attn_fwd_pcast_qk8_rot_prepared",
-           "attn_decode_pcast_qk8", "pcast_cast_e4m3", "pcast_collapse_check")
+           "attn_decode_pcast_qk8", "pcast_cast_e4m3", "pcast_collapse_check",
+           "attn_fwd_pcast_noalloc")
 
 _lock = threading.Lock()
 _lib = None
@@ -50,6 +51,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             P, I = ctypes.c_void_p, ctypes.c_int
             lib.attn_fwd_pcast.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P]
             lib.attn_fwd_pcast.restype = I
+            lib.attn_fwd_pcast_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P]
+            lib.attn_fwd_pcast_noalloc.restype = I
             lib.pcast_prepare_v.argtypes = [P, I, I, I, I, ctypes.c_float, P, P]
             lib.pcast_prepare_v.restype = I
             lib.attn_fwd_pcast_prepared.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I,
@@ -115,6 +118,15 @@ def attn_fwd_pcast(Q, K, V, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats
     """Raw call with integer device addresses (0 for NULL); returns the C return code."""
     return int(load_library().attn_fwd_pcast(Q, K, V, bias or None, B, Hq, Hkv, N, d, int(causal),
                                              float(S), int(order), out, stats or None, stream or None))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def attn_fwd_pcast_noalloc(Q, K, V, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats, stream) -> int:
+    """Raw attn_fwd_pcast_noalloc (no allocation; library scratch) with integer device addresses."""
+    return int(load_library().attn_fwd_pcast_noalloc(Q, K, V, bias or None, B, Hq, Hkv, N, d, int(causal),
+                                                     float(S), int(order), out, stats or None, stream or None))
 
 
 def prepare_v(V, B, Hkv, N, d, S, workspace, stream) -> int:

@@ -59,6 +59,12 @@
 
 #include "pcast_attn.h"
 
+// Scratch memory of attn_fwd_pcast_noalloc: the V operand copy of one call.  Each
+// device the library runs on holds its own copy until the process ends; host code
+// reaches it only through the address hipGetSymbolAddress returns for the current
+// device (the name itself is a host-side stand-in, not a device address).
+static __device__ __align__(256) uint8_t scratch[PCAST_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -2205,6 +2211,26 @@ int arch_check(int dev) {
   return cache[dev];
 }
 
+// Device address of `scratch` on the current device, looked up once per device.
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(PCAST_ENOTSUP, "device %d: at most 64 devices", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(PCAST_EHIP, "hipGetSymbolAddress(scratch) returned null");
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return PCAST_OK;
+}
+
 bool is_pow2(float S) {
   int e;
   return std::frexp(S, &e) == 0.5f;
@@ -2610,6 +2636,31 @@ int attn_fwd_pcast(const void* Q, const void* K, const void* V, const float* bia
   if (rc != PCAST_OK) return rc;
   if (e != hipSuccess) return hip_fail(e, "hipFreeAsync(workspace)");
   return PCAST_OK;
+}
+
+int attn_fwd_pcast_noalloc(const void* Q, const void* K, const void* V, const float* bias, int B, int Hq,
+                           int Hkv, int N, int d, int causal, float S, int order, float* out,
+                           unsigned long long* stats, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_attn_args(Q, K, bias, causal, order, out, stats);
+  if (rc != PCAST_OK) return rc;
+  if (!V) return fail(PCAST_EINVAL, "V must be non-null");
+  if (!aligned(V, 16)) return fail(PCAST_EINVAL, "V must be 16-byte aligned");
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  const size_t need = pcast_workspace_bytes(B, Hkv, N, d, S);
+  if (need > (size_t)PCAST_NOALLOC_SCRATCH_BYTES)
+    return fail(PCAST_ENOTSUP,
+                "the V operand copy needs %zu bytes, above the %zu bytes of scratch of attn_fwd_pcast_noalloc; "
+                "use attn_fwd_pcast, or pcast_prepare_v + attn_fwd_pcast_prepared with a caller workspace",
+                need, (size_t)PCAST_NOALLOC_SCRATCH_BYTES);
+  if ((rc = check_device()) != PCAST_OK) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws)) != PCAST_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the pre-pass writes every byte of the copy that the attention kernel reads: no clearing
+  rc = enqueue_prep(V, B, Hkv, N, d, S, ws, st);
+  if (rc == PCAST_OK) rc = enqueue_attn(Q, K, ws, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats, st);
+  return rc;
 }
 
 int attn_fwd_pcast_rows(const void* Q, const void* K, const void* workspace, const float* bias, int B,

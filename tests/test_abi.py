@@ -302,3 +302,12 @@ def test_cast_argument_errors(lib, kw, code):
     a = dict(P=FAKE, codes=FAKE, n=1024, S=256.0, stream=0)
     a.update(kw)
     assert sna.cast_e4m3(**a) == code
+
+
+def test_noalloc_rejects_inputs_above_its_scratch(lib):
+    # 1 x 8 kv heads x 131072 keys x d 128 of E4M3 V = 2^27 bytes, twice the scratch: refused on the host
+    rc = sna.attn_fwd_pcast_noalloc(FAKE, FAKE, FAKE, 0, 1, 8, 8, 131072, 128, 1, 256.0, 1, FAKE, 0, 0)
+    assert rc == sna.PCAST_ENOTSUP and "scratch" in sna.strerror(rc)
+    # S = 0 keeps a bf16 copy: twice the bytes, so half the keys fit
+    assert sna.attn_fwd_pcast_noalloc(FAKE, FAKE, FAKE, 0, 1, 4, 4, 131072, 128, 1, 0.0, 1, FAKE, 0, 0) == sna.PCAST_ENOTSUP
+    assert sna.attn_fwd_pcast_noalloc(0, FAKE, FAKE, 0, 1, 1, 1, 64, 64, 1, 256.0, 1, FAKE, 0, 0) == sna.PCAST_EINVAL
