@@ -924,15 +924,20 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
   auto visible = [&](int t) __attribute__((always_inline)) {
     return wave_active && (!kCausal || t * kKvBlock <= wrow0 + kRowsPerWave - 1);
   };
+  // The LDS destination of a direct load is a wave-uniform register (M0): form this
+  // wave's offset once per load group as a scalar, so that no load waits on a
+  // vector-to-scalar move.
   auto load_k = [&](int t, int buf) __attribute__((always_inline)) {
     const uint8_t* ks = kbase + t * kKTile;
+    const int dst = __builtin_amdgcn_readfirstlane(wave * kKLoads * 1024);
 #pragma unroll
-    for (int i = 0; i < kKLoads; ++i) load_to_lds16(ks + ksrc[i], kbuf(buf) + (wave * kKLoads + i) * 1024);
+    for (int i = 0; i < kKLoads; ++i) load_to_lds16(ks + ksrc[i], kbuf(buf) + dst + i * 1024);
   };
   auto load_v = [&](int t, int buf) __attribute__((always_inline)) {
     const uint8_t* vs = vbase + t * kVTile;
+    const int dst = __builtin_amdgcn_readfirstlane(wave * kVLoads * 1024);
 #pragma unroll
-    for (int i = 0; i < kVLoads; ++i) load_to_lds16(vs + vsrc[i], vbuf(buf) + (wave * kVLoads + i) * 1024);
+    for (int i = 0; i < kVLoads; ++i) load_to_lds16(vs + vsrc[i], vbuf(buf) + dst + i * 1024);
   };
   auto load_b = [&](int t, int buf) __attribute__((always_inline)) {
     if (with_bias && wave == 0) load_to_lds4(p.bias + t * kKvBlock + lane, bbuf(buf));
@@ -1138,6 +1143,10 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
   // FP8 logits: exponent of each key block's scale, read one step ahead
   const int* kexp_head = kQ8 ? p.kexp + ((int64_t)b * p.Hkv + hk) * n_tiles : nullptr;
   int ke_next = kQ8 ? kexp_head[tile_of(0)] : 0;
+  // the lane's bias value in the block the next step processes (0 without a bias), read
+  // from global memory one step ahead: the step's fast / general decision then waits
+  // for no LDS read
+  float bias_next = with_bias ? p.bias[tile_of(0) * kKvBlock + lane] : 0.0f;
 
   auto step = [&](int it, auto cur_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
@@ -1156,7 +1165,8 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
     const bool vis1 = it + 1 < n_it && visible(tile_of(it + 1));
     const int key0 = t * kKvBlock;
     const bool diag = kCausal && (key0 + kKvBlock - 1 > wrow0);
-    const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bbuf(cur)[lane] != 0.0f) != 0;
+    const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bias_next != 0.0f) != 0;
+    if (with_bias && it + 1 < n_it) bias_next = p.bias[tile_of(it + 1) * kKvBlock + lane];
     const bool fast = vis && !diag && !has_bias;
     if (!kDiag && fast && pend && vis1) {
       // Steady state: the step's MFMAs (20 at d = 128), each in a chunk of its own
@@ -1191,7 +1201,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
       constexpr int kS = 2 * kSSteps;  // logit MFMAs
       i32x8_t vf[G::kDTiles];
       KFrag kf[kS];
-      float m4[4], ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float m4[4], ps[4];
       auto chain = [&](int q) __attribute__((always_inline)) {
         m4[q] = fmaxf(sacc[q / 2][(q % 2) * 8], sacc[q / 2][(q % 2) * 8 + 1]);
 #pragma unroll
@@ -1202,7 +1212,8 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
       auto expo = [&](int hh, int r) __attribute__((always_inline)) {
         const float pj = __builtin_amdgcn_exp2f(fmaf(sacc[hh][r], c, neg));
         sacc[hh][r] = pj;
-        ps[r % 4] += pj;
+        if (hh == 0 && r < 4) ps[r] = pj;  // the first four start the partial sums
+        else ps[r % 4] += pj;
       };
       auto cast = [&](int w) __attribute__((always_inline)) {  // codes of slots 4w..4w+3
         const int hh = w / 4, r = 4 * (w % 4);
