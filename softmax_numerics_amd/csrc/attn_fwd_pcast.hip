@@ -1222,7 +1222,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
 #define PCAST_FENCE __builtin_amdgcn_sched_barrier(0)
       // operand fragments run kAhead MFMAs ahead: MFMA i (P.V tiles first, then the
       // logit halves) takes fragment i
-      constexpr int kAhead = 2;
+      constexpr int kAhead = 4;
       constexpr int kM = G::kDTiles + kS;
       auto fetch = [&](int i) __attribute__((always_inline)) {
         if (i < G::kDTiles) vf[i] = vfrag(i);
