@@ -160,11 +160,11 @@ def bench_backward(sna, torch, np, synthetic, w, q, k, v, ws, bias_t, dev, strea
                          "flops_rule": "2.5 x the forward's 2*B*H*N^2*d (causal)"}}
 
 
-def bench_sweep_all(sna, torch, np, synthetic, w, q, k, v, dev, n_streams: int = 4, reps: int = 3):
-    """The whole Sweep workload: every (delta, S, order) cell on the same Q, K, V, one
-    attention call per cell, the cells spread round-robin over `n_streams` streams so that
-    several are in flight.  Returns the aggregate rate (all cells' flops over the time from
-    the first launch to the last completion), with the counters on."""
+def bench_sweep_all(sna, torch, np, synthetic, w, q, k, v, dev, reps: int = 3):
+    """The whole Sweep workload: every (delta, S, order) cell on the same Q, K, V through
+    one attn_fwd_pcast_multi call (one launch per conversion mode and per 64 cells, the
+    row blocks of all cells in one grid), each cell with its own out and counters.
+    Returns the aggregate rate: all cells' flops over the call's time."""
     cells = [c for c in w.cases if c[1] > 0]
     ws = torch.empty(sna.workspace_bytes(w.B, w.Hkv, w.N, w.d, 256.0), dtype=torch.uint8, device=dev)
     main = torch.cuda.current_stream(dev)
@@ -172,27 +172,19 @@ def bench_sweep_all(sna, torch, np, synthetic, w, q, k, v, dev, n_streams: int =
     if rc != sna.PCAST_OK:
         raise sna.PcastError(rc, sna.strerror(rc))
     biases = {dl: torch.from_numpy(synthetic.sink_bias(w.N, dl)).to(dev) for dl in sorted({c[0] for c in cells})}
-    outs = [torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device=dev) for _ in range(n_streams)]
-    sts = [torch.empty(sna.stats_words(w.B, w.Hq, w.N), dtype=torch.int64, device=dev) for _ in range(n_streams)]
-    streams = [torch.cuda.Stream(device=dev) for _ in range(n_streams)]
+    outs = [torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device=dev) for _ in cells]
+    sts = [torch.empty(sna.stats_words(w.B, w.Hq, w.N), dtype=torch.int64, device=dev) for _ in cells]
+    args = dict(biases=[biases[c[0]].data_ptr() for c in cells], Ss=[c[1] for c in cells],
+                orders=[c[2] for c in cells], outs=[o.data_ptr() for o in outs], stats=[x.data_ptr() for x in sts])
     torch.cuda.synchronize()
 
     def run():
         start, done = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(main)
-        for s_ in streams:
-            s_.wait_event(start)
-        for i, (dl, S_, order_) in enumerate(cells):
-            j = i % n_streams
-            rc_ = sna.attn_fwd_pcast_prepared(q.data_ptr(), k.data_ptr(), ws.data_ptr(), biases[dl].data_ptr(), w.B,
-                                              w.Hq, w.Hkv, w.N, w.d, int(w.causal), S_, order_, outs[j].data_ptr(),
-                                              sts[j].data_ptr(), streams[j].cuda_stream)
-            if rc_ != sna.PCAST_OK:
-                raise sna.PcastError(rc_, sna.strerror(rc_))
-        for s_ in streams:
-            ev = torch.cuda.Event()
-            ev.record(s_)
-            main.wait_event(ev)
+        rc_ = sna.attn_fwd_pcast_multi(q.data_ptr(), k.data_ptr(), ws.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d,
+                                       int(w.causal), stream=main.cuda_stream, **args)
+        if rc_ != sna.PCAST_OK:
+            raise sna.PcastError(rc_, sna.strerror(rc_))
         done.record(main)
         done.synchronize()
         return start.elapsed_time(done)
@@ -201,14 +193,14 @@ def bench_sweep_all(sna, torch, np, synthetic, w, q, k, v, dev, n_streams: int =
     ms = sorted(run() for _ in range(reps))[reps // 2]
     flops = len(cells) * w.flops
     achieved = flops / (ms * 1e-3) / 1e12
-    print(f"[bench] whole sweep: {len(cells)} cells on {n_streams} streams in {ms:.3f} ms "
+    print(f"[bench] whole sweep: {len(cells)} cells in one multi-configuration call, {ms:.3f} ms "
           f"({achieved:.0f} TFLOP/s)", file=sys.stderr, flush=True)
-    return {"cells": len(cells), "streams": n_streams, "ms": round(ms, 4), "achieved": round(achieved, 2),
+    return {"cells": len(cells), "ms": round(ms, 4), "achieved": round(achieved, 2),
             "peak": PEAK_FP8, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8, 4),
             "per_cell_us": round(ms * 1e3 / len(cells), 2),
             "what": "every cell of the Sweep (delta 0..10, S = 2^0..2^9 and 448, both orders) on the same Q, K, V "
-                    "(one V pre-pass for all), counters on, one attention call per cell, cells round-robin over "
-                    "the streams"}
+                    "(one V pre-pass for all, outside the timed call), counters on, one attn_fwd_pcast_multi "
+                    "call: one launch per conversion mode and per 64 cells"}
 
 
 def bench_decode(sna, torch, np, synthetic, dev, stream, steps, warmup):

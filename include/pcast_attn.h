@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define PCAST_ABI_VERSION 9
+#define PCAST_ABI_VERSION 10
 
 /* Keys per KV block.  The block size is part of the numerics (the running
  * max is updated once per block), so it is fixed. */
@@ -141,6 +141,36 @@ int pcast_prepare_v(const void* V, int B, int Hkv, int N, int d, float S, void* 
 int attn_fwd_pcast_prepared(const void* Q, const void* K, const void* workspace, const float* bias,
                             int B, int Hq, int Hkv, int N, int d, int causal, float S, int order,
                             float* out, unsigned long long* stats, void* stream);
+
+/*
+ * attn_fwd_pcast_multi -- several configurations of the prepared forward on the same
+ * Q, K and V in one grid: configuration i has its own bias[i], S[i], order[i], out[i]
+ * and stats[i], and its results equal those of attn_fwd_pcast_prepared with these
+ * arguments, bit for bit.  This is the shape of the P-cast summary's experiment
+ * (section "Risultati Sperimentali": the same inputs under a sweep of sink
+ * strengths, scales and key-block orders); one launch lets the row blocks of all
+ * configurations share the chip, longest first, instead of each configuration
+ * waiting for its own longest rows.
+ *
+ * Q, K       device, bf16, as for attn_fwd_pcast.
+ * workspace  the V operand copy that pcast_prepare_v(V, B, Hkv, N, d, S > 0, ...)
+ *            wrote (every S[i] must be > 0: the FP8 P.V path; S[i] = 0 gives
+ *            PCAST_ENOTSUP).
+ * B, Hq, Hkv, N, d, causal  as for attn_fwd_pcast, shared by all configurations.
+ * n_cfg      number of configurations, >= 1.
+ * bias       host array of n_cfg device pointers (float32 [N], or NULL for no bias),
+ *            or NULL for no bias in any configuration.
+ * S, order   host arrays of n_cfg values (S finite and > 0; order 0 or 1).
+ * out        host array of n_cfg device pointers, float32 [B][Hq][N][d], 16-byte aligned.
+ * stats      host array of n_cfg device pointers (uint64 [pcast_stats_words(B, Hq, N)],
+ *            8-byte aligned, all non-null), or NULL for no counting.
+ * The host arrays are read during the call only.  Configurations are grouped by how
+ * P is converted (S a power of two or not, S above 448 or not), at most 64 per launch.
+ * Allocates nothing; errors as for attn_fwd_pcast_prepared.
+ */
+int attn_fwd_pcast_multi(const void* Q, const void* K, const void* workspace, int B, int Hq, int Hkv, int N, int d,
+                         int causal, int n_cfg, const float* const* bias, const float* S, const int* order,
+                         float* const* out, unsigned long long* const* stats, void* stream);
 
 /*
  * attn_fwd_pcast_rows -- attn_fwd_pcast_prepared (same arguments, same out and

@@ -27,7 +27,7 @@ EXPORTS = ("attn_fwd_pcast", "pcast_prepare_v", "attn_fwd_pcast_prepared", "pcas
            "pcast_decode_workspace_bytes", "attn_bwd_pcast", "pcast_bwd_workspace_bytes",
            "pcast_workspace_bytes_qk8_rot", "pcast_prepare_qk8_rot", "attn_fwd_pcast_qk8_rot_prepared",
            "attn_decode_pcast_qk8", "pcast_cast_e4m3", "pcast_collapse_check",
-           "attn_fwd_pcast_noalloc")
+           "attn_fwd_pcast_noalloc", "attn_fwd_pcast_multi")
 
 _lock = threading.Lock()
 _lib = None
@@ -53,6 +53,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_fwd_pcast.restype = I
             lib.attn_fwd_pcast_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P]
             lib.attn_fwd_pcast_noalloc.restype = I
+            lib.attn_fwd_pcast_multi.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, P]
+            lib.attn_fwd_pcast_multi.restype = I
             lib.pcast_prepare_v.argtypes = [P, I, I, I, I, ctypes.c_float, P, P]
             lib.pcast_prepare_v.restype = I
             lib.attn_fwd_pcast_prepared.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I,
@@ -127,6 +129,21 @@ def attn_fwd_pcast_noalloc(Q, K, V, bias, B, Hq, Hkv, N, d, causal, S, order, ou
     """Raw attn_fwd_pcast_noalloc (no allocation; library scratch) with integer device addresses."""
     return int(load_library().attn_fwd_pcast_noalloc(Q, K, V, bias or None, B, Hq, Hkv, N, d, int(causal),
                                                      float(S), int(order), out, stats or None, stream or None))
+
+
+def attn_fwd_pcast_multi(Q, K, workspace, B, Hq, Hkv, N, d, causal, biases, Ss, orders, outs, stats,
+                         stream) -> int:
+    """Raw attn_fwd_pcast_multi: integer device addresses; biases, outs and stats are lists of
+    addresses (0 for NULL; stats None for no counting), Ss and orders lists of numbers."""
+    n = len(Ss)
+    ptrs = ctypes.c_void_p * n
+    b_arr = ptrs(*[(x or None) for x in biases]) if biases is not None else None
+    o_arr = ptrs(*outs)
+    s_arr = ptrs(*stats) if stats is not None else None
+    S_arr = (ctypes.c_float * n)(*[float(x) for x in Ss])
+    r_arr = (ctypes.c_int * n)(*[int(x) for x in orders])
+    return int(load_library().attn_fwd_pcast_multi(Q, K, workspace, B, Hq, Hkv, N, d, int(causal), n, b_arr, S_arr,
+                                                   r_arr, o_arr, s_arr, stream or None))
 
 
 def prepare_v(V, B, Hkv, N, d, S, workspace, stream) -> int:
@@ -324,3 +341,40 @@ def forward(q, k, v, bias=None, causal: bool = True, S: float = 256.0, order="re
     if st is not None:
         st = st.view(B, Hq, -1, 2)
     return out, st
+
+
+def forward_multi(q, k, v, configs, causal: bool = True, stats: bool = False):
+    """Several (bias, S, order) configurations of the forward on the same q, k, v in one
+    launch per conversion mode (attn_fwd_pcast_multi).  configs: list of (bias fp32 [N]
+    tensor or None, S > 0, order).  Returns (list of out, list of stats or None), each
+    equal to forward() with that configuration."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D bfloat16 tensor on the GPU")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, N, d] matching q")
+    if not configs:
+        raise ValueError("configs must not be empty")
+    for bias, _, _ in configs:
+        if bias is not None and (bias.dtype != torch.float32 or not bias.is_cuda or bias.shape != (N,)
+                                 or not bias.is_contiguous()):
+            raise ValueError("each bias must be a contiguous float32 [N] tensor on the GPU")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    ws = torch.empty(workspace_bytes(B, Hkv, N, d, 1.0), dtype=torch.uint8, device=q.device)
+    rc = prepare_v(v.data_ptr(), B, Hkv, N, d, 1.0, ws.data_ptr(), stream)
+    if rc != PCAST_OK:
+        raise PcastError(rc, strerror(rc))
+    outs = [torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device) for _ in configs]
+    sts = [torch.empty(stats_words(B, Hq, N), dtype=torch.int64, device=q.device) for _ in configs] if stats else None
+    rc = attn_fwd_pcast_multi(q.data_ptr(), k.data_ptr(), ws.data_ptr(), B, Hq, Hkv, N, d, causal,
+                              [0 if c[0] is None else c[0].data_ptr() for c in configs],
+                              [c[1] for c in configs], [ORDERS[c[2]] for c in configs],
+                              [o.data_ptr() for o in outs], None if sts is None else [x.data_ptr() for x in sts],
+                              stream)
+    if rc != PCAST_OK:
+        raise PcastError(rc, strerror(rc))
+    return outs, (None if sts is None else [x.view(B, Hq, -1, 2) for x in sts])

@@ -796,13 +796,32 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params 
 // block j-1's alpha comes first).  The three streams are independent, so the
 // MFMAs interleave with the exponentials inside one basic block.
 // ---------------------------------------------------------------------------
+// Several configurations of one forward in one launch: the cells share Q, K and the V
+// operand copy, each has its own bias, scale, key-block order, output and counters.
+// The table travels by value in the kernel arguments.
+constexpr int kMaxCells = 64;
+struct Cells {
+  const float* bias[kMaxCells];
+  float* out[kMaxCells];
+  unsigned long long* stats[kMaxCells];
+  float S[kMaxCells], inv_S[kMaxCells], p_clamp[kMaxCells];
+  int order[kMaxCells];
+  int n;
+};
+struct NoCells {};
+
 // kStats: 0 = no counting; 1 = underflow counters; 2 = counters (if p.stats) and the
 // per-row log-sum-exp and lost non-sink mass (every block then takes the sequential step).
 // kQ8: 0 = bf16 logits; 1 = FP8 logits, Q rounded here per row; 2 = FP8 logits of the
 // rotated Q and K, both as codes from the pre-pass.
-template <int D, int kMode, bool kCausal, int kStats, int kQ8>
-__global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p) {
+// kMulti: the grid covers cells.n configurations (an outer batch dimension), each
+// workgroup taking its cell's bias, scale, order, output and counters from the table.
+template <int D, int kMode, bool kCausal, int kStats, int kQ8, bool kMulti = false>
+__global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
+    const Params p0, const typename Select<kMulti, Cells, NoCells>::type cells) {
   static_assert(kMode != kBf16, "FP8 modes only");
+  static_assert(!kMulti || (kStats < 2 && kQ8 == 0), "configuration cells: bf16 logits, no row diagnostics");
+  Params p = p0;
   constexpr bool kDiag = kStats == 2;
   using G = Geometry<D>;
   // kQ8: Q and K as E4M3 codes, logits on the FP8 MFMA (K = 64 per step), else bf16
@@ -838,7 +857,21 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(const Params p
   const int g = lane / 32, li = lane % 32;
   const int n_rb = (p.N + kBlockRows - 1) / kBlockRows;
   int b, h, rb;
-  decode_block(blockIdx.x, n_rb * p.Hq * p.B, n_rb, p.Hq, kCausal, b, h, rb);
+  if constexpr (kMulti) {
+    // cells are an outer batch dimension: every cell's longest row blocks come first
+    decode_block(blockIdx.x, n_rb * p.Hq * p.B * cells.n, n_rb, p.Hq, kCausal, b, h, rb);
+    const int cell = b / p.B;
+    b -= cell * p.B;
+    p.bias = cells.bias[cell];
+    p.out = cells.out[cell];
+    p.stats = cells.stats[cell];
+    p.S = cells.S[cell];
+    p.inv_S = cells.inv_S[cell];
+    p.p_clamp = cells.p_clamp[cell];
+    p.order = cells.order[cell];
+  } else {
+    decode_block(blockIdx.x, n_rb * p.Hq * p.B, n_rb, p.Hq, kCausal, b, h, rb);
+  }
   const int hk = h / (p.Hq / p.Hkv);
   const int n_tiles = p.N / kKvBlock;
   const int row0 = rb * kBlockRows;
@@ -2263,21 +2296,21 @@ void launch_attn3(const Params& p, hipStream_t stream) {
       hipLaunchKernelGGL((pcast_attn_fwd_bf16<D, kCausal, false>), grid, dim3(kThreads), 0, stream, p);
   } else if (p.k8 && p.q8) {
     if (p.stats)
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, 2>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, 2>), grid, dim3(kThreads), 0, stream, p, NoCells{});
     else
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, 2>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, 2>), grid, dim3(kThreads), 0, stream, p, NoCells{});
   } else if (p.k8) {
     if (p.stats)
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, 1>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, 1>), grid, dim3(kThreads), 0, stream, p, NoCells{});
     else
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, 1>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, 1>), grid, dim3(kThreads), 0, stream, p, NoCells{});
   } else if (p.lse || p.lost) {
-    hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 2, 0>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 2, 0>), grid, dim3(kThreads), 0, stream, p, NoCells{});
   } else {
     if (p.stats)
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, 0>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, 0>), grid, dim3(kThreads), 0, stream, p, NoCells{});
     else
-      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, 0>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, 0>), grid, dim3(kThreads), 0, stream, p, NoCells{});
   }
 }
 
@@ -2295,6 +2328,32 @@ void launch_attn(const Params& p, int mode, int causal, hipStream_t stream) {
     case kMul: launch_attn2<D, kMul>(p, causal, stream); break;
     case kMulClamp: launch_attn2<D, kMulClamp>(p, causal, stream); break;
     default: launch_attn2<D, kBf16>(p, causal, stream); break;
+  }
+}
+
+template <int D, int kMode, bool kCausal>
+void launch_multi3(const Params& p, const Cells& cells, bool stats, hipStream_t stream) {
+  const int n_rb = (p.N + kBlockRows - 1) / kBlockRows;
+  const dim3 grid((unsigned)(n_rb * p.Hq * p.B * cells.n));
+  if (stats)
+    hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, 0, true>), grid, dim3(kThreads), 0, stream, p, cells);
+  else
+    hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, 0, true>), grid, dim3(kThreads), 0, stream, p, cells);
+}
+
+template <int D, int kMode>
+void launch_multi2(const Params& p, const Cells& cells, int causal, bool stats, hipStream_t stream) {
+  if (causal) launch_multi3<D, kMode, true>(p, cells, stats, stream);
+  else launch_multi3<D, kMode, false>(p, cells, stats, stream);
+}
+
+template <int D>
+void launch_multi(const Params& p, const Cells& cells, int mode, int causal, bool stats, hipStream_t stream) {
+  switch (mode) {
+    case kPow2: launch_multi2<D, kPow2>(p, cells, causal, stats, stream); break;
+    case kPow2Clamp: launch_multi2<D, kPow2Clamp>(p, cells, causal, stats, stream); break;
+    case kMul: launch_multi2<D, kMul>(p, cells, causal, stats, stream); break;
+    default: launch_multi2<D, kMulClamp>(p, cells, causal, stats, stream); break;
   }
 }
 
@@ -2672,6 +2731,74 @@ int attn_fwd_pcast_noalloc(const void* Q, const void* K, const void* V, const fl
   rc = enqueue_prep(V, B, Hkv, N, d, S, ws, st);
   if (rc == PCAST_OK) rc = enqueue_attn(Q, K, ws, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats, st);
   return rc;
+}
+
+int attn_fwd_pcast_multi(const void* Q, const void* K, const void* workspace, int B, int Hq, int Hkv, int N, int d,
+                         int causal, int n_cfg, const float* const* bias, const float* S, const int* order,
+                         float* const* out, unsigned long long* const* stats, void* stream) {
+  g_last_error[0] = '\0';
+  if (!Q || !K || !workspace) return fail(PCAST_EINVAL, "Q, K and workspace must be non-null");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(workspace, 16))
+    return fail(PCAST_EINVAL, "Q, K and workspace must be 16-byte aligned");
+  if (causal != 0 && causal != 1) return fail(PCAST_EINVAL, "causal must be 0 or 1");
+  if (n_cfg < 1) return fail(PCAST_EINVAL, "n_cfg = %d: must be positive", n_cfg);
+  if (!S || !order || !out) return fail(PCAST_EINVAL, "the S, order and out arrays must be non-null");
+  for (int i = 0; i < n_cfg; ++i) {
+    if (!out[i] || !aligned(out[i], 16)) return fail(PCAST_EINVAL, "out[%d] must be non-null and 16-byte aligned", i);
+    if (bias && bias[i] && !aligned(bias[i], 4)) return fail(PCAST_EINVAL, "bias[%d] must be 4-byte aligned", i);
+    if (stats && (!stats[i] || !aligned(stats[i], 8)))
+      return fail(PCAST_EINVAL, "stats[%d] must be non-null and 8-byte aligned when stats is given", i);
+    if (order[i] != PCAST_ORDER_FORWARD && order[i] != PCAST_ORDER_REVERSE)
+      return fail(PCAST_EINVAL, "order[%d] must be 0 (forward) or 1 (reverse)", i);
+    if (!std::isfinite(S[i]) || S[i] < 0.0f) return fail(PCAST_EINVAL, "S[%d] must be finite and >= 0", i);
+    if (S[i] == 0.0f) return fail(PCAST_ENOTSUP, "S[%d] = 0: the multi-configuration call runs the FP8 P.V path only", i);
+  }
+  int rc = check_shape(B, Hq, Hkv, N, d, S[0]);
+  if (rc != PCAST_OK) return rc;
+  if ((int64_t)B * Hq * ((N + kBlockRows - 1) / kBlockRows) * kMaxCells > (int64_t)INT32_MAX)
+    return fail(PCAST_ENOTSUP, "grid too large");
+  if ((rc = check_device()) != PCAST_OK) return rc;
+
+  Params p{};
+  p.q = static_cast<const uint16_t*>(Q);
+  p.k = static_cast<const uint16_t*>(K);
+  p.vop = workspace;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N;
+  p.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)d));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // one launch per conversion mode and per kMaxCells cells of that mode, the cells of a
+  // mode split evenly over its launches (no small last launch draining the chip alone)
+  auto mode_of = [&](int i) { return (is_pow2(S[i]) ? kPow2 : kMul) + (S[i] > 448.0f ? 1 : 0); };
+  for (int mode = kPow2; mode <= kMulClamp; ++mode) {
+    int count = 0;
+    for (int i = 0; i < n_cfg; ++i) count += mode_of(i) == mode;
+    if (count == 0) continue;
+    const int launches = (count + kMaxCells - 1) / kMaxCells;
+    const int per_launch = (count + launches - 1) / launches;
+    Cells cells{};
+    auto flush = [&]() -> int {
+      if (cells.n == 0) return PCAST_OK;
+      if (d == 64) launch_multi<64>(p, cells, mode, causal, stats != nullptr, st);
+      else launch_multi<128>(p, cells, mode, causal, stats != nullptr, st);
+      cells.n = 0;
+      const hipError_t e = hipGetLastError();
+      return e == hipSuccess ? PCAST_OK : hip_fail(e, "multi-configuration attention launch");
+    };
+    for (int i = 0; i < n_cfg; ++i) {
+      if (mode_of(i) != mode) continue;
+      const int c = cells.n++;
+      cells.bias[c] = bias ? bias[i] : nullptr;
+      cells.out[c] = out[i];
+      cells.stats[c] = stats ? stats[i] : nullptr;
+      cells.S[c] = S[i];
+      cells.inv_S[c] = 1.0f / S[i];
+      cells.p_clamp[c] = 448.0f / S[i];
+      cells.order[c] = order[i];
+      if (cells.n == per_launch && (rc = flush()) != PCAST_OK) return rc;
+    }
+    if ((rc = flush()) != PCAST_OK) return rc;
+  }
+  return PCAST_OK;
 }
 
 int attn_fwd_pcast_rows(const void* Q, const void* K, const void* workspace, const float* bias, int B,

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_sizes(lib):
-    assert lib.pcast_abi_version() == 9
+    assert lib.pcast_abi_version() == 10
     assert sna.stats_words(4, 32, 8192) == 4 * 32 * 128 * 2
     assert sna.stats_words(1, 1, 100) == 4
     assert sna.workspace_bytes(4, 32, 8192, 128, 256.0) == 4 * 32 * 8192 * 128
@@ -311,3 +311,36 @@ def test_noalloc_rejects_inputs_above_its_scratch(lib):
     # S = 0 keeps a bf16 copy: twice the bytes, so half the keys fit
     assert sna.attn_fwd_pcast_noalloc(FAKE, FAKE, FAKE, 0, 1, 4, 4, 131072, 128, 1, 0.0, 1, FAKE, 0, 0) == sna.PCAST_ENOTSUP
     assert sna.attn_fwd_pcast_noalloc(0, FAKE, FAKE, 0, 1, 1, 1, 64, 64, 1, 256.0, 1, FAKE, 0, 0) == sna.PCAST_EINVAL
+
+
+def _multi(**kw):
+    a = dict(Q=FAKE, K=FAKE, workspace=FAKE, B=1, Hq=2, Hkv=1, N=128, d=128, causal=1, biases=[0, 0],
+             Ss=[256.0, 1.0], orders=[1, 0], outs=[FAKE, FAKE], stats=None, stream=0)
+    a.update(kw)
+    return sna.attn_fwd_pcast_multi(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=0), sna.PCAST_EINVAL),
+    (dict(workspace=FAKE + 4), sna.PCAST_EINVAL),
+    (dict(causal=2), sna.PCAST_EINVAL),
+    (dict(outs=[FAKE, 0]), sna.PCAST_EINVAL),
+    (dict(outs=[FAKE, FAKE + 4]), sna.PCAST_EINVAL),
+    (dict(orders=[1, 3]), sna.PCAST_EINVAL),
+    (dict(Ss=[256.0, float("nan")]), sna.PCAST_EINVAL),
+    (dict(Ss=[256.0, -1.0]), sna.PCAST_EINVAL),
+    (dict(stats=[FAKE, 0]), sna.PCAST_EINVAL),
+    (dict(biases=[FAKE + 2, 0]), sna.PCAST_EINVAL),
+    (dict(Ss=[256.0, 0.0]), sna.PCAST_ENOTSUP),
+    (dict(d=96), sna.PCAST_ENOTSUP),
+    (dict(N=100), sna.PCAST_ENOTSUP),
+    (dict(Hq=3, Hkv=2), sna.PCAST_EINVAL),
+])
+def test_multi_argument_errors(lib, kw, code):
+    assert _multi(**kw) == code
+
+
+def test_multi_needs_a_configuration(lib):
+    a = dict(Q=FAKE, K=FAKE, workspace=FAKE, B=1, Hq=2, Hkv=1, N=128, d=128, causal=1)
+    assert sna.load_library().attn_fwd_pcast_multi(a["Q"], a["K"], a["workspace"], 1, 2, 1, 128, 128, 1, 0,
+                                                   None, None, None, None, None, None) == sna.PCAST_EINVAL
