@@ -276,6 +276,119 @@ def bench_decode(sna, torch, np, synthetic, dev, stream, steps, warmup):
                                     "frac": round(gbs8 / 8000.0, 4), "algorithmic_bytes": w.bytes_qk8}}}
 
 
+def smi_sample() -> dict:
+    """One reading of socket power (W) and shader clock (MHz) from rocm-smi, with the raw
+    power lines kept when no number can be read from them."""
+    import re
+    import subprocess
+    try:
+        txt = subprocess.run(["rocm-smi", "-a"], capture_output=True, text=True, timeout=30).stdout
+    except (OSError, subprocess.SubprocessError) as e:
+        return {"error": str(e)[:200]}
+    out = {}
+    for line in txt.splitlines():
+        low = line.lower()
+        if "power" in low and "(w)" in low and "max" not in low and "power_w" not in out:
+            m = re.search(r"\(w\)\s*:\s*([0-9]+(?:\.[0-9]+)?)", low)
+            if m:
+                out["power_w"] = float(m.group(1))
+            else:
+                out.setdefault("raw", []).append(line.strip()[:160])
+        if "sclk clock level" in low and "sclk_mhz" not in out:
+            m = re.search(r"\((\d+)mhz\)", low)
+            if m:
+                out["sclk_mhz"] = float(m.group(1))
+    return out
+
+
+def run_sustained(launch, seconds: float, stream):
+    """Call launch() back to back for about `seconds` (synchronising every 5 calls) while
+    rocm-smi is sampled once a second after a short warm-up; returns (calls, ms, samples)."""
+    import threading
+
+    import torch
+
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        time.sleep(min(2.0, seconds / 3))
+        while not stop.is_set():
+            samples.append(smi_sample())
+            stop.wait(1.0)
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n, t0 = 0, time.time()
+    e0.record(stream)
+    while time.time() - t0 < seconds:
+        for _ in range(5):
+            launch()
+        n += 5
+        torch.cuda.synchronize()
+    e1.record(stream)
+    e1.synchronize()
+    stop.set()
+    th.join()
+    return n, e0.elapsed_time(e1), samples
+
+
+def smi_summary(samples) -> dict:
+    pw = sorted(x["power_w"] for x in samples if "power_w" in x)
+    ck = sorted(x["sclk_mhz"] for x in samples if "sclk_mhz" in x)
+    out = {"power_w_median": pw[len(pw) // 2] if pw else None, "sclk_mhz_median": ck[len(ck) // 2] if ck else None,
+           "samples": len(samples)}
+    if not pw and samples:
+        out["smi"] = samples[0]
+    return out
+
+
+def bench_roof(seconds: float) -> dict:
+    """Sustained matrix-core rates of the rate probe (libpcast_roof.so): bf16 32x32x16 only,
+    FP8 32x32x64 only, and the attention forward's mix (16 bf16 : 4 FP8 instructions per
+    64-key block), each run back to back for `seconds` on every compute unit while rocm-smi
+    samples socket power and shader clock."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "softmax_numerics_amd", "libpcast_roof.so"))
+    lib.pcast_roof_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pcast_roof_run.restype = ctypes.c_int
+    lib.pcast_roof_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.pcast_roof_flops.restype = ctypes.c_double
+    dev = torch.device("cuda:0")
+    blocks = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {"blocks": blocks, "threads": 256}
+    for mode, name, peak in ((0, "bf16_32x32x16", PEAK_BF16), (1, "fp8_32x32x64", PEAK_FP8),
+                             (2, "forward_mix_16bf16_4fp8", None)):
+        def launch(iters):
+            rc = lib.pcast_roof_run(mode, iters, blocks, ctypes.c_void_p(sink.data_ptr()),
+                                    ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"rate probe launch failed ({rc})")
+        iters = 200
+        launch(iters)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream); launch(iters); e1.record(stream); e1.synchronize()
+        iters = max(1, int(iters * 20.0 / max(e0.elapsed_time(e1), 1e-3)))   # ~20 ms per launch
+        n, ms, samples = run_sustained(lambda: launch(iters), seconds, stream)
+        tflops = lib.pcast_roof_flops(mode, iters, blocks) * n / (ms * 1e-3) / 1e12
+        entry = {"tflops": round(tflops, 1), "launches": n, "iters": iters, "seconds": round(ms * 1e-3, 2),
+                 **smi_summary(samples)}
+        if peak:
+            entry["frac_of_peak"] = round(tflops / peak, 4)
+        res[name] = entry
+        print(f"[bench] rate probe {name}: {tflops:.0f} TFLOP/s, power {entry['power_w_median']} W, "
+              f"sclk {entry['sclk_mhz_median']} MHz", file=sys.stderr, flush=True)
+    bf, f8 = res["bf16_32x32x16"]["tflops"], res["fp8_32x32x64"]["tflops"]
+    # equal flops on each type, at the measured sustained rates
+    res["mixed_roof_from_rates"] = round(1.0 / (0.5 / bf + 0.5 / f8), 1)
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,10 +401,19 @@ def main() -> int:
     ap.add_argument("--no-qk8", action="store_true", help="skip the FP8-logit variant")
     ap.add_argument("--no-decode", action="store_true", help="skip the split-KV decode measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
+                    help="after the timed steps, run the attention kernel back to back for SECONDS with "
+                         "power and clock samples")
+    ap.add_argument("--roof", type=float, default=0.0, metavar="SECONDS",
+                    help="only run the matrix-core rate probe (bf16, FP8 and the forward's mix), SECONDS "
+                         "each, with power and clock samples")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes, 3 times (scale for "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.roof > 0:
+        print(json.dumps({"roof": bench_roof(args.roof)}))
+        return 0
     if args.calibrate_copy:
         import torch
         x = torch.empty(args.calibrate_copy, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -405,6 +527,15 @@ def main() -> int:
         "frac_bf16_peak": round(achieved / PEAK_BF16, 4),
         "frac_mixed_roof": round(achieved / mixed_roof, 4),
     }
+
+    if args.sustain > 0:
+        launch = lambda: sna.attn_fwd_pcast_prepared(  # noqa: E731
+            q.data_ptr(), k.data_ptr(), ws.data_ptr(), bias_t.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d,
+            int(w.causal), S, order, out.data_ptr(), 0 if stats is None else stats.data_ptr(), sh)
+        n, ms, samples = run_sustained(launch, args.sustain, stream)
+        result["sustained"] = {"calls": n, "ms_per_call": round(ms / n, 5),
+                               "tflops": round(flops * n / (ms * 1e-3) / 1e12, 1), **smi_summary(samples)}
+        print(f"[bench] sustained: {result['sustained']}", file=sys.stderr, flush=True)
 
     out_rev = out.cpu().numpy() if not args.no_cpu_baseline else None
     st_rev = None if stats is None else stats.cpu().numpy().reshape(-1, 2)

@@ -11,6 +11,9 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "attn_fwd_pcast.hip")
 SRC_HOST = os.path.join(PKG, "csrc", "collapse_model.cpp")
 LIB = os.path.join(PKG, "libpcast_attn.so")
+# the benchmark's matrix-core rate probe (not part of the attention path)
+SRC_ROOF = os.path.join(PKG, "csrc", "mfma_roof.hip")
+LIB_ROOF = os.path.join(PKG, "libpcast_roof.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -44,6 +47,10 @@ def build(verbose: bool = False) -> str:
     if verbose and err:
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
+    roof = subprocess.run([HIPCC, *FLAGS, SRC_ROOF, "-o", LIB_ROOF + ".tmp"], capture_output=True, text=True)
+    if roof.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the rate probe ({roof.returncode}):\n{roof.stderr}")
+    os.replace(LIB_ROOF + ".tmp", LIB_ROOF)
     return LIB
 
 
