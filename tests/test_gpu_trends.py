@@ -96,3 +96,36 @@ def test_gain_grows_with_n(sweep):
               for n in (1024, 2048, 4096)]
     print(f"[case] trends: fwd S=1 / rev S=256 at N=1024, 2048, 4096: {ratios}", flush=True)
     assert ratios[0] < ratios[1] < ratios[2]
+
+
+@pytest.mark.parametrize("name", ["gqa", "long"])
+def test_gain_at_scale(sna, name):
+    """The forward-S=1 / reverse-S=256 MSE ratio at the GQA (N = 65536) and Long
+    (N = 131072) shapes, on 256 rows sampled uniformly over heads and positions: the
+    GPU's MSE against fp64 attention agrees with the oracle's kernel-mode MSE on the
+    same rows (within 3 %), and the ratio exceeds the Sweep shape's (1.18 at N = 4096).
+    In the oracle's pages mode (V exact) the same ratio is about 2 at N = 4096, 3.3
+    at 16k, 5.9 at 64k and 11 at 128k (Delta = 7)."""
+    w = synthetic.WORKLOADS[name]
+    print(f"\n[case] trends at scale: {name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N}", flush=True)
+    qb, kb, vb = synthetic.qkv_bf16(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed)
+    q, k, v = (_parity.to_gpu_bf16(x) for x in (qb, kb, vb))
+    rng = np.random.default_rng(5)
+    ids = np.sort(rng.choice(w.B * w.Hq * w.N, 256, replace=False))
+    bias = synthetic.sink_bias(w.N, 7.0)
+    bt = torch.from_numpy(bias).cuda()
+    idx = torch.from_numpy(ids).cuda()
+    mse = {}
+    for S, order in ((1.0, "forward"), (256.0, "reverse")):
+        out, _ = sna.forward(q, k, v, bt, causal=True, S=S, order=order)
+        got = out.view(-1, w.d)[idx].double().cpu().numpy()
+        del out
+        torch.cuda.synchronize()
+        r = core.rows(qb, kb, vb, bias, True, S, 0 if order == "forward" else 1, "kernel", row_ids=ids)
+        mse[S] = (float(np.mean((got - r["o1"]) ** 2)), float(np.mean((r["o2"] - r["o1"]) ** 2)))
+        print(f"[case] trends at scale: {name} S={S} {order}: MSE gpu {mse[S][0]:.4e} oracle {mse[S][1]:.4e}",
+              flush=True)
+        assert abs(mse[S][0] - mse[S][1]) <= 0.03 * mse[S][1]
+    ratio = mse[1.0][0] / mse[256.0][0]
+    print(f"[case] trends at scale: {name}: fwd S=1 / rev S=256 = {ratio:.2f}", flush=True)
+    assert ratio > 1.3

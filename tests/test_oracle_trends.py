@@ -85,3 +85,26 @@ def test_reverse_256_no_underflow_beyond_sink_block(sweep_inputs, delta):
     assert r["zero_beyond_block0"].sum() == 0
     f = _run(sweep_inputs, delta, 1.0, 0, mode="kernel")
     assert f["zero_beyond_block0"].sum() > 0
+
+
+@pytest.mark.slow
+def test_gain_reaches_the_pages_range_at_long_sequences():
+    """[PC-it] section 4 reports 3-10x lower MSE for reverse order with S = 256 than for
+    forward order with S = 1, growing with N.  In pages mode (V exact) on 512 rows
+    sampled uniformly over positions (Delta = 7, one head, d = 128, causal), the ratio is
+    about 1.9 at N = 4096, 3.3 at 16384 and 5.9 at 65536: inside the pages' range from
+    N = 16k on."""
+    rng = np.random.default_rng(11)
+    ratios = []
+    for n in (4096, 16384, 65536):
+        q, k, v = synthetic.qkv_bf16(1, 1, 1, n, D, 2)
+        rows = np.sort(rng.choice(n, 512, replace=False))
+        bias = synthetic.sink_bias(n, 7.0)
+        mse = []
+        for S, order in ((1.0, 0), (256.0, 1)):
+            r = core.rows(q, k, v, bias, True, S, order, "pages", row_ids=rows)
+            mse.append(float(np.mean((r["o2"] - r["o1"]) ** 2)))
+        ratios.append(mse[0] / mse[1])
+    print(f"fwd S=1 / rev S=256 (pages mode) at N = 4096, 16384, 65536: {ratios}")
+    assert ratios[0] < ratios[1] < ratios[2]
+    assert ratios[1] > 3.0 and ratios[2] > 5.0
