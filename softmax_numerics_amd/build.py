@@ -24,6 +24,10 @@ FLAGS = [
     # are still honoured), so max/min need no NaN canonicalisation; host code
     # keeps full IEEE semantics for its argument checks
     "-Xarch_device", "-fno-honor-nans",
+    # matrix-core results and accumulators in ordinary VGPRs (AGPRs only when a kernel
+    # runs out of them): the backward and decode kernels read their logits with VALU
+    # instructions, which would otherwise copy every value out of the AGPRs first
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

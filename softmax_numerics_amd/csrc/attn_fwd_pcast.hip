@@ -2182,12 +2182,11 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
     constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
     if (it + 1 < n_it) load(it + 1, nxt);
     const int rrow0 = rblk_of(it) * kKvBlock;
-    if (wave_active && (!kCausal || rrow0 + kKvBlock - 1 >= wkey0)) {
-      if (kCausal && rrow0 < wkey0 + kRowsPerWave - 1)
-        block(cur_c, std::true_type{}, rrow0);
-      else
-        block(cur_c, std::false_type{}, rrow0);
-    }
+    // one code path for masked and unmasked blocks (the mask is exact and masks nothing
+    // past the diagonal): with two, the register allocator moves the dK / dV
+    // accumulators between register files where the paths join
+    if (wave_active && (!kCausal || rrow0 + kKvBlock - 1 >= wkey0))
+      block(cur_c, std::integral_constant<bool, kCausal>{}, rrow0);
     wait_loads();
     __syncthreads();
   };
