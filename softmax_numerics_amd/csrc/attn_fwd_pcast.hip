@@ -2094,6 +2094,7 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
     constexpr int kAhead = 3, kRing = kAhead + 1;
     const uint8_t* ql = qbuf(cur) + li * kRow;
     const uint8_t* ol = obuf(cur) + li * kRow;
+    const int lim = mykey - rrow0 - 4 * g;
     f32x16_t sacc[2], pacc[2];
     uint32_t pp[2][8], ps[2][8];
     bf16x8_t ring[kRing];
@@ -2150,8 +2151,10 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
       float pj0 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][2 * w], c, bkl) - lr.x * kLog2e);
       float pj1 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][2 * w + 1], c, bkl) - lr.y * kLog2e);
       if constexpr (kDiag) {
-        if (rrow0 + slot_key(g, 16 * hh + 2 * w) < mykey) pj0 = 0.0f;
-        if (rrow0 + slot_key(g, 16 * hh + 2 * w + 1) < mykey) pj1 = 0.0f;
+        // row rrow0 + slot_key(g, j) is masked when it lies above the key: slot_key(0, j) <
+        // lim with lim = mykey - rrow0 - 4 g, one compare with a constant per pair
+        if (slot_key(0, 16 * hh + 2 * w) < lim) pj0 = 0.0f;
+        if (slot_key(0, 16 * hh + 2 * w + 1) < lim) pj1 = 0.0f;
       }
       pp[hh][w] = cast2_bf16(pj0, pj1);
       ps[hh][w] = cast2_bf16(pj0 * (pacc[hh][2 * w] - dr.x), pj1 * (pacc[hh][2 * w + 1] - dr.y));
