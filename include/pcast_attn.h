@@ -164,7 +164,9 @@ int attn_fwd_pcast_prepared(const void* Q, const void* K, const void* workspace,
  * out        host array of n_cfg device pointers, float32 [B][Hq][N][d], 16-byte aligned.
  * stats      host array of n_cfg device pointers (uint64 [pcast_stats_words(B, Hq, N)],
  *            8-byte aligned, all non-null), or NULL for no counting.
- * The host arrays are read during the call only.  Configurations are grouped by how
+ * The out and stats buffers of different configurations must not overlap (their
+ * writes are unordered).  The host arrays are read during the call only.
+ * Configurations are grouped by how
  * P is converted (S a power of two or not, S above 448 or not), at most 64 per launch.
  * Allocates nothing; errors as for attn_fwd_pcast_prepared.
  */
