@@ -259,7 +259,8 @@ int pcast_collapse_check(const float* bias, int N, double S, int order, double* 
  * dQ       device, float32 [B][Hq][N][d]; dK, dV device, float32 [B][Hkv][N][d];
  *          written completely.
  * workspace  device, pcast_bwd_workspace_bytes(B, Hq, Hkv, N, d) bytes, 16-byte
- *          aligned, owned by the caller (the row dots D = dO . O, fp32 [B][Hq][N]).
+ *          aligned, owned by the caller (per row, fp32 [B][Hq][N] each: -D with the row dot
+ *          D = dO . O, then -lse * sqrt(d)).
  * All products run on bf16 matrix cores with fp32 accumulation; P and dS are
  * rounded to bf16 where they are operands.  Allocates nothing; errors as for
  * attn_fwd_pcast, plus PCAST_ENOTSUP when one head's rows (N * d * 2 bytes)

@@ -376,7 +376,8 @@ struct Params {
   const uint16_t* v;
   const uint16_t* dout;
   const float* lse_in;
-  const float* dvec;
+  const float* dvec;      // -D = -(dO . O) per row
+  const float* nls;       // -lse * sqrt(d) per row: lse in the logits' own units
   float* dq;
   float* dk;
   float* dv;
@@ -1744,10 +1745,13 @@ __global__ __launch_bounds__(256) void pcast_decode_merge(const Params p) {
 // rounded to bf16 for the products that take them as operands.
 // ---------------------------------------------------------------------------
 
-// D_i = dO_i . O_i, eight lanes per row.
+// Per row i: -D_i = -(dO_i . O_i), eight lanes per row, and -lse_i * sqrt(d), the
+// log-sum-exp in the units of the raw logits q.k (both start the dK / dV kernel's
+// accumulators, so that the products come out as dP - D and s - lse).
 template <int D>
 __global__ __launch_bounds__(256) void pcast_bwd_rowdot(const uint16_t* __restrict__ dout, const float* __restrict__ o,
-                                                        float* __restrict__ dvec, int64_t rows) {
+                                                        const float* __restrict__ lse, float* __restrict__ dvec,
+                                                        float* __restrict__ nls, float sqrt_d, int64_t rows) {
   constexpr int kPer = D / 8;  // elements per lane
   const int64_t row = (int64_t)blockIdx.x * 32 + threadIdx.x / 8;
   const int part = threadIdx.x % 8;
@@ -1773,7 +1777,10 @@ __global__ __launch_bounds__(256) void pcast_bwd_rowdot(const uint16_t* __restri
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 4);
-  if (row < rows && part == 0) dvec[row] = acc;
+  if (row < rows && part == 0) {
+    dvec[row] = -acc;
+    nls[row] = -lse[row] * sqrt_d;
+  }
 }
 
 // dQ: a workgroup of 8 waves (two per SIMD) takes 256 query rows of one (b, h),
@@ -1820,7 +1827,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Para
   const int64_t row = ((int64_t)b * p.Hq + h) * p.N + myrow;
 
   bf16x8_t qf[G::kQSteps], df[G::kQSteps];
-  float lse2 = 0.0f, drow = 0.0f;
+  float lse2 = 0.0f, ndrow = 0.0f;
   if (wave_active) {
     const uint16_t* qrow = p.q + row * D + g * 8;
     const uint16_t* drw = p.dout + row * D + g * 8;
@@ -1830,7 +1837,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Para
       df[s] = *reinterpret_cast<const bf16x8_t*>(drw + s * 16);
     }
     lse2 = p.lse_in[row] * kLog2e;
-    drow = p.dvec[row];
+    ndrow = p.dvec[row];
   }
   const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(p.k + ((int64_t)b * p.Hkv + hk) * p.N * D);
   const __amdgpu_buffer_rsrc_t vres = buffer_rsrc(p.v + ((int64_t)b * p.Hkv + hk) * p.N * D);
@@ -1905,7 +1912,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Para
           for (int w = 0; w < 8; ++w) {
             const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * w], c, -lse2));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * w + 1], c, -lse2));
-            pw[w] = cast2_bf16(p0 * (pacc[2 * w] - drow), p1 * (pacc[2 * w + 1] - drow));
+            pw[w] = cast2_bf16(p0 * (pacc[2 * w] + ndrow), p1 * (pacc[2 * w + 1] + ndrow));
           }
         } else {
 #pragma unroll
@@ -1921,7 +1928,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void pcast_attn_bwd_dq(const Para
               const float x = has_bias ? fmaf(sacc[jj], c, bj * kLog2e) - lse2 : fmaf(sacc[jj], c, -lse2);
               float pj = __builtin_amdgcn_exp2f(x);
               if (diag && key0 + slot_key(g, j) > myrow) pj = 0.0f;
-              ds2[e] = pj * (pacc[jj] - drow);
+              ds2[e] = pj * (pacc[jj] + ndrow);
             }
             pw[w] = cast2_bf16(ds2[0], ds2[1]);
           }
@@ -2065,7 +2072,7 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
       buffer_to_lds16(os, toff + rsrc[i], obuf(buf) + (wave * kLoads + i) * 1024);
     }
     if (wave == 0) {
-      buffer_to_lds4(buffer_rsrc(p.lse_in + hrow), (r * kKvBlock + lane) * 4, lbuf(buf));
+      buffer_to_lds4(buffer_rsrc(p.nls + hrow), (r * kKvBlock + lane) * 4, lbuf(buf));
       buffer_to_lds4(buffer_rsrc(p.dvec + hrow), (r * kKvBlock + lane) * 4, dbuf(buf));
     }
   };
@@ -2084,10 +2091,13 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
   // half 0, then of half 1 while half 0's P and dS are formed, then half 0's dV and
   // dK k-steps while half 1's are formed, then half 1's.  Each MFMA sits in a chunk
   // of its own with the operand fragment of the MFMA kAhead later and a slice of
-  // the VALU work; sched_barrier fences keep the chunks in order.
-  auto block = [&](auto cur_c, auto diag_c, int rrow0) __attribute__((always_inline)) {
+  // the VALU work; sched_barrier fences keep the chunks in order.  The S
+  // accumulator of a half starts at -lse * sqrt(d) of its rows (-inf where the
+  // causal mask hides the pair) and the dP accumulator at -D, so the products
+  // come out as s - lse and dP - D and a pair costs one fma, one exp2, one
+  // multiply and a conversion.
+  auto block = [&](auto cur_c, bool diag, int rrow0) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value;
-    constexpr bool kDiag = decltype(diag_c)::value;
     constexpr int kA = 2 * G::kQSteps;   // S and dP MFMAs of one half
     constexpr int kC = 4 * G::kDTiles;   // dV and dK MFMAs of one half (two k-steps)
     constexpr int kM = 2 * kA + 2 * kC;  // the block's MFMAs
@@ -2098,7 +2108,26 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
     f32x16_t sacc[2], pacc[2];
     uint32_t pp[2][8], ps[2][8];
     bf16x8_t ring[kRing];
-    float2 lq2[2], dq2[2];
+    // accumulator starts: element e of half hh is row 32 hh + 8 (e / 4) + 4 g + e % 4
+    // of the block (slot order), whose -lse sqrt(d) and -D sit in the staged rows
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 a = *reinterpret_cast<const float4*>(lbuf(cur) + 32 * hh + 8 * q + 4 * g);
+        const float4 e = *reinterpret_cast<const float4*>(dbuf(cur) + 32 * hh + 8 * q + 4 * g);
+        sacc[hh][4 * q] = a.x; sacc[hh][4 * q + 1] = a.y; sacc[hh][4 * q + 2] = a.z; sacc[hh][4 * q + 3] = a.w;
+        pacc[hh][4 * q] = e.x; pacc[hh][4 * q + 1] = e.y; pacc[hh][4 * q + 2] = e.z; pacc[hh][4 * q + 3] = e.w;
+      }
+    if (kCausal && diag) {
+      // row rrow0 + slot_key(g, j) is masked when it lies above the key: slot_key(0, j) <
+      // lim with lim = mykey - rrow0 - 4 g
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (slot_key(0, 16 * hh + e) < lim) sacc[hh][e] = -INFINITY;
+    }
     // MFMA i: i < 2 kA: half i / kA, k-step (i % kA) / 2, S (even) or dP (odd);
     // then half hh = (i - 2 kA) / kC and q = (i - 2 kA) % kC: k-step 2 hh + q / (2 kDTiles),
     // tile (q / 2) % kDTiles, dV (even) or dK (odd)
@@ -2121,9 +2150,9 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
       if constexpr (i < 2 * kA) {
         constexpr int hh = i / kA, r = i % kA, st = r / 2;
         if constexpr (r % 2 == 0)
-          sacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[st], st == 0 ? f32x16_t{} : sacc[hh], 0, 0, 0);
+          sacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[st], sacc[hh], 0, 0, 0);
         else
-          pacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[st], st == 0 ? f32x16_t{} : pacc[hh], 0, 0, 0);
+          pacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[st], pacc[hh], 0, 0, 0);
       } else {
         constexpr int r = i - 2 * kA, hh = r / kC, q = r % kC, s2 = q / (2 * G::kDTiles), dt = (q / 2) % G::kDTiles;
         const uint32_t* src = q % 2 == 0 ? pp[hh] : ps[hh];
@@ -2134,34 +2163,15 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
           dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bw), dkacc[dt], 0, 0, 0);
       }
     };
-    // lse and D of rows 2w, 2w + 1 of half hh (adjacent slots) for unit n = 8 hh + w,
-    // read one unit ahead
-    auto rowstats = [&](auto nc) __attribute__((always_inline)) {
-      constexpr int n = decltype(nc)::value;
-      if constexpr (n < 16) {
-        const int k = slot_key(g, 2 * n);
-        lq2[n % 2] = *reinterpret_cast<const float2*>(lbuf(cur) + k);
-        dq2[n % 2] = *reinterpret_cast<const float2*>(dbuf(cur) + k);
-      }
-    };
     auto unit = [&](auto nc) __attribute__((always_inline)) {  // P and dS of rows 2w, 2w + 1
       constexpr int n = decltype(nc)::value, hh = n / 8, w = n % 8;
-      const float2 lr = lq2[n % 2], dr = dq2[n % 2];
-      rowstats(IC<n + 1>{});
-      float pj0 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][2 * w], c, bkl) - lr.x * kLog2e);
-      float pj1 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][2 * w + 1], c, bkl) - lr.y * kLog2e);
-      if constexpr (kDiag) {
-        // row rrow0 + slot_key(g, j) is masked when it lies above the key: slot_key(0, j) <
-        // lim with lim = mykey - rrow0 - 4 g, one compare with a constant per pair
-        if (slot_key(0, 16 * hh + 2 * w) < lim) pj0 = 0.0f;
-        if (slot_key(0, 16 * hh + 2 * w + 1) < lim) pj1 = 0.0f;
-      }
+      const float pj0 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][2 * w], c, bkl));
+      const float pj1 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][2 * w + 1], c, bkl));
       pp[hh][w] = cast2_bf16(pj0, pj1);
-      ps[hh][w] = cast2_bf16(pj0 * (pacc[hh][2 * w] - dr.x), pj1 * (pacc[hh][2 * w + 1] - dr.y));
+      ps[hh][w] = cast2_bf16(pj0 * pacc[hh][2 * w], pj1 * pacc[hh][2 * w + 1]);
     };
 #define PCAST_FENCE __builtin_amdgcn_sched_barrier(0)
     static_for<kAhead>([&](auto ic) __attribute__((always_inline)) { fetch(ic); });
-    rowstats(IC<0>{});
     PCAST_FENCE;
     static_for<kM>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
@@ -2185,11 +2195,11 @@ __global__ __launch_bounds__(kThreads, 1) void pcast_attn_bwd_dkv(const Params p
     constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
     if (it + 1 < n_it) load(it + 1, nxt);
     const int rrow0 = rblk_of(it) * kKvBlock;
-    // one code path for masked and unmasked blocks (the mask is exact and masks nothing
-    // past the diagonal): with two, the register allocator moves the dK / dV
-    // accumulators between register files where the paths join
+    // one code path for masked and unmasked blocks, the mask only in the accumulator
+    // starts (with two paths the register allocator moves the dK / dV accumulators
+    // between register files where they join)
     if (wave_active && (!kCausal || rrow0 + kKvBlock - 1 >= wkey0))
-      block(cur_c, std::integral_constant<bool, kCausal>{}, rrow0);
+      block(cur_c, rrow0 < wkey0 + kRowsPerWave - 1, rrow0);
     wait_loads();
     __syncthreads();
   };
@@ -2361,16 +2371,17 @@ void launch_multi(const Params& p, const Cells& cells, int mode, int causal, boo
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
-// Workspace of the backward: slot-order transposes of K, Q and dO (bf16, the
-// layout pcast_prep_v writes for V), then the row dots D (fp32); 256-aligned parts.
+// Workspace of the backward: per row, -D = -(dO . O), then -lse * sqrt(d) (fp32,
+// [B][Hq][N] each); 256-aligned parts.
 struct BwdLayout {
-  size_t dvec, total;
+  size_t dvec, nls, total;
 };
 BwdLayout bwd_layout(int B, int Hq, int /*Hkv*/, int N, int /*d*/) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   BwdLayout l;
   l.dvec = 0;
-  l.total = up((size_t)B * Hq * N * 4);
+  l.nls = up((size_t)B * Hq * N * 4);
+  l.total = l.nls + up((size_t)B * Hq * N * 4);
   return l;
 }
 
@@ -2845,19 +2856,23 @@ int attn_bwd_pcast(const void* Q, const void* K, const void* V, const float* O, 
   const uint16_t* Qb = static_cast<const uint16_t*>(Q);
   const uint16_t* Kb = static_cast<const uint16_t*>(K);
   const uint16_t* dOb = static_cast<const uint16_t*>(dO);
+  const float sqrt_d = std::sqrt((float)d);
+  float* dvec = reinterpret_cast<float*>(base + l.dvec);
+  float* nls = reinterpret_cast<float*>(base + l.nls);
   if (d == 64)
-    hipLaunchKernelGGL(pcast_bwd_rowdot<64>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, st, dOb, O,
-                       reinterpret_cast<float*>(base + l.dvec), rows);
+    hipLaunchKernelGGL(pcast_bwd_rowdot<64>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, st, dOb, O, lse,
+                       dvec, nls, sqrt_d, rows);
   else
-    hipLaunchKernelGGL(pcast_bwd_rowdot<128>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, st, dOb, O,
-                       reinterpret_cast<float*>(base + l.dvec), rows);
+    hipLaunchKernelGGL(pcast_bwd_rowdot<128>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, st, dOb, O, lse,
+                       dvec, nls, sqrt_d, rows);
   Params p{};
   p.q = Qb;
   p.k = Kb;
   p.v = static_cast<const uint16_t*>(V);
   p.dout = dOb;
   p.lse_in = lse;
-  p.dvec = reinterpret_cast<const float*>(base + l.dvec);
+  p.dvec = dvec;
+  p.nls = nls;
   p.bias = bias;
   p.dq = dQ;
   p.dk = dK;

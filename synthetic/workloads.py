@@ -89,8 +89,9 @@ class DecodeWorkload:
 
 
 DECODE_WORKLOADS = {
-    # one new token for each of 16 sequences of 16k cached keys, GQA 32 / 8
-    "decode": DecodeWorkload("decode", 16, 32, 8, 1, 16384, 128, 1024, 6,
+    # one new token for each of 16 sequences of 16k cached keys, GQA 32 / 8; ranges of
+    # 2048 keys make 16 * 8 * 8 = 1024 split workgroups, one wave for each SIMD of 256 CUs
+    "decode": DecodeWorkload("decode", 16, 32, 8, 1, 16384, 128, 2048, 6,
                              ((7.0, 256.0, 1), (7.0, 1.0, 0))),
     # four new tokens of one 128k-key sequence
     "decode_long": DecodeWorkload("decode_long", 1, 32, 8, 4, 131072, 128, 4096, 7,

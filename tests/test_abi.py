@@ -209,7 +209,7 @@ def test_decode_qk8_argument_errors(lib, kw, code):
 def test_bwd_workspace_layout(lib):
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     for B, Hq, Hkv, N, d in ((4, 32, 32, 8192, 128), (1, 3, 1, 64, 64)):
-        want = up(4 * B * Hq * N)  # the row dots D, fp32
+        want = 2 * up(4 * B * Hq * N)  # -D and -lse * sqrt(d) per row, fp32
         assert sna.bwd_workspace_bytes(B, Hq, Hkv, N, d) == want
 
 
