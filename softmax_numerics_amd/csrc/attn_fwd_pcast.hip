@@ -980,16 +980,43 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
 
   // S^T = K Q^T for the key block in K buffer `buf`: two 32-key halves, fp32 accumulation
   const int xk = SK::key(li);  // rows li and li + 32 share the swizzle key
+  // The lane's byte offset of each K chunk it reads within a tile (row li, swizzled
+  // chunk), computed once; the empty asm keeps the compiler from splitting it again
+  // into a row part and a chunk part, so that a read is this register plus an
+  // immediate (buffer, 32-key half) and needs no add.
+  constexpr int kKChunks = kQ8 ? 2 * kSSteps : kSSteps;
+  int koff[kKChunks];
+#pragma unroll
+  for (int i = 0; i < kKChunks; ++i) {
+    const int chunk = kQ8 ? (4 * (i / 2) + 2 * g + i % 2) : (2 * i + g);
+    koff[i] = li * kKRow + ((chunk ^ xk) << 4);
+    asm volatile("" : "+v"(koff[i]));
+  }
   // K fragment of 32-key half kb and k-step s from K buffer `buf`
   auto kread = [&](int buf, int kb, int s) __attribute__((always_inline)) -> KFrag {
-    const uint8_t* kl = kbuf(buf) + (kb * 32 + li) * kKRow;
+    const uint8_t* kl = kbuf(buf) + kb * 32 * kKRow;
     if constexpr (kQ8 != 0) {
-      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kl + (((4 * s + 2 * g) ^ xk) << 4));
-      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(kl + (((4 * s + 2 * g + 1) ^ xk) << 4));
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kl + koff[2 * s]);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(kl + koff[2 * s + 1]);
       return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     } else {
-      return *reinterpret_cast<const bf16x8_t*>(kl + (((2 * s + g) ^ xk) << 4));
+      return *reinterpret_cast<const bf16x8_t*>(kl + koff[s]);
     }
+  };
+  // the same for the two V chunks a lane reads per 32-column tile (row li of the tile)
+  int voff[2];
+  {
+    const int xv = SV::key(li);  // rows dt*32 + li share the swizzle key
+    voff[0] = li * kVRow + (((2 * g) ^ xv) << 4);
+    voff[1] = li * kVRow + (((2 * g + 1) ^ xv) << 4);
+    asm volatile("" : "+v"(voff[0]));
+    asm volatile("" : "+v"(voff[1]));
+  }
+  auto vread = [&](int buf, int dt) __attribute__((always_inline)) -> i32x8_t {
+    const uint8_t* vl = vbuf(buf) + dt * 32 * kVRow;
+    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(vl + voff[0]);
+    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(vl + voff[1]);
+    return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
   auto smma = [&](const KFrag& a, int s, const f32x16_t& acc) __attribute__((always_inline)) -> f32x16_t {
     if constexpr (kQ8 != 0) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[s], acc, 0, 0, 0, 0, 0, 0);
@@ -1009,16 +1036,9 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
   // O^T += V8^T P8^T for the V block in V buffer `buf`
   auto accumulate = [&](int buf, const i32x8_t& pb) __attribute__((always_inline)) {
-    const uint8_t* vl = vbuf(buf) + li * kVRow;
-    const int xv = SV::key(li);  // rows dt*32 + li share the swizzle key
-    const int vlo = ((2 * g) ^ xv) << 4, vhi = ((2 * g + 1) ^ xv) << 4;
 #pragma unroll
-    for (int dt = 0; dt < G::kDTiles; ++dt) {
-      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vlo);
-      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vhi);
-      const i32x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, oacc[dt], 0, 0, 0, 0, 0, 0);
-    }
+    for (int dt = 0; dt < G::kDTiles; ++dt)
+      oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vread(buf, dt), pb, oacc[dt], 0, 0, 0, 0, 0, 0);
   };
   auto rescale = [&](float alpha) __attribute__((always_inline)) {
     // alpha == 1 in every lane: an exact no-op, skipped
@@ -1214,14 +1234,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
       // The rescale owed by block j-1 comes first, skipped when no row's max grew.
       rescale(alpha_pend);
       i32x8_t& pb = pbuf[cur];
-      const uint8_t* vl = vbuf(nxt) + li * kVRow;
-      const int xv = SV::key(li);
-      const int vlo = ((2 * g) ^ xv) << 4, vhi = ((2 * g + 1) ^ xv) << 4;
-      auto vfrag = [&](int dt) __attribute__((always_inline)) {
-        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vlo);
-        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(vl + dt * 32 * kVRow + vhi);
-        return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      };
+      auto vfrag = [&](int dt) __attribute__((always_inline)) { return vread(nxt, dt); };
       auto kfrag = [&](int f) __attribute__((always_inline)) {  // f = half * kSSteps + step
         return kread(nxt, f / kSSteps, f % kSSteps);
       };
