@@ -167,7 +167,7 @@ int attn_fwd_pcast_prepared(const void* Q, const void* K, const void* workspace,
  * The out and stats buffers of different configurations must not overlap (their
  * writes are unordered).  The host arrays are read during the call only.
  * Configurations are grouped by how
- * P is converted (S a power of two or not, S above 448 or not), at most 64 per launch.
+ * P is converted (S a power of two or not, S above 448 or not), at most 112 per launch.
  * Allocates nothing; errors as for attn_fwd_pcast_prepared.
  */
 int attn_fwd_pcast_multi(const void* Q, const void* K, const void* workspace, int B, int Hq, int Hkv, int N, int d,

@@ -486,6 +486,18 @@ __device__ inline float halves_max(float x) {
   return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
 }
 
+// Sum over the 64 lanes of a wave, returned uniform: DPP row shifts leave each
+// 16-lane row's total in its lane 15, the two row broadcasts carry them into lane 63.
+__device__ inline unsigned int wave_sum(unsigned int x) {
+  x += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return (unsigned int)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 __device__ inline float halves_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
                                                   false, false);
@@ -767,12 +779,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params 
       }
   }
   if constexpr (kStats) {
-    unsigned int a = cnt_tot, z = cnt_zero;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      a += __shfl_xor(a, off);
-      z += __shfl_xor(z, off);
-    }
+    const unsigned int a = wave_sum(cnt_tot), z = wave_sum(cnt_zero);
     if (lane == 0 && wave_active) {
       atomicAdd(&lds_cnt[wave / 2][0], a);
       atomicAdd(&lds_cnt[wave / 2][1], z);
@@ -800,15 +807,19 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params 
 // Several configurations of one forward in one launch: the cells share Q, K and the V
 // operand copy, each has its own bias, scale, key-block order, output and counters.
 // The table travels by value in the kernel arguments.
-constexpr int kMaxCells = 64;
+// Configurations per launch: the table travels in the kernel arguments (4 KiB with
+// the Params); 1/S and the clamp 448/S are formed in the kernel with the same
+// correctly rounded division as on the host.
+constexpr int kMaxCells = 112;
 struct Cells {
   const float* bias[kMaxCells];
   float* out[kMaxCells];
   unsigned long long* stats[kMaxCells];
-  float S[kMaxCells], inv_S[kMaxCells], p_clamp[kMaxCells];
+  float S[kMaxCells];
   int order[kMaxCells];
   int n;
 };
+static_assert(sizeof(Cells) + sizeof(Params) <= 4096, "kernel arguments above 4 KiB");
 struct NoCells {};
 
 // kStats: 0 = no counting; 1 = underflow counters; 2 = counters (if p.stats) and the
@@ -867,8 +878,8 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
     p.out = cells.out[cell];
     p.stats = cells.stats[cell];
     p.S = cells.S[cell];
-    p.inv_S = cells.inv_S[cell];
-    p.p_clamp = cells.p_clamp[cell];
+    p.inv_S = 1.0f / p.S;
+    p.p_clamp = 448.0f / p.S;
     p.order = cells.order[cell];
   } else {
     decode_block(blockIdx.x, n_rb * p.Hq * p.B, n_rb, p.Hq, kCausal, b, h, rb);
@@ -1398,12 +1409,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
   }
   if constexpr (kStats) {
     // fast blocks: every one of the lane's 32 pairs is visible and non-sink
-    unsigned int a = cnt_tot + 32u * n_fast, z = cnt_zero + 32u * n_fast - (cnt_nz_fast >> 7);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      a += __shfl_xor(a, off);
-      z += __shfl_xor(z, off);
-    }
+    const unsigned int a = wave_sum(cnt_tot + 32u * n_fast), z = wave_sum(cnt_zero + 32u * n_fast - (cnt_nz_fast >> 7));
     if (lane == 0 && wave_active) {
       atomicAdd(&lds_cnt[wave / 2][0], a);
       atomicAdd(&lds_cnt[wave / 2][1], z);
@@ -2817,8 +2823,6 @@ int attn_fwd_pcast_multi(const void* Q, const void* K, const void* workspace, in
       cells.out[c] = out[i];
       cells.stats[c] = stats ? stats[i] : nullptr;
       cells.S[c] = S[i];
-      cells.inv_S[c] = 1.0f / S[i];
-      cells.p_clamp[c] = 448.0f / S[i];
       cells.order[c] = order[i];
       if (cells.n == per_launch && (rc = flush()) != PCAST_OK) return rc;
     }

@@ -21,9 +21,10 @@ def sna():
     return softmax_numerics_amd
 
 
-# every conversion mode (powers of two, 448 and 3 multiply, 512 clamps), both orders, with
-# and without a sink, one configuration without any bias
-CONFIGS = [(dl, S, o) for dl in (None, 0.0, 7.0) for S in (1.0, 2.0, 256.0, 448.0, 512.0, 3.0) for o in (0, 1)]
+# every conversion mode (powers of two, 448 and 3 multiply, 512 clamps, 600 multiplies and
+# clamps), both orders, with and without a sink, one configuration without any bias
+CONFIGS = [(dl, S, o) for dl in (None, 0.0, 7.0) for S in (1.0, 2.0, 256.0, 448.0, 512.0, 3.0, 600.0)
+           for o in (0, 1)]
 
 
 def _check(sna, B, Hq, Hkv, N, d, causal, configs, seed, stats=True):
@@ -54,8 +55,8 @@ def test_multi_without_counters(sna):
 
 
 def test_multi_more_cells_than_one_launch(sna):
-    # 70 configurations of one conversion mode: two launches of that mode
-    configs = [(float(i % 11), 256.0, i % 2) for i in range(70)]
+    # 130 configurations of one conversion mode: two launches of that mode (at most 112 each)
+    configs = [(float(i % 11), 256.0, i % 2) for i in range(130)]
     _check(sna, 1, 2, 2, 192, 128, True, configs, 63)
 
 
