@@ -344,9 +344,10 @@ def smi_summary(samples) -> dict:
 
 def bench_roof(seconds: float) -> dict:
     """Sustained matrix-core rates of the rate probe (libpcast_roof.so): bf16 32x32x16 only,
-    FP8 32x32x64 only, and the attention forward's mix (16 bf16 : 4 FP8 instructions per
-    64-key block), each run back to back for `seconds` on every compute unit while rocm-smi
-    samples socket power and shader clock."""
+    FP8 32x32x64 only, the attention forward's mix (16 bf16 : 4 FP8 instructions per
+    64-key block), the forward's softmax VALU work per block alone, and both interleaved
+    as in the forward's steady step; each run back to back for `seconds` on every compute
+    unit while rocm-smi samples socket power and shader clock."""
     import ctypes
 
     import torch
@@ -361,8 +362,10 @@ def bench_roof(seconds: float) -> dict:
     sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     res = {"blocks": blocks, "threads": 256}
+    waves_per_simd = blocks * 4 / (4 * torch.cuda.get_device_properties(dev).multi_processor_count)
     for mode, name, peak in ((0, "bf16_32x32x16", PEAK_BF16), (1, "fp8_32x32x64", PEAK_FP8),
-                             (2, "forward_mix_16bf16_4fp8", None)):
+                             (2, "forward_mix_16bf16_4fp8", None), (3, "forward_valu_per_block", None),
+                             (4, "forward_mix_with_valu", None)):
         def launch(iters):
             rc = lib.pcast_roof_run(mode, iters, blocks, ctypes.c_void_p(sink.data_ptr()),
                                     ctypes.c_void_p(stream.cuda_stream))
@@ -378,14 +381,23 @@ def bench_roof(seconds: float) -> dict:
         tflops = lib.pcast_roof_flops(mode, iters, blocks) * n / (ms * 1e-3) / 1e12
         entry = {"tflops": round(tflops, 1), "launches": n, "iters": iters, "seconds": round(ms * 1e-3, 2),
                  **smi_summary(samples)}
+        # one iteration of every wave is one 64-key block of 32 query rows (modes 2-4); a
+        # SIMD runs waves_per_simd of them side by side
+        entry["ns_per_iteration_per_simd"] = round(ms * 1e6 / (n * iters * waves_per_simd), 2)
         if peak:
             entry["frac_of_peak"] = round(tflops / peak, 4)
         res[name] = entry
-        print(f"[bench] rate probe {name}: {tflops:.0f} TFLOP/s, power {entry['power_w_median']} W, "
-              f"sclk {entry['sclk_mhz_median']} MHz", file=sys.stderr, flush=True)
+        print(f"[bench] rate probe {name}: {tflops:.0f} TFLOP/s, {entry['ns_per_iteration_per_simd']} ns per "
+              f"iteration and SIMD, power {entry['power_w_median']} W, sclk {entry['sclk_mhz_median']} MHz",
+              file=sys.stderr, flush=True)
     bf, f8 = res["bf16_32x32x16"]["tflops"], res["fp8_32x32x64"]["tflops"]
     # equal flops on each type, at the measured sustained rates
     res["mixed_roof_from_rates"] = round(1.0 / (0.5 / bf + 0.5 / f8), 1)
+    t2, t3, t4 = (res[k]["ns_per_iteration_per_simd"] for k in
+                  ("forward_mix_16bf16_4fp8", "forward_valu_per_block", "forward_mix_with_valu"))
+    # 1 when the softmax's VALU work hides completely under the matrix cores, 0 when the
+    # two only add up
+    res["valu_overlap"] = round((t2 + t3 - t4) / min(t2, t3), 3)
     return res
 
 

@@ -9,6 +9,14 @@
 //   mode 1: v_mfma_scale_f32_32x32x64_f8f6f4   (E4M3 x E4M3, 131072 flops)
 //   mode 2: the forward's mix per 64-key block and 32 query rows at d = 128:
 //           16 bf16 logit instructions and 4 FP8 P.V instructions
+//   mode 3: the forward's softmax VALU work per such block and lane, alone: the
+//           max of 32 values (16 v_max3), 32 fma + 32 v_exp_f32 + 32 adds, 16
+//           P-cast conversions, 8 + 8 counter instructions
+//   mode 4: modes 2 and 3 together, interleaved as in the forward's steady step
+//           (P.V under the max and the first half's exponentials, the first logit
+//           half under the second half's, the second under the counters), on
+//           independent registers, so that the time against modes 2 and 3 alone
+//           shows how far the SIMD overlaps matrix-core and VALU work
 // One workgroup of 256 threads per compute unit share, two per CU by default;
 // the result of every accumulator is folded into one float per thread so the
 // work cannot be removed.
@@ -50,8 +58,72 @@ __global__ __launch_bounds__(256, 2) void roof(float* __restrict__ sink, int ite
     }
   f32x16_t acc[4] = {};
   f32x16_t acc8[4] = {};
+  // softmax-like state: 32 values in (0, 1] that each block's exponentials replace
+  float x[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) x[j] = 0.5f + (float)(mix32(seed + tid * 32 + j) & 0xFFFF) * 7.6e-6f;
+  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t codes[8] = {}, cnt = 0;
+  const float c = 0.12752f;  // log2(e)/sqrt(128)
+  float mneg = 0.0f;
+  auto vmax = [&]() __attribute__((always_inline)) {
+    float mx = fmaxf(x[0], x[1]);
+#pragma unroll
+    for (int j = 2; j < 32; j += 2) mx = fmaxf(fmaxf(mx, x[j]), x[j + 1]);
+    mneg = -mx * c;
+  };
+  auto vexp = [&](int j) __attribute__((always_inline)) {
+    x[j] = __builtin_amdgcn_exp2f(fmaf(x[j], c, mneg));
+    ps[j % 4] += x[j];
+  };
+  auto vcast = [&](int w) __attribute__((always_inline)) {
+    typedef __attribute__((ext_vector_type(2))) short s16x2;
+    s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(s16x2, codes[w]), x[4 * w], x[4 * w + 1],
+                                                         0.00390625f, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, x[4 * w + 2], x[4 * w + 3], 0.00390625f, true);
+    codes[w] = __builtin_bit_cast(uint32_t, r);
+  };
+  auto vcount = [&](int w) __attribute__((always_inline)) {
+    cnt = __builtin_amdgcn_msad_u8(codes[w] | 0x80808080u, codes[w], cnt);
+  };
   for (int it = 0; it < iters; ++it) {
-    if constexpr (kMode == 0) {
+    if constexpr (kMode == 3) {
+      vmax();
+#pragma unroll
+      for (int j = 0; j < 32; ++j) vexp(j);
+#pragma unroll
+      for (int w = 0; w < 8; ++w) vcast(w);
+#pragma unroll
+      for (int w = 0; w < 8; ++w) vcount(w);
+    } else if constexpr (kMode == 4) {
+      // P.V: 4 FP8 instructions | max, first 16 exponentials, their 4 casts
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // two operand fragments per type here, so that the softmax state fits beside them
+        acc8[s] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8[s % 2], b8[s % 2], acc8[s], 0, 0, 0, 0, 0, 0);
+        if (s == 0) vmax();
+#pragma unroll
+        for (int j = 4 * s; j < 4 * s + 4; ++j) vexp(j);
+        vcast(s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // first logit half: 8 bf16 instructions | second 16 exponentials and casts
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        acc[s % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s % 2], b[(s / 4) % 2], acc[s % 4], 0, 0, 0);
+        vexp(16 + 2 * s);
+        vexp(17 + 2 * s);
+        if (s % 2 == 1) vcast(4 + s / 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // second logit half: 8 bf16 instructions | counters
+#pragma unroll
+      for (int s = 8; s < 16; ++s) {
+        acc[s % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s % 2], b[(s / 4) % 2], acc[s % 4], 0, 0, 0);
+        vcount(s - 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (kMode == 0) {
 #pragma unroll
       for (int s = 0; s < 16; ++s)
         acc[s % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s % 4], b[(s / 4) % 4], acc[s % 4], 0, 0, 0);
@@ -69,7 +141,7 @@ __global__ __launch_bounds__(256, 2) void roof(float* __restrict__ sink, int ite
         acc[s % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s % 4], b[(s / 4) % 4], acc[s % 4], 0, 0, 0);
     }
   }
-  float r = 0.0f;
+  float r = (float)cnt + (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -81,10 +153,13 @@ __global__ __launch_bounds__(256, 2) void roof(float* __restrict__ sink, int ite
 
 extern "C" {
 
-// Flops of one launch of pcast_roof_run(mode, iters, blocks, ...), counted as
-// 2 * M * N * K per instruction.
+// Matrix-core flops of one launch of pcast_roof_run(mode, iters, blocks, ...), counted
+// as 2 * M * N * K per instruction (0 for the VALU-only mode 3).
 double pcast_roof_flops(int mode, int iters, int blocks) {
-  const double per_wave = mode == 0 ? 16.0 * 32768 : mode == 1 ? 16.0 * 131072 : 16.0 * 32768 + 4.0 * 131072;
+  const double per_wave = mode == 0 ? 16.0 * 32768
+                          : mode == 1 ? 16.0 * 131072
+                          : mode == 3 ? 0.0
+                                      : 16.0 * 32768 + 4.0 * 131072;
   return per_wave * iters * blocks * 4.0;
 }
 
@@ -92,11 +167,13 @@ double pcast_roof_flops(int mode, int iters, int blocks) {
 // sink holds blocks * 256 floats.  Returns 0, or 1 for a bad argument, or the HIP
 // error code of the launch.
 int pcast_roof_run(int mode, int iters, int blocks, float* sink, void* stream) {
-  if (mode < 0 || mode > 2 || iters < 1 || blocks < 1 || !sink) return 1;
+  if (mode < 0 || mode > 4 || iters < 1 || blocks < 1 || !sink) return 1;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (mode == 0) hipLaunchKernelGGL(roof<0>, dim3(blocks), dim3(256), 0, st, sink, iters, 0x9E3779B9u);
   else if (mode == 1) hipLaunchKernelGGL(roof<1>, dim3(blocks), dim3(256), 0, st, sink, iters, 0x9E3779B9u);
-  else hipLaunchKernelGGL(roof<2>, dim3(blocks), dim3(256), 0, st, sink, iters, 0x9E3779B9u);
+  else if (mode == 2) hipLaunchKernelGGL(roof<2>, dim3(blocks), dim3(256), 0, st, sink, iters, 0x9E3779B9u);
+  else if (mode == 3) hipLaunchKernelGGL(roof<3>, dim3(blocks), dim3(256), 0, st, sink, iters, 0x9E3779B9u);
+  else hipLaunchKernelGGL(roof<4>, dim3(blocks), dim3(256), 0, st, sink, iters, 0x9E3779B9u);
   return (int)hipGetLastError();
 }
 
