@@ -870,10 +870,13 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
   const int n_rb = (p.N + kBlockRows - 1) / kBlockRows;
   int b, h, rb;
   if constexpr (kMulti) {
-    // cells are an outer batch dimension: every cell's longest row blocks come first
+    // cells are the innermost index of the (batch, head) range an XCD takes: the cells
+    // of a head follow one another, so its K and V stay in that XCD's L2
     decode_block(blockIdx.x, n_rb * p.Hq * p.B * cells.n, n_rb, p.Hq, kCausal, b, h, rb);
-    const int cell = b / p.B;
-    b -= cell * p.B;
+    const int hh = b * p.Hq + h;
+    const int cell = hh % cells.n, bh = hh / cells.n;
+    b = bh / p.Hq;
+    h = bh % p.Hq;
     p.bias = cells.bias[cell];
     p.out = cells.out[cell];
     p.stats = cells.stats[cell];
