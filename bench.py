@@ -162,7 +162,7 @@ def bench_backward(sna, torch, np, synthetic, w, q, k, v, ws, bias_t, dev, strea
 
 def bench_sweep_all(sna, torch, np, synthetic, w, q, k, v, dev, reps: int = 3):
     """The whole Sweep workload: every (delta, S, order) cell on the same Q, K, V through
-    one attn_fwd_pcast_multi call (one launch per conversion mode and per 64 cells, the
+    one attn_fwd_pcast_multi call (one launch per conversion mode and per 112 cells, the
     row blocks of all cells in one grid), each cell with its own out and counters.
     Returns the aggregate rate: all cells' flops over the call's time."""
     cells = [c for c in w.cases if c[1] > 0]
@@ -200,7 +200,7 @@ def bench_sweep_all(sna, torch, np, synthetic, w, q, k, v, dev, reps: int = 3):
             "per_cell_us": round(ms * 1e3 / len(cells), 2),
             "what": "every cell of the Sweep (delta 0..10, S = 2^0..2^9 and 448, both orders) on the same Q, K, V "
                     "(one V pre-pass for all, outside the timed call), counters on, one attn_fwd_pcast_multi "
-                    "call: one launch per conversion mode and per 64 cells"}
+                    "call: one launch per conversion mode and per 112 cells"}
 
 
 def bench_decode(sna, torch, np, synthetic, dev, stream, steps, warmup):
