@@ -401,6 +401,71 @@ def bench_roof(seconds: float) -> dict:
     return res
 
 
+ISSUE_KINDS = {1: "v_mfma_f32_32x32x16_bf16", 2: "softmax_work_per_block", 3: "v_exp_f32", 4: "v_fma_f32",
+               5: "v_cvt_scalef32_pk_fp8_f32", 6: "v_cvt_pk_fp8_f32", 7: "v_max3_f32", 8: "v_add_f32",
+               9: "v_or_b32+v_msad_u8", 10: "v_mul_f32"}
+
+
+def bench_issue() -> dict:
+    """Issue costs on one SIMD from the rate probe's second kernel (libpcast_roof.so): each
+    instruction type of the forward's step alone with two waves per SIMD (ns per instruction
+    and SIMD), the bf16 matrix-core stream and the softmax work per block alone with one
+    wave per SIMD, and VALU waves beside a matrix-core wave on the same SIMD (how much of
+    the matrix-core time the VALU wave loses)."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "softmax_numerics_amd", "libpcast_roof.so"))
+    lib.pcast_issue_run.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.pcast_issue_run.restype = ctypes.c_int
+    lib.pcast_issue_count.argtypes = [ctypes.c_int]
+    lib.pcast_issue_count.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count  # one 8-wave workgroup per CU
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(klo, ilo, khi, ihi):
+        def launch():
+            rc = lib.pcast_issue_run(klo, ilo, khi, ihi, blocks, ctypes.c_void_p(sink.data_ptr()),
+                                     ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"issue probe launch failed ({rc})")
+        launch()
+        best = float("inf")
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream); launch(); e1.record(stream); e1.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    it = 2000
+    res = {"blocks": blocks, "threads": 512, "iterations": it, "two_waves_per_simd_ns_per_instruction": {}}
+    for k in range(3, 11):
+        ms = timed(k, it, k, it)
+        res["two_waves_per_simd_ns_per_instruction"][ISSUE_KINDS[k]] = round(ms * 1e6 / (it * 2 * lib.pcast_issue_count(k)), 3)
+    mf = timed(1, it, 0, 1)
+    sm = timed(0, 1, 2, it)
+    both = timed(1, it, 2, it)
+    res["one_wave_ns_per_iteration"] = {"mfma_16_bf16": round(mf * 1e6 / it, 2),
+                                        "softmax_work_per_block": round(sm * 1e6 / it, 2),
+                                        "both_on_one_simd": round(both * 1e6 / it, 2)}
+    res["overlap_mfma_wave_with_softmax_wave"] = round((mf + sm - both) / min(mf, sm), 3)
+    # a VALU wave four times longer than the matrix-core wave beside it: the extra time
+    # it takes, as a share of the matrix-core wave's time, is what the matrix cores cost it
+    lost = {}
+    for k in (3, 4, 5, 8, 2):
+        alone1 = timed(0, 1, k, it)
+        ih = max(1, int(it * 4.0 * mf / alone1))
+        alone = timed(0, 1, k, ih)
+        beside = timed(1, it, k, ih)
+        lost[ISSUE_KINDS[k]] = round((beside - alone) / mf, 3)
+    res["valu_wave_loses_share_of_mfma_time"] = lost
+    print(f"[bench] issue probe: {json.dumps(res)}", file=sys.stderr, flush=True)
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -419,12 +484,18 @@ def main() -> int:
     ap.add_argument("--roof", type=float, default=0.0, metavar="SECONDS",
                     help="only run the matrix-core rate probe (bf16, FP8 and the forward's mix), SECONDS "
                          "each, with power and clock samples")
+    ap.add_argument("--issue", action="store_true",
+                    help="only run the issue-cost probe (VALU instruction types of the forward's step, "
+                         "matrix-core and VALU waves on one SIMD)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes, 3 times (scale for "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.roof > 0:
         print(json.dumps({"roof": bench_roof(args.roof)}))
+        return 0
+    if args.issue:
+        print(json.dumps({"issue": bench_issue()}))
         return 0
     if args.calibrate_copy:
         import torch

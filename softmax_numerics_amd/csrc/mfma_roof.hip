@@ -20,6 +20,15 @@
 // One workgroup of 256 threads per compute unit share, two per CU by default;
 // the result of every accumulator is folded into one float per thread so the
 // work cannot be removed.
+//
+// A second probe (issue_probe) measures issue costs on one SIMD: 512-thread workgroups,
+// one per compute unit, so that each SIMD holds two waves (wave w runs on SIMD w % 4);
+// waves 0-3 run kind_lo and waves 4-7 kind_hi, where a kind is one instruction type of
+// the forward's step, written out in inline assembly so that the count per iteration is
+// exact, or the bf16 matrix-core stream, or the forward's softmax VALU work per block.
+// With kind_lo == kind_hi the time gives the throughput of that instruction type with two
+// waves per SIMD; with the matrix-core stream beside a VALU kind it shows how far the
+// SIMD runs the two side by side.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -149,6 +158,147 @@ __global__ __launch_bounds__(256, 2) void roof(float* __restrict__ sink, int ite
   sink[tid] = r;
 }
 
+
+// Issue-cost kinds (per wave and iteration):
+//   0 idle, 1 sixteen v_mfma_f32_32x32x16_bf16, 2 the softmax VALU work of roof mode 3,
+//   3 32 v_exp_f32, 4 64 v_fma_f32, 5 16 v_cvt_scalef32_pk_fp8_f32, 6 16 v_cvt_pk_fp8_f32,
+//   7 16 v_max3_f32, 8 32 v_add_f32, 9 8 v_or_b32 + 8 v_msad_u8, 10 32 v_mul_f32
+// Every VALU kind keeps 16 or more independent chains, so that with two waves per SIMD
+// the time is the issue cost, not the latency.
+constexpr int kIssueKinds = 11;
+constexpr int kIssueCount[kIssueKinds] = {0, 16, 146, 32, 64, 16, 16, 16, 32, 16, 32};
+
+template <int kKind>
+__device__ __attribute__((noinline)) float issue_loop(uint32_t tid, int iters) {
+  float x[32], acc[32];
+  uint32_t w[16];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    x[j] = -(float)(mix32(tid * 32 + j) & 0xFF) * 0.01f;
+    acc[j] = x[j];
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) w[k] = mix32(tid + k) & 0x7F7F7F7Fu;
+  uint32_t cnt = 0;
+  const float fa = 0.999f, fb = 0.001f, sc = 0.00390625f;
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (kKind == 3) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) asm volatile("v_exp_f32 %0, %1" : "=v"(acc[j]) : "v"(x[j]));
+    } else if constexpr (kKind == 4) {
+#pragma unroll
+      for (int j = 0; j < 64; ++j) asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc[j % 32]) : "v"(fa), "v"(fb));
+    } else if constexpr (kKind == 5) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        asm volatile("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, %3" : "=v"(w[k]) : "v"(x[2 * k]), "v"(x[2 * k + 1]), "s"(sc));
+    } else if constexpr (kKind == 6) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) asm volatile("v_cvt_pk_fp8_f32 %0, %1, %2" : "=v"(w[k]) : "v"(x[2 * k]), "v"(x[2 * k + 1]));
+    } else if constexpr (kKind == 7) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(acc[k]) : "v"(x[k]), "v"(x[16 + k]));
+    } else if constexpr (kKind == 8) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) asm volatile("v_add_f32 %0, %0, %1" : "+v"(acc[j % 16]) : "v"(x[j]));
+    } else if constexpr (kKind == 9) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        asm volatile("v_or_b32 %0, 0x80808080, %1" : "=v"(w[8 + k]) : "v"(w[k]));
+        asm volatile("v_msad_u8 %0, %1, %2, %0" : "+v"(acc[k]) : "v"(w[8 + k]), "v"(w[k]));
+      }
+    } else if constexpr (kKind == 10) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) asm volatile("v_mul_f32 %0, %1, %2" : "=v"(acc[j]) : "v"(x[j]), "s"(sc));
+    }
+  }
+  // every asm result above is consumed here, several instructions after the loop
+  asm volatile("s_nop 7" ::);
+  float r = (float)cnt;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) r += acc[j];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) r += (float)w[k];
+  return r;
+}
+
+__device__ __attribute__((noinline)) float issue_mfma(uint32_t tid, int iters) {
+  bf16x8_t a[4], b[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t h = mix32(tid * 64 + f * 8 + i);
+      a[f][i] = __builtin_bit_cast(__bf16, (uint16_t)(0x3F80 | (h & 0x7F)));
+      b[f][i] = __builtin_bit_cast(__bf16, (uint16_t)(0x3F80 | ((h >> 7) & 0x7F)));
+    }
+  f32x16_t acc[4] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      acc[s % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s % 4], b[(s / 4) % 4], acc[s % 4], 0, 0, 0);
+  }
+  float r = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r += acc[q][i];
+  return r;
+}
+
+__device__ __attribute__((noinline)) float issue_softmax(uint32_t tid, int iters) {
+  float x[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) x[j] = 0.5f + (float)(mix32(tid * 32 + j) & 0xFFFF) * 7.6e-6f;
+  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t codes[8] = {}, cnt = 0;
+  const float c = 0.12752f;
+  for (int it = 0; it < iters; ++it) {
+    float mx = fmaxf(x[0], x[1]);
+#pragma unroll
+    for (int j = 2; j < 32; j += 2) mx = fmaxf(fmaxf(mx, x[j]), x[j + 1]);
+    const float mneg = -mx * c;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      x[j] = __builtin_amdgcn_exp2f(fmaf(x[j], c, mneg));
+      ps[j % 4] += x[j];
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      typedef __attribute__((ext_vector_type(2))) short s16x2;
+      s16x2 q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(s16x2, codes[w]), x[4 * w], x[4 * w + 1],
+                                                         0.00390625f, false);
+      q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(q, x[4 * w + 2], x[4 * w + 3], 0.00390625f, true);
+      codes[w] = __builtin_bit_cast(uint32_t, q);
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) cnt = __builtin_amdgcn_msad_u8(codes[w] | 0x80808080u, codes[w], cnt);
+  }
+  return (float)cnt + (ps[0] + ps[1]) + (ps[2] + ps[3]);
+}
+
+__global__ __launch_bounds__(512, 1) void issue_probe(float* __restrict__ sink, int iters_lo, int iters_hi,
+                                                      int kind_lo, int kind_hi) {
+  const uint32_t tid = blockIdx.x * blockDim.x + threadIdx.x;
+  const bool lo = (threadIdx.x / 64) < 4;
+  const int kind = lo ? kind_lo : kind_hi, iters = lo ? iters_lo : iters_hi;
+  float r = 0.0f;
+  switch (kind) {
+    case 1: r = issue_mfma(tid, iters); break;
+    case 2: r = issue_softmax(tid, iters); break;
+    case 3: r = issue_loop<3>(tid, iters); break;
+    case 4: r = issue_loop<4>(tid, iters); break;
+    case 5: r = issue_loop<5>(tid, iters); break;
+    case 6: r = issue_loop<6>(tid, iters); break;
+    case 7: r = issue_loop<7>(tid, iters); break;
+    case 8: r = issue_loop<8>(tid, iters); break;
+    case 9: r = issue_loop<9>(tid, iters); break;
+    case 10: r = issue_loop<10>(tid, iters); break;
+    default: break;
+  }
+  sink[tid] = r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,6 +324,24 @@ int pcast_roof_run(int mode, int iters, int blocks, float* sink, void* stream) {
   else if (mode == 2) hipLaunchKernelGGL(roof<2>, dim3(blocks), dim3(256), 0, st, sink, iters, 0x9E3779B9u);
   else if (mode == 3) hipLaunchKernelGGL(roof<3>, dim3(blocks), dim3(256), 0, st, sink, iters, 0x9E3779B9u);
   else hipLaunchKernelGGL(roof<4>, dim3(blocks), dim3(256), 0, st, sink, iters, 0x9E3779B9u);
+  return (int)hipGetLastError();
+}
+
+// Instructions of one kind per wave and iteration of issue_probe (0 for idle, 146 VALU
+// instructions for the softmax work, 16 MFMAs for the matrix-core stream); -1 for an
+// unknown kind.
+int pcast_issue_count(int kind) { return kind >= 0 && kind < kIssueKinds ? kIssueCount[kind] : -1; }
+
+// Launches issue_probe: `blocks` workgroups of 512 threads (one per compute unit gives two
+// waves per SIMD); waves 0-3 of each workgroup run kind_lo for iters_lo iterations, waves
+// 4-7 kind_hi for iters_hi.  sink holds blocks * 512 floats.  Returns 0, 1 for a bad
+// argument, or the HIP error code of the launch.
+int pcast_issue_run(int kind_lo, int iters_lo, int kind_hi, int iters_hi, int blocks, float* sink, void* stream) {
+  if (kind_lo < 0 || kind_lo >= kIssueKinds || kind_hi < 0 || kind_hi >= kIssueKinds || iters_lo < 1 ||
+      iters_hi < 1 || blocks < 1 || !sink)
+    return 1;
+  hipLaunchKernelGGL(issue_probe, dim3(blocks), dim3(512), 0, static_cast<hipStream_t>(stream), sink, iters_lo,
+                     iters_hi, kind_lo, kind_hi);
   return (int)hipGetLastError();
 }
 
