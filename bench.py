@@ -138,23 +138,38 @@ def bench_backward(sna, torch, np, synthetic, w, q, k, v, ws, bias_t, dev, strea
         if r != sna.PCAST_OK:
             raise sna.PcastError(r, sna.strerror(r))
 
-    for _ in range(warmup):
-        call()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for e in ev:
-        e[0].record(stream)
-        call()
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    def fwd_lse():
+        r = sna.attn_fwd_pcast_rows(q.data_ptr(), k.data_ptr(), ws.data_ptr(), bias_t.data_ptr(), B, Hq, Hkv, N,
+                                    d, int(w.causal), S, order, o.data_ptr(), 0, lse.data_ptr(), 0, sh)
+        if r != sna.PCAST_OK:
+            raise sna.PcastError(r, sna.strerror(r))
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+    # the forward a training step runs before the backward: out and lse (no counters),
+    # the attention kernel alone (the V copy is made once above)
+    ms_fwd = timed(fwd_lse)
+    ms = timed(call)
     flops = 2.5 * w.flops   # five products of the forward's two (FlashAttention convention)
     tf = flops / (ms * 1e-3) / 1e12
-    print(f"[bench] backward: {ms:.4f} ms per call ({tf:.0f} TFLOP/s)", file=sys.stderr, flush=True)
+    print(f"[bench] backward: {ms:.4f} ms per call ({tf:.0f} TFLOP/s); forward with lse {ms_fwd:.4f} ms",
+          file=sys.stderr, flush=True)
     return {"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal, sink bias 7 on keys 0..3, "
                         f"gradients of the S={S:g} {'reverse' if order else 'forward'} forward",
             "ms_per_call": round(ms, 5), "steps": steps,
             "kernels": "pcast_bwd_rowdot + pcast_attn_bwd_dq + pcast_attn_bwd_dkv",
+            "forward_with_lse_ms": round(ms_fwd, 5),
+            "forward_with_lse": "attn_fwd_pcast_rows with lost NULL (the pipelined forward, lse in its epilogue)",
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_BF16, 4), "algorithmic_flops": flops,
                          "flops_rule": "2.5 x the forward's 2*B*H*N^2*d (causal)"}}

@@ -187,8 +187,10 @@ int attn_fwd_pcast_multi(const void* Q, const void* K, const void* workspace, in
  *         non-sink probability mass whose E4M3 code is 0,
  *         sum_{j non-sink, code 0} p_j / sum_{j non-sink} p_j with p_j the
  *         un-cast probability (0 for a row with no non-sink key).
- * Requires S > 0 (PCAST_ENOTSUP for S = 0).  Every key block takes the
- * kernel's sequential step, so the call is slower than the plain one.
+ * Requires S > 0 (PCAST_ENOTSUP for S = 0).  With lost requested every key
+ * block takes the kernel's sequential step, so the call is slower than the
+ * plain one; with lost NULL the plain pipelined kernel runs and also writes
+ * lse (the same values bit for bit), at the plain call's speed.
  * Allocates nothing.
  */
 int attn_fwd_pcast_rows(const void* Q, const void* K, const void* workspace, const float* bias, int B,

@@ -1391,6 +1391,11 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
     const float l_all = halves_sum(l_run);
     const float inv = 1.0f / (p.S * l_all);
     const int64_t row = ((int64_t)b * p.Hq + h) * p.N + myrow;
+    if constexpr (!kDiag && !kMulti && kQ8 == 0) {
+      // the log-sum-exp alone (no lost mass requested): the pipelined and the sequential
+      // steps keep the same m and l bit for bit, so this equals the diagnostic kernel's
+      if (g == 0 && p.lse) p.lse[row] = (m_run + log2f(l_all)) * kLn2;
+    }
     if constexpr (kDiag) {
       // log-sum-exp of the row's logits (natural units) and the lost non-sink mass fraction
       const float ns = halves_sum(l_ns), lo = halves_sum(l_lost);
@@ -2338,7 +2343,9 @@ void launch_attn3(const Params& p, hipStream_t stream) {
       hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 1, 1>), grid, dim3(kThreads), 0, stream, p, NoCells{});
     else
       hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 0, 1>), grid, dim3(kThreads), 0, stream, p, NoCells{});
-  } else if (p.lse || p.lost) {
+  } else if (p.lost) {
+    // the lost mass needs the per-key work of the sequential step in every block; the
+    // log-sum-exp alone is written by the pipelined kernels below
     hipLaunchKernelGGL((pcast_attn_fwd_fp8<D, kMode, kCausal, 2, 0>), grid, dim3(kThreads), 0, stream, p, NoCells{});
   } else {
     if (p.stats)

@@ -2,6 +2,8 @@
 
 * out and stats equal attn_fwd_pcast_prepared's bit for bit (the diagnostics take
   the kernel's sequential step for every block, which computes the same numbers);
+  with lost NULL the pipelined kernel writes lse alone, bit-identical to the lse
+  written beside the lost mass;
 * lse and lost against oracle.rowdiag: |lse_gpu - lse| <= 1e-4 + 1e-5 |lse|
   (fp32 logits, exp2 and log2: about 1e-6 relative each); |lost_gpu - lost| <=
   2e-5 + 1e-4 lost + lost_amb, lost_amb the oracle's share of non-sink mass whose
@@ -39,24 +41,29 @@ def _run(sna, qb, kb, vb, bias, causal, S, order):
     st = torch.cuda.current_stream().cuda_stream
     assert sna.prepare_v(v.data_ptr(), B, Hkv, N, d, S, ws.data_ptr(), st) == 0
     res = {}
-    for name, rows in (("plain", False), ("rows", True)):
+    for name, rows in (("plain", False), ("rows", True), ("lse_only", True)):
         out = torch.full((B, Hq, N, d), float("nan"), device="cuda")
         stats = torch.full((sna.stats_words(B, Hq, N),), -1, dtype=torch.int64, device="cuda")
         bp = 0 if bt is None else bt.data_ptr()
         if rows:
             lse = torch.full((B, Hq, N), float("nan"), device="cuda")
             lost = torch.full((B, Hq, N), float("nan"), device="cuda")
+            # lost NULL: the pipelined kernel writes lse alone
+            lost_ptr = 0 if name == "lse_only" else lost.data_ptr()
             rc = sna.attn_fwd_pcast_rows(q.data_ptr(), k.data_ptr(), ws.data_ptr(), bp, B, Hq, Hkv, N, d,
                                          causal, S, order, out.data_ptr(), stats.data_ptr(), lse.data_ptr(),
-                                         lost.data_ptr(), st)
+                                         lost_ptr, st)
         else:
             rc = sna.attn_fwd_pcast_prepared(q.data_ptr(), k.data_ptr(), ws.data_ptr(), bp, B, Hq, Hkv, N, d,
                                              causal, S, order, out.data_ptr(), stats.data_ptr(), st)
         assert rc == 0, sna.strerror(rc)
         torch.cuda.synchronize()
         res[name] = (out.cpu().numpy(), stats.cpu().numpy())
-        if rows:
+        if name == "rows":
             res["lse"], res["lost"] = lse.cpu().numpy().ravel(), lost.cpu().numpy().ravel()
+        elif name == "lse_only":
+            res["lse_only_lse"] = lse.cpu().numpy().ravel()
+            assert torch.isnan(lost).all().item(), "lost written although not requested"
     return res
 
 
@@ -64,6 +71,9 @@ def _check(res, qb, kb, bias, causal, S, order, ids=None):
     a, sa = res["plain"]
     b, sb = res["rows"]
     assert np.array_equal(a, b) and np.array_equal(sa, sb), "diagnostics changed out or stats"
+    c, sc = res["lse_only"]
+    assert np.array_equal(a, c) and np.array_equal(sa, sc), "lse alone changed out or stats"
+    assert np.array_equal(res["lse_only_lse"], res["lse"]), "lse alone differs from lse with the lost mass"
     r = rowdiag.rows(qb, kb, bias, causal, S, order, ids)
     sel = slice(None) if ids is None else ids
     lse, lost = res["lse"][sel], res["lost"][sel]
