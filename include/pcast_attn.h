@@ -57,7 +57,11 @@ extern "C" {
  *        key is "non-sink" (all keys when bias is NULL).
  * B, Hq, Hkv  batch and head counts, Hq % Hkv == 0; query head h reads key/value
  *        head h / (Hq / Hkv).
- * N      sequence length (queries and keys), N >= 1 and N % 64 == 0.
+ * N      sequence length (queries and keys), N >= 1.  For S > 0 any N: when
+ *        N % 64 != 0 the last key block is partial and its keys past N are
+ *        masked (they take no probability), query rows past N are neither
+ *        stored nor counted.  For S = 0 (and for the FP8-logit, decode and
+ *        backward entry points below) N % 64 == 0, else PCAST_ENOTSUP.
  * d      head size, 64 or 128.
  * causal 0 = every key visible; 1 = key j visible to query i iff j <= i.
  * S      > 0 and finite: P-cast scale (powers of two are exact in fp32; values
@@ -66,7 +70,7 @@ extern "C" {
  * out    device, float32 [B][Hq][N][d], written completely.
  * stats  device, uint64 [pcast_stats_words(B, Hq, N)], or NULL for no
  *        counting.  For query rows [64r, 64r + 64) of (batch b, head h), word
- *        2*((b*Hq + h)*(N/64) + r) receives the number of unmasked non-sink
+ *        2*((b*Hq + h)*ceil(N/64) + r) receives the number of unmasked non-sink
  *        (query, key) pairs evaluated, and the next word the number of those
  *        whose E4M3 code of P*S is zero (underflow).  Words are overwritten,
  *        not accumulated.  In the bf16 path the second word counts P values
@@ -122,7 +126,8 @@ int attn_fwd_pcast_noalloc(const void* Q, const void* K, const void* V, const fl
  * pcast_prepare_v -- enqueue the copy of V that the matrix cores read: for
  * each (b, kv head, key block) a [d][64] tile of E4M3(V) (S > 0: round to
  * nearest even, saturating at +/-448) or of V itself (S = 0, bf16), with the
- * 64 keys in the order in which the attention kernel holds its probabilities.
+ * 64 keys in the order in which the attention kernel holds its probabilities
+ * (a partial last block, N % 64 != 0, is padded with zeros).
  *   V          device, bf16 [B][Hkv][N][d], 16-byte aligned.
  *   workspace  device, pcast_workspace_bytes(B, Hkv, N, d, S) bytes, 16-byte
  *              aligned, owned by the caller; overwritten.
@@ -431,7 +436,8 @@ int pcast_cast_e4m3(const float* P, unsigned char* codes, long long n, float S, 
 /* Number of uint64 words the stats buffer needs: B * Hq * ceil(N / 64) * 2. */
 size_t pcast_stats_words(int B, int Hq, int N);
 
-/* Bytes of the V operand copy: B * Hkv * N * d for S > 0, twice that for S = 0. */
+/* Bytes of the V operand copy: B * Hkv * (N rounded up to a multiple of 64) * d
+ * for S > 0, twice that for S = 0. */
 size_t pcast_workspace_bytes(int B, int Hkv, int N, int d, float S);
 
 /* Human-readable text for a return code, with the detail of the last error

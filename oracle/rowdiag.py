@@ -44,13 +44,14 @@ def _row_logits(q_rows, pos, k, bias, causal):
 
 def _running_max(s, order, bc):
     R, N = s.shape
-    nblk = N // bc
-    bmax = s.reshape(R, nblk, bc).max(axis=2)
+    nblk = -(-N // bc)  # a partial last block holds the keys from its start up to N
+    sp = np.pad(s, ((0, 0), (0, nblk * bc - N)), constant_values=-np.inf)
+    bmax = sp.reshape(R, nblk, bc).max(axis=2)
     if order == 0:
         run = np.maximum.accumulate(bmax, axis=1)
     else:
         run = np.maximum.accumulate(bmax[:, ::-1], axis=1)[:, ::-1]
-    return np.repeat(run, bc, axis=1)
+    return np.repeat(run, bc, axis=1)[:, :N]
 
 
 def rows(q_bits, k_bits, bias, causal: bool, S: float, order: int, row_ids=None, bc: int = 64,
@@ -61,8 +62,6 @@ def rows(q_bits, k_bits, bias, causal: bool, S: float, order: int, row_ids=None,
     """
     B, Hq, N, d = q_bits.shape
     Hkv = k_bits.shape[1]
-    if N % bc:
-        raise ValueError("N must be a multiple of the block size")
     ids = np.arange(B * Hq * N) if row_ids is None else np.asarray(row_ids, dtype=np.int64)
     nonsink = np.ones(N, dtype=bool) if bias is None else (np.asarray(bias) == 0)
     out = {k: np.zeros(ids.size) for k in ("lse", "lost", "lost_amb")}

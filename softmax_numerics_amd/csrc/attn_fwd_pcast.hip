@@ -120,17 +120,22 @@ struct SwizzleT {
 };
 
 // ---------------------------------------------------------------------------
-// Pre-pass: V (bf16, [B][Hkv][N][D]) -> operand copy [B][Hkv][N/64][D][64]
-// in slot order, E4M3 (RNE, saturating) or bf16.
+// Pre-pass: V (bf16, [B][Hkv][N][D]) -> operand copy [B][Hkv][ceil(N/64)][D][64]
+// in slot order, E4M3 (RNE, saturating) or bf16.  Keys past N in a partial last
+// block are written as zeros (their probabilities are 0).
 // ---------------------------------------------------------------------------
 template <int D, bool kFp8>
-__device__ inline void prep_v_block(const uint16_t* __restrict__ V, void* __restrict__ vop, int64_t blk) {
+__device__ inline void prep_v_block(const uint16_t* __restrict__ V, void* __restrict__ vop, int64_t blk, int N,
+                                    int n_tiles) {
   __shared__ uint16_t tile[kKvBlock][D + 2];
   const int tid = threadIdx.x;
-  const uint16_t* src = V + blk * kKvBlock * D;
+  const int64_t bh = blk / n_tiles;
+  const int t = (int)(blk % n_tiles);
+  const int rows = min(kKvBlock, N - t * kKvBlock);  // keys of this block inside the sequence
+  const uint16_t* src = V + (bh * N + (int64_t)t * kKvBlock) * D;
   for (int c = tid; c < kKvBlock * D / 8; c += 256) {
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    const i32x4_t v = *reinterpret_cast<const i32x4_t*>(src + row * D + col);
+    const i32x4_t v = row < rows ? *reinterpret_cast<const i32x4_t*>(src + row * D + col) : i32x4_t{0, 0, 0, 0};
     const uint32_t w[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -168,8 +173,8 @@ __device__ inline void prep_v_block(const uint16_t* __restrict__ V, void* __rest
 
 template <int D, bool kFp8>
 __global__ __launch_bounds__(256) void pcast_prep_v(const uint16_t* __restrict__ V,
-                                                     void* __restrict__ vop) {
-  prep_v_block<D, kFp8>(V, vop, blockIdx.x);  // one (b, hkv, key block) per workgroup
+                                                     void* __restrict__ vop, int N, int n_tiles) {
+  prep_v_block<D, kFp8>(V, vop, blockIdx.x, N, n_tiles);  // one (b, hkv, key block) per workgroup
 }
 
 // ---------------------------------------------------------------------------
@@ -241,7 +246,8 @@ __global__ __launch_bounds__(256) void pcast_prep_kv8(const uint16_t* __restrict
     *reinterpret_cast<int2*>(dst + (i * 256 + tid) * 8) = make_int2(lo, hi);
   }
   if (tid == 0) kexp[blk] = e;
-  prep_v_block<D, true>(V, vop, blk);
+  // N is a multiple of 64 here: the flat block index addresses V as one block per "head"
+  prep_v_block<D, true>(V, vop, blk, kKvBlock, 1);
 }
 
 // Rotated FP8 logits: x -> x diag(sigma) H (H the Sylvester matrix of +-1, sigma the
@@ -888,11 +894,13 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
     decode_block(blockIdx.x, n_rb * p.Hq * p.B, n_rb, p.Hq, kCausal, b, h, rb);
   }
   const int hk = h / (p.Hq / p.Hkv);
-  const int n_tiles = p.N / kKvBlock;
+  // key blocks; with N not a multiple of 64 the last one is partial (keys past N masked)
+  const int n_tiles = (p.N + kKvBlock - 1) / kKvBlock, n_full = p.N / kKvBlock;
   const int row0 = rb * kBlockRows;
   const int wrow0 = row0 + wave * kRowsPerWave;  // first row of this wave
   const int myrow = wrow0 + li;
   const bool wave_active = wrow0 < p.N;
+  const bool row_valid = myrow < p.N;  // rows past N (last row block) are computed, never stored
   const int t_last = kCausal ? min((row0 + kBlockRows - 1) / kKvBlock, n_tiles - 1) : n_tiles - 1;
   const int n_it = t_last + 1;
   // log2(e)/sqrt(d); with FP8 logits times 2^(e_row + e_block) of the row's and the
@@ -908,7 +916,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
   KFrag qf[kSSteps];
   float c_row = p.logit_scale;
   if (wave_active) {
-    const int64_t row = ((int64_t)b * p.Hq + h) * p.N + myrow;
+    const int64_t row = ((int64_t)b * p.Hq + h) * p.N + min(myrow, p.N - 1);
     if constexpr (kQ8 == 2) {
       // the pre-pass's codes of the rotated row; the rotation scales Q K^T by d
       const uint8_t* qrow = p.q8 + row * D + g * 32;
@@ -978,8 +986,16 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
   auto load_k = [&](int t, int buf) __attribute__((always_inline)) {
     const uint8_t* ks = kbase + t * kKTile;
     const int dst = __builtin_amdgcn_readfirstlane(wave * kKLoads * 1024);
+    if (t < n_full) {
 #pragma unroll
-    for (int i = 0; i < kKLoads; ++i) load_to_lds16(ks + ksrc[i], kbuf(buf) + dst + i * 1024);
+      for (int i = 0; i < kKLoads; ++i) load_to_lds16(ks + ksrc[i], kbuf(buf) + dst + i * 1024);
+    } else {
+      // partial last block: rows past N read row N - 1 instead (their logits are masked)
+      const int last = (p.N - 1 - t * kKvBlock) * kKRow;  // byte offset of row N - 1 in the tile
+#pragma unroll
+      for (int i = 0; i < kKLoads; ++i)
+        load_to_lds16(ks + min(ksrc[i], last + (ksrc[i] & (kKRow - 1))), kbuf(buf) + dst + i * 1024);
+    }
   };
   auto load_v = [&](int t, int buf) __attribute__((always_inline)) {
     const uint8_t* vs = vbase + t * kVTile;
@@ -987,8 +1003,10 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) load_to_lds16(vs + vsrc[i], vbuf(buf) + dst + i * 1024);
   };
+  // bias of key min(j, N - 1): keys past N take the last key's value (masked anyway)
+  auto bias_at = [&](int t) __attribute__((always_inline)) { return p.bias + min(t * kKvBlock + lane, p.N - 1); };
   auto load_b = [&](int t, int buf) __attribute__((always_inline)) {
-    if (with_bias && wave == 0) load_to_lds4(p.bias + t * kKvBlock + lane, bbuf(buf));
+    if (with_bias && wave == 0) load_to_lds4(bias_at(t), bbuf(buf));
   };
   auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -1129,11 +1147,14 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
       __attribute__((always_inline)) -> float {
     float bk[32];
     if (has_bias) lane_bias(buf, bk);
+    // keys past the row's position (causal diagonal) or past N (a partial last block)
+    const bool masked = diag || key0 + kKvBlock > p.N;
+    const int kmax = min(diag ? myrow - key0 : kKvBlock - 1, p.N - 1 - key0);  // last visible key
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       const int kj = slot_key(g, j);
       float xj = has_bias ? fmaf(sa[j / 16][j % 16], c, bk[j] * kLog2e) : sa[j / 16][j % 16] * c;
-      if (diag && key0 + kj > myrow) xj = -INFINITY;
+      if (masked && kj > kmax) xj = -INFINITY;
       sa[j / 16][j % 16] = xj;
     }
     const float m_new = fmaxf(m_run, block_max(sa));
@@ -1171,18 +1192,18 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
           const int kj = slot_key(g, j);
-          const bool vis = !kCausal || key0 + kj <= myrow;
+          const bool vis = (!kCausal || key0 + kj <= myrow) && key0 + kj < p.N;
           const bool nonsink = bk[j] == 0.0f;
           const bool z = (((uint32_t)pb[j / 4] >> (8 * (j % 4))) & 0xFFu) == 0;
           cnt_tot += (vis && nonsink);
           cnt_zero += (vis && nonsink && z);
         }
       } else {
-        // causal mask only.  The lane's 32 keys are eight runs of four consecutive
-        // keys starting at h*32 + q*8 + g*4; the visible ones are those <= myrow -
-        // key0.  Masked keys have P = 0, whose code is 0, so the zero codes among
-        // the visible keys are all zero codes minus the masked keys.
-        const int lim = myrow - key0 + 1;  // keys below lim are visible
+        // causal mask and / or the end of the sequence.  The lane's 32 keys are eight
+        // runs of four consecutive keys starting at h*32 + q*8 + g*4; the visible ones
+        // are those below lim.  Masked keys have P = 0, whose code is 0, so the zero
+        // codes among the visible keys are all zero codes minus the masked keys.
+        const int lim = (kCausal ? min(myrow + 1, p.N) : p.N) - key0;  // keys below lim are visible
         int vis = 0;
 #pragma unroll
         for (int run = 0; run < 8; ++run) vis += min(max(lim - ((run / 4) * 32 + (run % 4) * 8 + g * 4), 0), 4);
@@ -1214,7 +1235,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
   // the lane's bias value in the block the next step processes (0 without a bias), read
   // from global memory one step ahead: the step's fast / general decision then waits
   // for no LDS read
-  float bias_next = with_bias ? p.bias[tile_of(0) * kKvBlock + lane] : 0.0f;
+  float bias_next = with_bias ? *bias_at(tile_of(0)) : 0.0f;
 
   auto step = [&](int it, auto cur_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
@@ -1234,8 +1255,8 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
     const int key0 = t * kKvBlock;
     const bool diag = kCausal && (key0 + kKvBlock - 1 > wrow0);
     const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bias_next != 0.0f) != 0;
-    if (with_bias && it + 1 < n_it) bias_next = p.bias[tile_of(it + 1) * kKvBlock + lane];
-    const bool fast = vis && !diag && !has_bias;
+    if (with_bias && it + 1 < n_it) bias_next = *bias_at(tile_of(it + 1));
+    const bool fast = vis && !diag && !has_bias && t < n_full;
     if (!kDiag && fast && pend && vis1) {
       // Steady state: the step's MFMAs (20 at d = 128), each in a chunk of its own
       // with the fragment read two MFMAs ahead and a slice of VALU work that does
@@ -1394,30 +1415,33 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
     if constexpr (!kDiag && !kMulti && kQ8 == 0) {
       // the log-sum-exp alone (no lost mass requested): the pipelined and the sequential
       // steps keep the same m and l bit for bit, so this equals the diagnostic kernel's
-      if (g == 0 && p.lse) p.lse[row] = (m_run + log2f(l_all)) * kLn2;
+      if (g == 0 && p.lse && row_valid) p.lse[row] = (m_run + log2f(l_all)) * kLn2;
     }
     if constexpr (kDiag) {
       // log-sum-exp of the row's logits (natural units) and the lost non-sink mass fraction
       const float ns = halves_sum(l_ns), lo = halves_sum(l_lost);
-      if (g == 0 && p.lse) p.lse[row] = (m_run + log2f(l_all)) * kLn2;
-      if (g == 0 && p.lost) p.lost[row] = ns > 0.0f ? lo / ns : 0.0f;
+      if (g == 0 && p.lse && row_valid) p.lse[row] = (m_run + log2f(l_all)) * kLn2;
+      if (g == 0 && p.lost && row_valid) p.lost[row] = ns > 0.0f ? lo / ns : 0.0f;
     }
     float* orow = p.out + row * D;
+    if (row_valid) {
 #pragma unroll
-    for (int dt = 0; dt < G::kDTiles; ++dt)
+      for (int dt = 0; dt < G::kDTiles; ++dt)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        float4 v;
-        v.x = oacc[dt][r4 * 4 + 0] * inv;
-        v.y = oacc[dt][r4 * 4 + 1] * inv;
-        v.z = oacc[dt][r4 * 4 + 2] * inv;
-        v.w = oacc[dt][r4 * 4 + 3] * inv;
-        *reinterpret_cast<float4*>(orow + dt * 32 + r4 * 8 + g * 4) = v;
-      }
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float4 v;
+          v.x = oacc[dt][r4 * 4 + 0] * inv;
+          v.y = oacc[dt][r4 * 4 + 1] * inv;
+          v.z = oacc[dt][r4 * 4 + 2] * inv;
+          v.w = oacc[dt][r4 * 4 + 3] * inv;
+          *reinterpret_cast<float4*>(orow + dt * 32 + r4 * 8 + g * 4) = v;
+        }
+    }
   }
   if constexpr (kStats) {
     // fast blocks: every one of the lane's 32 pairs is visible and non-sink
-    const unsigned int a = wave_sum(cnt_tot + 32u * n_fast), z = wave_sum(cnt_zero + 32u * n_fast - (cnt_nz_fast >> 7));
+    const unsigned int a = wave_sum(row_valid ? cnt_tot + 32u * n_fast : 0u),
+                       z = wave_sum(row_valid ? cnt_zero + 32u * n_fast - (cnt_nz_fast >> 7) : 0u);
     if (lane == 0 && wave_active) {
       atomicAdd(&lds_cnt[wave / 2][0], a);
       atomicAdd(&lds_cnt[wave / 2][1], z);
@@ -1426,7 +1450,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
     if (tid < 2 && (!kDiag || p.stats)) {
       const int r64 = row0 / kKvBlock + tid;  // 64-row block index
       if (r64 * kKvBlock < p.N) {
-        unsigned long long* st = p.stats + 2 * (((int64_t)b * p.Hq + h) * (p.N / kKvBlock) + r64);
+        unsigned long long* st = p.stats + 2 * (((int64_t)b * p.Hq + h) * n_tiles + r64);
         st[0] = lds_cnt[tid][0];
         st[1] = lds_cnt[tid][1];
       }
@@ -2320,8 +2344,9 @@ bool is_pow2(float S) {
 }
 
 template <int D, bool kFp8>
-void launch_prep(const uint16_t* V, void* ws, int64_t n_blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((pcast_prep_v<D, kFp8>), dim3((unsigned)n_blocks), dim3(256), 0, stream, V, ws);
+void launch_prep(const uint16_t* V, void* ws, int64_t n_blocks, int N, hipStream_t stream) {
+  const int n_tiles = (N + kKvBlock - 1) / kKvBlock;
+  hipLaunchKernelGGL((pcast_prep_v<D, kFp8>), dim3((unsigned)n_blocks), dim3(256), 0, stream, V, ws, N, n_tiles);
 }
 
 template <int D, int kMode, bool kCausal>
@@ -2463,7 +2488,8 @@ size_t pcast_stats_words(int B, int Hq, int N) {
 
 size_t pcast_workspace_bytes(int B, int Hkv, int N, int d, float S) {
   if (B <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return 0;
-  return (size_t)B * Hkv * N * d * ((S == 0.0f) ? 2 : 1);
+  const size_t keys = (size_t)(N + kKvBlock - 1) / kKvBlock * kKvBlock;  // whole key blocks
+  return (size_t)B * Hkv * keys * d * ((S == 0.0f) ? 2 : 1);
 }
 
 size_t pcast_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
@@ -2507,14 +2533,18 @@ const char* pcast_strerror(int code) {
 namespace {
 
 // Shape and scalar checks shared by the entry points.  Nothing here touches the device.
-int check_shape(int B, int Hq, int Hkv, int N, int d, float S) {
+// any_n: the entry point takes any N >= 1 on the P-cast path (S > 0), a partial last
+// key block being masked past N; otherwise N must be a multiple of 64.
+int check_shape(int B, int Hq, int Hkv, int N, int d, float S, bool any_n = false) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0)
     return fail(PCAST_EINVAL, "B, Hq, Hkv, N, d must be positive");
   if (Hq % Hkv != 0) return fail(PCAST_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (!std::isfinite(S) || S < 0.0f) return fail(PCAST_EINVAL, "S must be finite and >= 0");
   if (d != 64 && d != 128) return fail(PCAST_ENOTSUP, "d = %d: supported head sizes are 64 and 128", d);
-  if (N % kKvBlock != 0) return fail(PCAST_ENOTSUP, "N = %d: must be a multiple of %d", N, kKvBlock);
-  if ((int64_t)B * Hkv * (N / kKvBlock) > (int64_t)INT32_MAX ||
+  if (N % kKvBlock != 0 && !(any_n && S > 0.0f))
+    return fail(PCAST_ENOTSUP, "N = %d: must be a multiple of %d%s", N, kKvBlock,
+                any_n ? " on the bf16 reference path (S = 0)" : " for this entry point");
+  if ((int64_t)B * Hkv * ((N + kKvBlock - 1) / kKvBlock) > (int64_t)INT32_MAX ||
       (int64_t)B * Hq * ((N + kBlockRows - 1) / kBlockRows) > (int64_t)INT32_MAX)
     return fail(PCAST_ENOTSUP, "grid too large");
   return PCAST_OK;
@@ -2545,12 +2575,12 @@ int check_device() {
 
 int enqueue_prep(const void* V, int B, int Hkv, int N, int d, float S, void* ws, hipStream_t st) {
   const bool fp8 = S != 0.0f;
-  const int64_t n_blocks = (int64_t)B * Hkv * (N / kKvBlock);
+  const int64_t n_blocks = (int64_t)B * Hkv * ((N + kKvBlock - 1) / kKvBlock);
   const uint16_t* Vb = static_cast<const uint16_t*>(V);
   if (d == 64) {
-    if (fp8) launch_prep<64, true>(Vb, ws, n_blocks, st); else launch_prep<64, false>(Vb, ws, n_blocks, st);
+    if (fp8) launch_prep<64, true>(Vb, ws, n_blocks, N, st); else launch_prep<64, false>(Vb, ws, n_blocks, N, st);
   } else {
-    if (fp8) launch_prep<128, true>(Vb, ws, n_blocks, st); else launch_prep<128, false>(Vb, ws, n_blocks, st);
+    if (fp8) launch_prep<128, true>(Vb, ws, n_blocks, N, st); else launch_prep<128, false>(Vb, ws, n_blocks, N, st);
   }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? PCAST_OK : hip_fail(e, "V pre-pass launch");
@@ -2706,7 +2736,7 @@ int pcast_prepare_v(const void* V, int B, int Hkv, int N, int d, float S, void* 
   if (!V || !workspace) return fail(PCAST_EINVAL, "V and workspace must be non-null");
   if (!aligned(V, 16) || !aligned(workspace, 16))
     return fail(PCAST_EINVAL, "V and workspace must be 16-byte aligned");
-  int rc = check_shape(B, Hkv, Hkv, N, d, S);
+  int rc = check_shape(B, Hkv, Hkv, N, d, S, true);
   if (rc != PCAST_OK) return rc;
   if ((rc = check_device()) != PCAST_OK) return rc;
   return enqueue_prep(V, B, Hkv, N, d, S, workspace, static_cast<hipStream_t>(stream));
@@ -2720,7 +2750,7 @@ int attn_fwd_pcast_prepared(const void* Q, const void* K, const void* workspace,
   if (!aligned(workspace, 16)) return fail(PCAST_EINVAL, "workspace must be 16-byte aligned");
   int rc = check_attn_args(Q, K, bias, causal, order, out, stats);
   if (rc != PCAST_OK) return rc;
-  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S, true)) != PCAST_OK) return rc;
   if ((rc = check_device()) != PCAST_OK) return rc;
   return enqueue_attn(Q, K, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
                       static_cast<hipStream_t>(stream));
@@ -2735,7 +2765,7 @@ int attn_fwd_pcast(const void* Q, const void* K, const void* V, const float* bia
   if (rc != PCAST_OK) return rc;
   if (!V) return fail(PCAST_EINVAL, "V must be non-null");
   if (!aligned(V, 16)) return fail(PCAST_EINVAL, "V must be 16-byte aligned");
-  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S, true)) != PCAST_OK) return rc;
   if ((rc = check_device()) != PCAST_OK) return rc;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -2758,7 +2788,7 @@ int attn_fwd_pcast_noalloc(const void* Q, const void* K, const void* V, const fl
   if (rc != PCAST_OK) return rc;
   if (!V) return fail(PCAST_EINVAL, "V must be non-null");
   if (!aligned(V, 16)) return fail(PCAST_EINVAL, "V must be 16-byte aligned");
-  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S, true)) != PCAST_OK) return rc;
   const size_t need = pcast_workspace_bytes(B, Hkv, N, d, S);
   if (need > (size_t)PCAST_NOALLOC_SCRATCH_BYTES)
     return fail(PCAST_ENOTSUP,
@@ -2795,7 +2825,7 @@ int attn_fwd_pcast_multi(const void* Q, const void* K, const void* workspace, in
     if (!std::isfinite(S[i]) || S[i] < 0.0f) return fail(PCAST_EINVAL, "S[%d] must be finite and >= 0", i);
     if (S[i] == 0.0f) return fail(PCAST_ENOTSUP, "S[%d] = 0: the multi-configuration call runs the FP8 P.V path only", i);
   }
-  int rc = check_shape(B, Hq, Hkv, N, d, S[0]);
+  int rc = check_shape(B, Hq, Hkv, N, d, S[0], true);
   if (rc != PCAST_OK) return rc;
   if ((int64_t)B * Hq * ((N + kBlockRows - 1) / kBlockRows) * kMaxCells > (int64_t)INT32_MAX)
     return fail(PCAST_ENOTSUP, "grid too large");
@@ -2851,7 +2881,7 @@ int attn_fwd_pcast_rows(const void* Q, const void* K, const void* workspace, con
   if (rc != PCAST_OK) return rc;
   if ((lse && !aligned(lse, 4)) || (lost && !aligned(lost, 4)))
     return fail(PCAST_EINVAL, "lse and lost must be 4-byte aligned");
-  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S, true)) != PCAST_OK) return rc;
   if (S == 0.0f) return fail(PCAST_ENOTSUP, "row diagnostics need S > 0 (the FP8 P.V path)");
   if ((rc = check_device()) != PCAST_OK) return rc;
   return enqueue_attn(Q, K, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,

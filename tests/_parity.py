@@ -34,11 +34,12 @@ def to_gpu_bf16(bits: np.ndarray, device="cuda:0"):
 
 
 def block_rows(B: int, Hq: int, N: int, blocks):
-    """Flat row ids of the listed (b, h, r64) blocks, 64 rows each."""
+    """Flat row ids of the listed (b, h, r64) blocks: 64 rows each, fewer in a partial
+    last block (N not a multiple of 64)."""
     ids = []
     for b, h, r in blocks:
-        base = (b * Hq + h) * N + r * 64
-        ids.append(np.arange(base, base + 64, dtype=np.int64))
+        base = (b * Hq + h) * N
+        ids.append(np.arange(base + r * 64, base + min(r * 64 + 64, N), dtype=np.int64))
     return np.concatenate(ids) if ids else np.zeros(0, dtype=np.int64)
 
 
@@ -133,13 +134,13 @@ def compare(out_gpu: np.ndarray, stats_gpu, qb, kb, vb, bias, causal, S, order, 
             atol: float = ATOL, eps: float = EPS, nthreads: int = 0, extra=None):
     """Compare GPU results with the oracle on the given blocks (all rows if None).
 
-    out_gpu: [B,Hq,N,d] float array; stats_gpu: [B,Hq,N/64,2] ints or None.
+    out_gpu: [B,Hq,N,d] float array; stats_gpu: [B,Hq,ceil(N/64),2] ints or None.
     extra: optional callable(ids) -> per-row tolerance added to atol + slack.
     Returns a report dict; raises AssertionError on a parity failure.
     """
     B, Hq, N, d = qb.shape
     if blocks is None:
-        blocks = [(b, h, r) for b in range(B) for h in range(Hq) for r in range(N // 64)]
+        blocks = [(b, h, r) for b in range(B) for h in range(Hq) for r in range((N + 63) // 64)]
     ids = block_rows(B, Hq, N, blocks)
     mode = "bf16" if S == 0 else "kernel"
     ref = core.rows(qb, kb, vb, bias, causal, S if S != 0 else 1.0, order, mode, row_ids=ids,
@@ -167,9 +168,11 @@ def compare(out_gpu: np.ndarray, stats_gpu, qb, kb, vb, bias, causal, S, order, 
         assert rep["max_dev_exact"] <= 5e-3, f"bf16 path vs fp64: {rep['max_dev_exact']:.3g}"
     if stats_gpu is not None:
         nblk = len(blocks)
-        o_tot = ref["total"].reshape(nblk, 64).sum(axis=1)
-        o_zero = ref["zero"].reshape(nblk, 64).sum(axis=1)
-        o_amb = ref["zero_amb"].reshape(nblk, 64).sum(axis=1)
+        # rows per block: 64, or fewer in a partial last block
+        starts = np.cumsum([0] + [min(64, N - r * 64) for (_, _, r) in blocks[:-1]])
+        o_tot = np.add.reduceat(ref["total"], starts)
+        o_zero = np.add.reduceat(ref["zero"], starts)
+        o_amb = np.add.reduceat(ref["zero_amb"], starts)
         g = np.array([stats_gpu[b, h, r] for (b, h, r) in blocks], dtype=np.int64).reshape(nblk, 2)
         assert np.array_equal(g[:, 0], o_tot), "pair counts differ"
         assert np.all(np.abs(g[:, 1] - o_zero) <= o_amb), "underflow counts differ beyond near ties"

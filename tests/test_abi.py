@@ -41,6 +41,20 @@ def test_version_and_sizes(lib):
     assert sna.workspace_bytes(4, 32, 8192, 128, 0.0) == 2 * 4 * 32 * 8192 * 128
 
 
+def test_sizes_for_any_sequence_length(lib):
+    # the V copy and the counters take whole 64-key blocks; the bf16 path and the
+    # FP8-logit path keep N a multiple of 64
+    for N in (1, 63, 65, 100, 4097):
+        nb = (N + 63) // 64
+        assert sna.workspace_bytes(2, 3, N, 128, 256.0) == 2 * 3 * nb * 64 * 128
+        assert sna.workspace_bytes(2, 3, N, 64, 0.0) == 2 * 2 * 3 * nb * 64 * 64
+        assert sna.stats_words(2, 5, N) == 2 * 5 * nb * 2
+    rc = _call(N=100, S=0.0)
+    assert rc == sna.PCAST_ENOTSUP and "bf16 reference path" in sna.strerror(rc)
+    rc = sna.attn_fwd_pcast_qk8(FAKE, FAKE, FAKE, 0, 1, 2, 1, 100, 128, 1, 256.0, 1, FAKE, 0, 0)
+    assert rc == sna.PCAST_ENOTSUP and "multiple of 64" in sna.strerror(rc)
+
+
 def _call(**kw):
     a = dict(Q=FAKE, K=FAKE, V=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128, causal=1, S=256.0,
              order=1, out=FAKE, stats=0, stream=0)
@@ -61,7 +75,7 @@ def _call(**kw):
     (dict(Q=FAKE + 8), sna.PCAST_EINVAL),
     (dict(stats=FAKE + 4), sna.PCAST_EINVAL),
     (dict(d=96), sna.PCAST_ENOTSUP),
-    (dict(N=100), sna.PCAST_ENOTSUP),
+    (dict(N=100, S=0.0), sna.PCAST_ENOTSUP),  # any N only on the P-cast path
 ])
 def test_argument_errors(lib, kw, code):
     assert _call(**kw) == code
@@ -73,7 +87,7 @@ def test_argument_errors(lib, kw, code):
     (dict(workspace=FAKE + 4), sna.PCAST_EINVAL),
     (dict(Q=0), sna.PCAST_EINVAL),
     (dict(order=5), sna.PCAST_EINVAL),
-    (dict(N=96), sna.PCAST_ENOTSUP),
+    (dict(N=96, S=0.0), sna.PCAST_ENOTSUP),
 ])
 def test_prepared_argument_errors(lib, kw, code):
     a = dict(Q=FAKE, K=FAKE, workspace=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128, causal=1,
@@ -333,7 +347,6 @@ def _multi(**kw):
     (dict(biases=[FAKE + 2, 0]), sna.PCAST_EINVAL),
     (dict(Ss=[256.0, 0.0]), sna.PCAST_ENOTSUP),
     (dict(d=96), sna.PCAST_ENOTSUP),
-    (dict(N=100), sna.PCAST_ENOTSUP),
     (dict(Hq=3, Hkv=2), sna.PCAST_EINVAL),
 ])
 def test_multi_argument_errors(lib, kw, code):

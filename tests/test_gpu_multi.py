@@ -65,3 +65,9 @@ def test_multi_sweep_cells(sna):
     w = synthetic.WORKLOADS["sweep"]
     configs = [c for i, c in enumerate(w.cases) if i % 12 == 0]
     _check(sna, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, configs, w.seed)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_multi_ragged_sequence(sna, causal):
+    # N = 200: a partial last key block in every cell
+    _check(sna, 1, 2, 1, 200, 128, causal, CONFIGS[::3], 64)

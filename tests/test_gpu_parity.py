@@ -91,6 +91,46 @@ def test_partial_workgroups(sna, N, order):
     _case(sna, f"partial N={N}", 3, 6, 3, N, 128, True, 7.0, 256.0, order, 32)
 
 
+@pytest.mark.parametrize("N", [37, 100, 321])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("order", [0, 1])
+def test_ragged_sequence(sna, N, d, causal, order):
+    # N not a multiple of 64: the last key block is partial (keys past N masked), the
+    # last 64-row counter block short, and rows past N neither stored nor counted
+    _case(sna, f"ragged N={N}", 2, 4, 2, N, d, causal, 7.0, 256.0, order, 34)
+
+
+@pytest.mark.parametrize("S", [1.0, 448.0, 512.0, 3.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_sequence_scales(sna, S, causal):
+    _case(sna, "ragged scales", 1, 2, 1, 200, 128, causal, 7.0, S, 0, 35)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_sequence_random_bias(sna, causal):
+    B, Hq, Hkv, N, d, seed = 1, 3, 3, 150, 128, 36
+    print(f"\n[case] ragged random bias: N={N} causal={causal}", flush=True)
+    qb, kb, vb = synthetic.qkv_bf16(B, Hq, Hkv, N, d, seed)
+    bias = synthetic.random_bias(N, seed)
+    out, st = _run(sna, qb, kb, vb, bias, causal, 256.0, 1)
+    rep = _parity.compare(out, st, qb, kb, vb, bias, causal, 256.0, 1)
+    print(f"[case] ragged random bias: {rep}", flush=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_row(sna, causal):
+    # N = 1: one query, one key; the output is E4M3(V[0]) exactly
+    rep = _case(sna, "one row", 1, 2, 1, 1, 64, causal, None, 256.0, 1, 37)
+    assert rep["max_dev"] == 0.0
+
+
+def test_ragged_sequence_s0_rejected(sna):
+    q = torch.zeros(1, 1, 100, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sna.PcastError):
+        sna.forward(q, q, q, None, causal=True, S=0.0)
+
+
 def test_many_small_heads(sna):
     # a wide grid of short rows: 8 x 16 heads of 128 rows, groups of 4 query heads
     _case(sna, "many heads", 8, 16, 4, 128, 128, False, 7.0, 256.0, 1, 33)
@@ -132,9 +172,10 @@ def test_errors_are_reported(sna):
     with pytest.raises(sna.PcastError) as ei:
         sna.forward(q, q, q, None, S=256.0)
     assert ei.value.code == sna.PCAST_ENOTSUP
+    # N = 96 is supported on the P-cast path, not on the bf16 reference path
     q = torch.zeros(1, 1, 96, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(sna.PcastError) as ei:
-        sna.forward(q, q, q, None, S=256.0)
+        sna.forward(q, q, q, None, S=0.0)
     assert ei.value.code == sna.PCAST_ENOTSUP
     # a caller's out must be a contiguous fp32 [B, Hq, N, d] tensor on the same device
     q = torch.zeros(1, 2, 128, 64, dtype=torch.bfloat16, device="cuda")

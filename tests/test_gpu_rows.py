@@ -97,6 +97,16 @@ def test_small_grid(sna, d, causal, order, S):
     print(f"[case] rows grid: {rep}", flush=True)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("order", [0, 1])
+def test_ragged_sequence(sna, causal, order):
+    print(f"\n[case] rows ragged N=200 causal={causal} order={order}", flush=True)
+    qb, kb, vb = synthetic.qkv_bf16(1, 2, 1, 200, 128, 73)
+    bias = synthetic.sink_bias(200, 7.0)
+    rep = _check(_run(sna, qb, kb, vb, bias, causal, 1.0, order), qb, kb, bias, causal, 1.0, order)
+    print(f"[case] rows ragged: {rep}", flush=True)
+
+
 @pytest.mark.parametrize("bias_kind", ["none", "random", "strong"])
 def test_bias_kinds(sna, bias_kind):
     print(f"\n[case] rows bias {bias_kind}", flush=True)

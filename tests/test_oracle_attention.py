@@ -84,6 +84,25 @@ def test_twins_agree(mode, order):
         assert np.array_equal(r["zero"].reshape(zs.shape), zs)
 
 
+@pytest.mark.parametrize("mode", reference.MODES)
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("causal", [False, True])
+def test_twins_agree_with_a_partial_last_block(mode, order, causal):
+    """N = 200: the last key block holds 8 keys; the C core, the sequential twin (which
+    visits the keys of each block that exist) and the vectorised twin agree."""
+    q, k, v = _inputs(1, 2, 1, 200, 64, 16)
+    bias = synthetic.sink_bias(200, 7.0)
+    for S in (1.0, 256.0, 512.0):
+        _, seq, ts, zs = reference.attention_oracle(q, k, v, bias, causal, S, order, mode, sequential=True)
+        _, vec, tv, zv = reference.attention_oracle(q, k, v, bias, causal, S, order, mode)
+        r = core.rows(q, k, v, bias, causal, S, order, mode)
+        assert np.max(np.abs(seq - vec)) < 1e-12
+        assert np.max(np.abs(r["o2"].reshape(seq.shape) - seq)) < 1e-12
+        assert np.array_equal(ts, tv) and np.array_equal(zs, zv)
+        assert np.array_equal(r["total"].reshape(ts.shape), ts)
+        assert np.array_equal(r["zero"].reshape(zs.shape), zs)
+
+
 @pytest.mark.parametrize("S", [1.0, 2.0, 16.0, 256.0, 448.0])
 @pytest.mark.parametrize("order", [0, 1])
 def test_zero_queries_give_mean_of_cast_values(S, order):

@@ -33,10 +33,11 @@ def _logits(q_bits, k_bits, bias, causal):
     return s
 
 
+@pytest.mark.parametrize("N", [256, 200])
 @pytest.mark.parametrize("causal", [False, True])
-def test_lse_matches_torch(causal):
-    q, k, _ = synthetic.qkv_bf16(1, 2, 2, 256, 64, 61)
-    bias = synthetic.random_bias(256, 61)
+def test_lse_matches_torch(causal, N):
+    q, k, _ = synthetic.qkv_bf16(1, 2, 2, N, 64, 61)
+    bias = synthetic.random_bias(N, 61)
     r = rowdiag.rows(q, k, bias, causal, 256.0, 1)
     want = torch.logsumexp(_logits(q, k, bias, causal), dim=-1).numpy().ravel()
     assert np.max(np.abs(r["lse"] - want)) < 1e-12 * np.max(np.abs(want))
@@ -45,9 +46,10 @@ def test_lse_matches_torch(causal):
 @pytest.mark.parametrize("S,order,causal,delta", [(1.0, 0, True, 7.0), (1.0, 1, True, 7.0),
                                                    (256.0, 0, False, 9.0), (448.0, 1, True, 12.0),
                                                    (3.0, 0, True, 5.0), (512.0, 0, True, 11.0)])
-def test_zero_decisions_match_core_counter(S, order, causal, delta):
-    q, k, v = synthetic.qkv_bf16(1, 2, 2, 320, 64, 62)
-    bias = synthetic.sink_bias(320, delta)
+@pytest.mark.parametrize("N", [320, 300])  # 300: a partial last key block
+def test_zero_decisions_match_core_counter(S, order, causal, delta, N):
+    q, k, v = synthetic.qkv_bf16(1, 2, 2, N, 64, 62)
+    bias = synthetic.sink_bias(N, delta)
     r = rowdiag.rows(q, k, bias, causal, S, order)
     c = core.rows(q, k, v, bias, causal, S, order, "kernel", want_exact=False)
     assert np.array_equal(r["zero"], c["zero"])

@@ -41,6 +41,7 @@ CASES = [
     (2, 8, 2, 2048, 128, 1, 256.0, 1),   # 2 MiB of scratch
     (1, 2, 1, 192, 64, 0, 1.0, 0),       # smaller, another head size, non-causal, forward
     (1, 4, 4, 256, 128, 1, 0.0, 0),      # the bf16 path (a bf16 V copy)
+    (1, 2, 1, 200, 128, 0, 256.0, 1),    # a partial last key block (zero-padded V copy)
     (2, 8, 2, 2048, 128, 1, 448.0, 0),   # the first size again
 ]
 
