@@ -131,6 +131,34 @@ def test_ragged_sequence_s0_rejected(sna):
         sna.forward(q, q, q, None, causal=True, S=0.0)
 
 
+def _random_configs(n, seed):
+    """n seeded mixed configurations: shapes (any N up to 700, grouped kv heads, d 64 / 128),
+    mask, order, every conversion mode of S, and no / sink / random bias."""
+    rng = np.random.default_rng(seed)
+    heads = [(1, 1), (4, 2), (8, 1), (3, 3)]
+    scales = [1.0, 2.0, 3.0, 16.0, 256.0, 300.0, 448.0, 512.0, 1000.0]
+    out = []
+    for i in range(n):
+        Hq, Hkv = heads[rng.integers(len(heads))]
+        out.append(dict(B=int(rng.integers(1, 3)), Hq=Hq, Hkv=Hkv, N=int(rng.integers(1, 701)),
+                        d=int(rng.choice([64, 128])), causal=bool(rng.integers(2)), order=int(rng.integers(2)),
+                        S=float(rng.choice(scales)), bias=str(rng.choice(["none", "sink", "random"])),
+                        delta=float(rng.uniform(0.0, 12.0)), seed=1000 + i))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(40, 2024), ids=lambda c: f"N{c['N']}-d{c['d']}-S{c['S']:g}")
+def test_random_configurations(sna, cfg):
+    c = cfg
+    print(f"\n[case] random configuration: {c}", flush=True)
+    qb, kb, vb = synthetic.qkv_bf16(c["B"], c["Hq"], c["Hkv"], c["N"], c["d"], c["seed"])
+    bias = {"none": None, "sink": synthetic.sink_bias(c["N"], c["delta"]),
+            "random": synthetic.random_bias(c["N"], c["seed"])}[c["bias"]]
+    out, st = _run(sna, qb, kb, vb, bias, c["causal"], c["S"], c["order"])
+    rep = _parity.compare(out, st, qb, kb, vb, bias, c["causal"], c["S"], c["order"])
+    print(f"[case] random configuration: {rep}", flush=True)
+
+
 def test_many_small_heads(sna):
     # a wide grid of short rows: 8 x 16 heads of 128 rows, groups of 4 query heads
     _case(sna, "many heads", 8, 16, 4, 128, 128, False, 7.0, 256.0, 1, 33)
