@@ -378,3 +378,90 @@ def forward_multi(q, k, v, configs, causal: bool = True, stats: bool = False):
     if rc != PCAST_OK:
         raise PcastError(rc, strerror(rc))
     return outs, (None if sts is None else [x.view(B, Hq, -1, 2) for x in sts])
+
+
+_ATTENTION_FUNCTION = None
+
+
+def _attention_function():
+    """The torch.autograd.Function behind attention(), defined on first use (torch is
+    imported lazily by this package)."""
+    global _ATTENTION_FUNCTION
+    if _ATTENTION_FUNCTION is not None:
+        return _ATTENTION_FUNCTION
+    import torch
+
+    class PcastAttention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, bias, causal, S, order):
+            _check_qkv(q, k, v, bias)
+            if not S > 0:
+                raise ValueError("attention() needs S > 0 (the P-cast path; its log-sum-exp feeds the backward)")
+            B, Hq, N, d = q.shape
+            Hkv = k.shape[1]
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+            ws = torch.empty(workspace_bytes(B, Hkv, N, d, S), dtype=torch.uint8, device=q.device)
+            out = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+            lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+            bp = 0 if bias is None else bias.data_ptr()
+            rc = prepare_v(v.data_ptr(), B, Hkv, N, d, S, ws.data_ptr(), stream)
+            if rc == PCAST_OK:
+                # lost NULL: the pipelined forward writes out and lse alone
+                rc = attn_fwd_pcast_rows(q.data_ptr(), k.data_ptr(), ws.data_ptr(), bp, B, Hq, Hkv, N, d, causal, S,
+                                         ORDERS[order], out.data_ptr(), 0, lse.data_ptr(), 0, stream)
+            if rc != PCAST_OK:
+                raise PcastError(rc, strerror(rc))
+            ctx.causal = bool(causal)
+            ctx.has_bias = bias is not None
+            ctx.save_for_backward(q, k, v, out, lse, *([bias] if bias is not None else []))
+            return out
+
+        @staticmethod
+        def backward(ctx, grad_out):
+            q, k, v, out, lse, *rest = ctx.saved_tensors
+            bias = rest[0] if ctx.has_bias else None
+            B, Hq, N, d = q.shape
+            Hkv = k.shape[1]
+            # the backward's C ABI takes dO in bf16 and writes fp32 gradients; the
+            # conversions to and from the inputs' bf16 are torch's
+            do = grad_out.to(torch.bfloat16).contiguous()
+            dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+            dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
+            dv = torch.empty_like(dk)
+            wb = torch.empty(bwd_workspace_bytes(B, Hq, Hkv, N, d), dtype=torch.uint8, device=q.device)
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+            rc = attn_bwd_pcast(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), do.data_ptr(),
+                                lse.data_ptr(), 0 if bias is None else bias.data_ptr(), B, Hq, Hkv, N, d,
+                                ctx.causal, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), wb.data_ptr(), stream)
+            if rc != PCAST_OK:
+                raise PcastError(rc, strerror(rc))
+            return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None, None
+
+    _ATTENTION_FUNCTION = PcastAttention
+    return PcastAttention
+
+
+def _check_qkv(q, k, v, bias):
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D bfloat16 tensor on the GPU")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, N, d] matching q")
+    if bias is not None and (bias.dtype != torch.float32 or not bias.is_cuda or bias.shape != (N,)
+                             or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 [N] tensor on the GPU")
+
+
+def attention(q, k, v, bias=None, causal: bool = True, S: float = 256.0, order="reverse"):
+    """The P-cast forward as a differentiable torch operation (S > 0): out fp32
+    [B, Hq, N, d].  The forward runs pcast_prepare_v and attn_fwd_pcast_rows (out and
+    the log-sum-exp, no counters); the backward runs attn_bwd_pcast on the saved q, k,
+    v, out and log-sum-exp, i.e. the gradients of exact attention taken at the
+    forward's output (the cast itself has no gradient), with dO rounded to bf16 and
+    the fp32 gradients rounded to the inputs' bf16 by torch.  The backward needs
+    N % 64 == 0.  The bias gets no gradient."""
+    return _attention_function().apply(q, k, v, bias, causal, float(S), order)

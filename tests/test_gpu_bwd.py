@@ -135,3 +135,40 @@ def test_deterministic(sna):
     b = _run(sna, qb, kb, vb, dob, None, True)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("bias_kind", ["none", "sink"])
+def test_autograd_attention_equals_direct_calls(sna, bias_kind):
+    """softmax_numerics_amd.attention under autograd: out equals the plain forward and the
+    gradients equal the C backward's (rounded to bf16) on the same dO, bit for bit."""
+    B, Hq, Hkv, N, d, seed = 1, 4, 2, 256, 64, 91
+    print(f"\n[case] autograd attention: bias={bias_kind}", flush=True)
+    qb, kb, vb = synthetic.qkv_bf16(B, Hq, Hkv, N, d, seed)
+    q, k, v = (_parity.to_gpu_bf16(x).requires_grad_(True) for x in (qb, kb, vb))
+    bias = None if bias_kind == "none" else torch.from_numpy(synthetic.sink_bias(N, 7.0)).cuda()
+    out = sna.attention(q, k, v, bias, causal=True, S=256.0, order="reverse")
+    g = torch.from_numpy(np.random.default_rng(seed).standard_normal((B, Hq, N, d)).astype(np.float32)).cuda()
+    out.backward(g)
+    torch.cuda.synchronize()
+    ref, _ = sna.forward(q.detach(), k.detach(), v.detach(), bias, causal=True, S=256.0, order="reverse")
+    assert torch.equal(out.detach(), ref)
+    st = torch.cuda.current_stream().cuda_stream
+    ws = torch.empty(sna.workspace_bytes(B, Hkv, N, d, 256.0), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, Hq, N, d), device="cuda")
+    lse = torch.empty((B, Hq, N), device="cuda")
+    bp = 0 if bias is None else bias.data_ptr()
+    assert sna.prepare_v(v.data_ptr(), B, Hkv, N, d, 256.0, ws.data_ptr(), st) == 0
+    assert sna.attn_fwd_pcast_rows(q.data_ptr(), k.data_ptr(), ws.data_ptr(), bp, B, Hq, Hkv, N, d, True, 256.0, 1,
+                                   o.data_ptr(), 0, lse.data_ptr(), 0, st) == 0
+    do = g.to(torch.bfloat16).contiguous()
+    dq = torch.empty((B, Hq, N, d), device="cuda")
+    dk = torch.empty((B, Hkv, N, d), device="cuda")
+    dv = torch.empty_like(dk)
+    wb = torch.empty(sna.bwd_workspace_bytes(B, Hq, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    assert sna.attn_bwd_pcast(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                              bp, B, Hq, Hkv, N, d, True, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                              wb.data_ptr(), st) == 0
+    torch.cuda.synchronize()
+    for got, want in ((q.grad, dq), (k.grad, dk), (v.grad, dv)):
+        assert got.dtype == torch.bfloat16 and torch.equal(got, want.to(torch.bfloat16))
+
