@@ -60,8 +60,8 @@ def rows(q_bits, k_bits, v_bits, bias, S: float, order: int, split_keys: int, mo
     """
     B, Hq, Nq, d = q_bits.shape
     Hkv, Nk = k_bits.shape[1], k_bits.shape[2]
-    if split_keys % bc or Nk % bc:
-        raise ValueError("split_keys and Nk must be multiples of the block size")
+    if split_keys % bc:
+        raise ValueError("split_keys must be a multiple of the block size")
     G = Hq // Hkv
     nonsink = np.ones(Nk, dtype=bool) if bias is None else (np.asarray(bias) == 0)
     bvec = np.zeros(Nk) if bias is None else np.asarray(bias, dtype=np.float64)

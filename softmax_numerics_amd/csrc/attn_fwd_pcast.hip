@@ -1496,7 +1496,8 @@ __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
 
   const int lane = threadIdx.x;
   const int g = lane / 32, li = lane % 32;
-  const int n_blk = p.Nk / kKvBlock;
+  // key blocks of the cache; with Nk not a multiple of 64 the last one is partial
+  const int n_blk = (p.Nk + kKvBlock - 1) / kKvBlock, n_full = p.Nk / kKvBlock;
   const int split = blockIdx.x % p.n_split;
   const int bhk = blockIdx.x / p.n_split;
   const int hk = bhk % p.Hkv, b = bhk / p.Hkv;
@@ -1554,10 +1555,12 @@ __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
   // load i fills LDS chunk position i * 64 + lane, which holds logical chunk position ^ key(row)
   auto load_k = [&](int t) __attribute__((always_inline)) {
     const uint8_t* ks = kbase + (int64_t)t * kKTile;
+    // rows past Nk of a partial last block read row Nk - 1 instead (no row sees them)
+    const int last = t < n_full ? kKvBlock - 1 : p.Nk - 1 - t * kKvBlock;
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
       const int cp = i * 64 + lane, r = cp / SK::kChunks;
-      load_to_lds16(ks + r * kKRow + (((cp % SK::kChunks) ^ SK::key(r)) << 4), lds_k + i * 1024);
+      load_to_lds16(ks + min(r, last) * kKRow + (((cp % SK::kChunks) ^ SK::key(r)) << 4), lds_k + i * 1024);
     }
   };
   auto load_v = [&](int t, int buf) __attribute__((always_inline)) {
@@ -1569,7 +1572,7 @@ __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
     }
   };
   auto load_b = [&](int t, int buf) __attribute__((always_inline)) {
-    if (with_bias) load_to_lds4(p.bias + t * kKvBlock + lane, bbuf(buf));
+    if (with_bias) load_to_lds4(p.bias + min(t * kKvBlock + lane, p.Nk - 1), bbuf(buf));
   };
   auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -1654,13 +1657,15 @@ __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
       for (int r = 2; r < 8; r += 2)
         m4[q] = fmaxf(fmaxf(m4[q], sacc[q / 2][(q % 2) * 8 + r]), sacc[q / 2][(q % 2) * 8 + r + 1]);
     }
-    // every row sees at least one key of every block (Nq <= 32 < 64), so m_new is finite
+    // a row may see no key of a partial last block (Nk % 64 < Nq): then m_new stays -inf
+    // while the row has seen nothing, and every p of the block is 0
     const float m_new = fmaxf(m_run, halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))));
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      const float pj = __builtin_amdgcn_exp2f(sacc[j / 16][j % 16] - m_new);
+      const float pj = __builtin_amdgcn_exp2f(sacc[j / 16][j % 16] - m_use);
       sacc[j / 16][j % 16] = pj;
       ps[j % 4] += pj;
     }
@@ -2650,7 +2655,7 @@ int enqueue_attn(const void* Q, const void* K, const void* ws, const float* bias
 // Argument checks shared by the decode entry points (Q, out, workspace; shapes).
 int check_decode(const void* Q, const float* bias, int B, int Hq, int Hkv, int Nq, int Nk, int d, float S,
                  int order, int split_keys, const float* out, const unsigned long long* stats,
-                 const void* workspace) {
+                 const void* workspace, bool any_nk) {
   if (!aligned(Q, 16) || !aligned(out, 16) || !aligned(workspace, 16))
     return fail(PCAST_EINVAL, "Q, out and workspace must be 16-byte aligned");
   if (bias && !aligned(bias, 4)) return fail(PCAST_EINVAL, "bias must be 4-byte aligned");
@@ -2658,9 +2663,10 @@ int check_decode(const void* Q, const float* bias, int B, int Hq, int Hkv, int N
   if (order != PCAST_ORDER_FORWARD && order != PCAST_ORDER_REVERSE)
     return fail(PCAST_EINVAL, "order must be 0 (forward) or 1 (reverse)");
   if (Nq <= 0) return fail(PCAST_EINVAL, "Nq must be positive");
+  if (Nq > Nk) return fail(PCAST_EINVAL, "Nq = %d exceeds Nk = %d: the rows sit at the last Nq positions", Nq, Nk);
   if (split_keys <= 0 || split_keys % kKvBlock != 0)
     return fail(PCAST_EINVAL, "split_keys must be a positive multiple of %d", kKvBlock);
-  int rc = check_shape(B, Hq, Hkv, Nk, d, S);
+  int rc = check_shape(B, Hq, Hkv, Nk, d, S, any_nk);
   if (rc != PCAST_OK) return rc;
   if (S == 0.0f) return fail(PCAST_ENOTSUP, "decode needs S > 0 (the FP8 P.V path)");
   if ((int64_t)(Hq / Hkv) * Nq > 32)
@@ -2967,7 +2973,7 @@ int attn_decode_pcast(const void* Q, const void* K, const void* vop, const float
     return fail(PCAST_EINVAL, "Q, K, vop, out and workspace must be non-null");
   if (!aligned(K, 16) || !aligned(vop, 16))
     return fail(PCAST_EINVAL, "Q, K, vop, out and workspace must be 16-byte aligned");
-  const int rc = check_decode(Q, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out, stats, workspace);
+  const int rc = check_decode(Q, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out, stats, workspace, true);
   if (rc != PCAST_OK) return rc;
   return enqueue_decode(Q, K, vop, nullptr, nullptr, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out,
                         stats, workspace, static_cast<hipStream_t>(stream));
@@ -2981,7 +2987,7 @@ int attn_decode_pcast_qk8(const void* Q, const void* qk8_workspace, const float*
     return fail(PCAST_EINVAL, "Q, qk8_workspace, out and workspace must be non-null");
   if (!aligned(qk8_workspace, 16))
     return fail(PCAST_EINVAL, "Q, qk8_workspace, out and workspace must be 16-byte aligned");
-  const int rc = check_decode(Q, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out, stats, workspace);
+  const int rc = check_decode(Q, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out, stats, workspace, false);
   if (rc != PCAST_OK) return rc;
   const Qk8Layout l = qk8_layout(B, Hkv, Nk, d);
   const uint8_t* base = static_cast<const uint8_t*>(qk8_workspace);

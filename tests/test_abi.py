@@ -186,13 +186,13 @@ def test_decode_workspace_layout(lib):
     (dict(vop=0), sna.PCAST_EINVAL),
     (dict(workspace=FAKE + 8), sna.PCAST_EINVAL),
     (dict(Nq=0), sna.PCAST_EINVAL),
+    (dict(Nq=4, Nk=3), sna.PCAST_EINVAL),  # more rows than cached keys
     (dict(split_keys=100), sna.PCAST_EINVAL),
     (dict(split_keys=0), sna.PCAST_EINVAL),
     (dict(order=2), sna.PCAST_EINVAL),
     (dict(Hq=3, Hkv=2), sna.PCAST_EINVAL),
     (dict(S=0.0), sna.PCAST_ENOTSUP),
     (dict(Hq=32, Hkv=8, Nq=9), sna.PCAST_ENOTSUP),
-    (dict(Nk=1000), sna.PCAST_ENOTSUP),
     (dict(d=80), sna.PCAST_ENOTSUP),
 ])
 def test_decode_argument_errors(lib, kw, code):
@@ -212,6 +212,7 @@ def test_decode_argument_errors(lib, kw, code):
     (dict(S=0.0), sna.PCAST_ENOTSUP),
     (dict(Hq=32, Hkv=8, Nq=9), sna.PCAST_ENOTSUP),
     (dict(d=80), sna.PCAST_ENOTSUP),
+    (dict(Nk=1000), sna.PCAST_ENOTSUP),  # FP8 logits: whole key blocks (the bf16-logit decode takes any Nk)
 ])
 def test_decode_qk8_argument_errors(lib, kw, code):
     a = dict(Q=FAKE, qk8_workspace=FAKE, bias=0, B=1, Hq=8, Hkv=2, Nq=1, Nk=1024, d=128, S=256.0, order=1,

@@ -107,6 +107,16 @@ def test_rows_and_groups(sna, Hq, Hkv, Nq, order):
           order, 256, 92)
 
 
+@pytest.mark.parametrize("Nk", [1000, 1025, 2050, 65])
+@pytest.mark.parametrize("Hq,Hkv,Nq", [(8, 2, 1), (4, 1, 6)])
+@pytest.mark.parametrize("order", [0, 1])
+def test_ragged_cache(sna, Nk, Hq, Hkv, Nq, order):
+    # a cache length that is not a multiple of 64: the last key block is partial (with Nk = 1025
+    # and 2050 it holds 1 or 2 keys, fewer than the 6 rows of the second shape, so some rows
+    # see no key of it, and the last range of 1024 keys may hold only that block)
+    _case(sna, f"ragged Nk={Nk}", 2, Hq, Hkv, Nq, Nk, 128, synthetic.sink_bias(Nk, 7.0), 256.0, order, 1024, 95)
+
+
 @pytest.mark.parametrize("bias_kind", ["none", "random", "strong"])
 def test_bias_kinds(sna, bias_kind):
     Nk = 768

@@ -27,12 +27,13 @@ def _inputs(B, Hq, Hkv, Nq, Nk, d, seed):
     return q, k, v
 
 
+@pytest.mark.parametrize("Nk", [320, 300, 258])  # 300, 258: a partial last key block (258: 2 keys)
 @pytest.mark.parametrize("S,order,Nq", [(1.0, 0, 1), (256.0, 1, 1), (448.0, 0, 3), (3.0, 1, 4)])
-def test_one_range_is_the_pcast_path(S, order, Nq):
-    B, Hq, Hkv, Nk, d = 2, 4, 2, 320, 64
+def test_one_range_is_the_pcast_path(S, order, Nq, Nk):
+    B, Hq, Hkv, d = 2, 4, 2, 64
     q, k, v = _inputs(B, Hq, Hkv, Nq, Nk, d, 81)
     bias = synthetic.sink_bias(Nk, 7.0)
-    r = decode.rows(q, k, v, bias, S, order, split_keys=Nk)
+    r = decode.rows(q, k, v, bias, S, order, split_keys=-(-Nk // 64) * 64)  # one range
     qf = np.zeros((B, Hq, Nk, d), dtype=np.uint16)
     qf[:, :, Nk - Nq:] = q
     ids = np.array([(b * Hq + h) * Nk + Nk - Nq + i for b in range(B) for h in range(Hq) for i in range(Nq)])
@@ -43,11 +44,12 @@ def test_one_range_is_the_pcast_path(S, order, Nq):
     assert np.array_equal(r["total"].ravel(), c["total"]) and np.array_equal(r["zero"].ravel(), c["zero"])
 
 
+@pytest.mark.parametrize("Nk", [1024, 1000])
 @pytest.mark.parametrize("split", [64, 128, 192, 1024])
 @pytest.mark.parametrize("order", [0, 1])
-def test_nocast_merge_is_exact(split, order):
-    q, k, v = _inputs(1, 2, 1, 2, 1024, 32, 82)
-    bias = synthetic.sink_bias(1024, 5.0)
+def test_nocast_merge_is_exact(split, order, Nk):
+    q, k, v = _inputs(1, 2, 1, 2, Nk, 32, 82)
+    bias = synthetic.sink_bias(Nk, 5.0)
     r = decode.rows(q, k, v, bias, 1.0, order, split, mode="nocast")
     assert np.max(np.abs(r["o2"] - r["o1"])) < 1e-12
 
