@@ -60,8 +60,8 @@ extern "C" {
  * N      sequence length (queries and keys), N >= 1.  For S > 0 any N: when
  *        N % 64 != 0 the last key block is partial and its keys past N are
  *        masked (they take no probability), query rows past N are neither
- *        stored nor counted.  For S = 0 (and for the FP8-logit and backward
- *        entry points below) N % 64 == 0, else PCAST_ENOTSUP.
+ *        stored nor counted.  For S = 0 (and for the FP8-logit entry points
+ *        below) N % 64 == 0, else PCAST_ENOTSUP.
  * d      head size, 64 or 128.
  * causal 0 = every key visible; 1 = key j visible to query i iff j <= i.
  * S      > 0 and finite: P-cast scale (powers of two are exact in fp32; values
@@ -267,11 +267,15 @@ int pcast_collapse_check(const float* bias, int N, double S, int order, double* 
  *          written completely.
  * workspace  device, pcast_bwd_workspace_bytes(B, Hq, Hkv, N, d) bytes, 16-byte
  *          aligned, owned by the caller (per row, fp32 [B][Hq][N] each: -D with the row dot
- *          D = dO . O, then -lse * sqrt(d)).
+ *          D = dO . O, then -lse * sqrt(d)).  Any N >= 1: with N % 64 != 0 the
+ *          workspace also holds copies of Q, K, V, O, dO, lse, the bias and the
+ *          gradients padded to whole 64-key blocks (zero rows; the bias of the
+ *          keys past N is -inf, so they take no probability), the kernels run on
+ *          those, and the gradients of the first N rows are copied out.
  * All products run on bf16 matrix cores with fp32 accumulation; P and dS are
  * rounded to bf16 where they are operands.  Allocates nothing; errors as for
- * attn_fwd_pcast, plus PCAST_ENOTSUP when one head's rows (N * d * 2 bytes)
- * reach 2 GiB.
+ * attn_fwd_pcast, plus PCAST_ENOTSUP when one head's rows (N * d * 2 bytes,
+ * N rounded up to a multiple of 64) reach 2 GiB.
  */
 size_t pcast_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 

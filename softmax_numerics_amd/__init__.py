@@ -462,6 +462,6 @@ def attention(q, k, v, bias=None, causal: bool = True, S: float = 256.0, order="
     the log-sum-exp, no counters); the backward runs attn_bwd_pcast on the saved q, k,
     v, out and log-sum-exp, i.e. the gradients of exact attention taken at the
     forward's output (the cast itself has no gradient), with dO rounded to bf16 and
-    the fp32 gradients rounded to the inputs' bf16 by torch.  The backward needs
-    N % 64 == 0.  The bias gets no gradient."""
+    the fp32 gradients rounded to the inputs' bf16 by torch.  Any N.  The bias gets no
+    gradient."""
     return _attention_function().apply(q, k, v, bias, causal, float(S), order)

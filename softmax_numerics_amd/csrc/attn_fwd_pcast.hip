@@ -1804,6 +1804,12 @@ __global__ __launch_bounds__(256) void pcast_decode_merge(const Params p) {
 // Per row i: -D_i = -(dO_i . O_i), eight lanes per row, and -lse_i * sqrt(d), the
 // log-sum-exp in the units of the raw logits q.k (both start the dK / dV kernel's
 // accumulators, so that the products come out as dP - D and s - lse).
+// Fill n 32-bit words with one value (the padded copies of the backward).
+__global__ __launch_bounds__(256) void pcast_fill_u32(uint32_t* __restrict__ dst, uint32_t value, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) dst[i] = value;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void pcast_bwd_rowdot(const uint16_t* __restrict__ dout, const float* __restrict__ o,
                                                         const float* __restrict__ lse, float* __restrict__ dvec,
@@ -2444,6 +2450,35 @@ BwdLayout bwd_layout(int B, int Hq, int /*Hkv*/, int N, int /*d*/) {
   return l;
 }
 
+// With N not a multiple of 64 the backward runs on copies padded to Np = whole key blocks:
+// Q, K, V, dO (bf16) and O (fp32) with zero rows past N, lse with zeros, a bias of 0
+// (or the caller's) on the first N keys and -inf past them, and the three gradients; the
+// padded rows and keys contribute exactly nothing (their P is 0, or their dO is 0), and
+// the gradients of the first N rows are copied back.  Offsets after the row workspace of
+// Np, 256-aligned each.
+struct BwdPad {
+  int Np;
+  size_t q, k, v, o, dout, lse, bias, dq, dk, dv, total;
+};
+BwdPad bwd_pad_layout(int B, int Hq, int Hkv, int N, int d) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  BwdPad l;
+  l.Np = (N + kKvBlock - 1) / kKvBlock * kKvBlock;
+  const size_t nq = (size_t)B * Hq * l.Np * d, nk = (size_t)B * Hkv * l.Np * d;
+  l.q = up(bwd_layout(B, Hq, Hkv, l.Np, d).total);
+  l.k = up(l.q + nq * 2);
+  l.v = up(l.k + nk * 2);
+  l.o = up(l.v + nk * 2);
+  l.dout = up(l.o + nq * 4);
+  l.lse = up(l.dout + nq * 2);
+  l.bias = up(l.lse + (size_t)B * Hq * l.Np * 4);
+  l.dq = up(l.bias + (size_t)l.Np * 4);
+  l.dk = up(l.dq + nq * 4);
+  l.dv = up(l.dk + nk * 4);
+  l.total = up(l.dv + nk * 4);
+  return l;
+}
+
 // Workspace of the split-KV decode: per (b, kv head, range, packed row) the partial
 // accumulator [D] fp32, then (m, l) fp32, then the two counters u32; 256-aligned parts.
 struct DecodeLayout {
@@ -2499,7 +2534,7 @@ size_t pcast_workspace_bytes(int B, int Hkv, int N, int d, float S) {
 
 size_t pcast_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return 0;
-  return bwd_layout(B, Hq, Hkv, N, d).total;
+  return N % kKvBlock ? bwd_pad_layout(B, Hq, Hkv, N, d).total : bwd_layout(B, Hq, Hkv, N, d).total;
 }
 
 size_t pcast_decode_workspace_bytes(int B, int Hkv, int Nk, int d, int split_keys) {
@@ -2894,27 +2929,16 @@ int attn_fwd_pcast_rows(const void* Q, const void* K, const void* workspace, con
                       static_cast<hipStream_t>(stream), false, lse, lost);
 }
 
-int attn_bwd_pcast(const void* Q, const void* K, const void* V, const float* O, const void* dO,
-                   const float* lse, const float* bias, int B, int Hq, int Hkv, int N, int d, int causal,
-                   float* dQ, float* dK, float* dV, void* workspace, void* stream) {
-  g_last_error[0] = '\0';
-  if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !workspace)
-    return fail(PCAST_EINVAL, "Q, K, V, O, dO, lse, dQ, dK, dV and workspace must be non-null");
-  const void* a16[] = {Q, K, V, O, dO, dQ, dK, dV, workspace};
-  for (const void* ptr : a16)
-    if (!aligned(ptr, 16)) return fail(PCAST_EINVAL, "tensors and workspace must be 16-byte aligned");
-  if (!aligned(lse, 4) || (bias && !aligned(bias, 4))) return fail(PCAST_EINVAL, "lse and bias must be 4-byte aligned");
-  if (causal != 0 && causal != 1) return fail(PCAST_EINVAL, "causal must be 0 or 1");
-  int rc = check_shape(B, Hq, Hkv, N, d, 1.0f);
-  if (rc != PCAST_OK) return rc;
-  if ((int64_t)B * Hkv * ((N + kBlockRows - 1) / kBlockRows) > (int64_t)INT32_MAX) return fail(PCAST_ENOTSUP, "grid too large");
-  if ((int64_t)N * d * 2 > (int64_t)INT32_MAX)
-    return fail(PCAST_ENOTSUP, "N = %d, d = %d: the backward addresses one head's rows with 32-bit byte offsets", N, d);
-  if ((rc = check_device()) != PCAST_OK) return rc;
+}  // extern "C"
 
+namespace {
+
+// The backward's three launches on N rows (N a multiple of 64 here).
+int enqueue_bwd(const void* Q, const void* K, const void* V, const float* O, const void* dO, const float* lse,
+                const float* bias, int B, int Hq, int Hkv, int N, int d, int causal, float* dQ, float* dK, float* dV,
+                void* workspace, hipStream_t st) {
   const BwdLayout l = bwd_layout(B, Hq, Hkv, N, d);
   uint8_t* base = static_cast<uint8_t*>(workspace);
-  hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t rows = (int64_t)B * Hq * N;
   const uint16_t* Qb = static_cast<const uint16_t*>(Q);
   const uint16_t* Kb = static_cast<const uint16_t*>(K);
@@ -2963,6 +2987,75 @@ int attn_bwd_pcast(const void* Q, const void* K, const void* V, const float* O, 
   }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? PCAST_OK : hip_fail(e, "backward launch");
+}
+
+int fill_u32(void* dst, uint32_t value, int64_t n, hipStream_t st) {
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  if (blocks > 0)
+    hipLaunchKernelGGL(pcast_fill_u32, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<uint32_t*>(dst), value, n);
+  return hipGetLastError() == hipSuccess ? PCAST_OK : fail(PCAST_EHIP, "fill launch");
+}
+
+// rows of `width` bytes from a tensor of `rows` x N rows into one of `rows` x Np rows (and back)
+int copy_rows(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width, size_t rows, hipStream_t st) {
+  const hipError_t e = hipMemcpy2DAsync(dst, dpitch, src, spitch, width, rows, hipMemcpyDeviceToDevice, st);
+  return e == hipSuccess ? PCAST_OK : hip_fail(e, "hipMemcpy2DAsync");
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd_pcast(const void* Q, const void* K, const void* V, const float* O, const void* dO,
+                   const float* lse, const float* bias, int B, int Hq, int Hkv, int N, int d, int causal,
+                   float* dQ, float* dK, float* dV, void* workspace, void* stream) {
+  g_last_error[0] = '\0';
+  if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !workspace)
+    return fail(PCAST_EINVAL, "Q, K, V, O, dO, lse, dQ, dK, dV and workspace must be non-null");
+  const void* a16[] = {Q, K, V, O, dO, dQ, dK, dV, workspace};
+  for (const void* ptr : a16)
+    if (!aligned(ptr, 16)) return fail(PCAST_EINVAL, "tensors and workspace must be 16-byte aligned");
+  if (!aligned(lse, 4) || (bias && !aligned(bias, 4))) return fail(PCAST_EINVAL, "lse and bias must be 4-byte aligned");
+  if (causal != 0 && causal != 1) return fail(PCAST_EINVAL, "causal must be 0 or 1");
+  int rc = check_shape(B, Hq, Hkv, N, d, 1.0f, true);
+  if (rc != PCAST_OK) return rc;
+  if ((int64_t)B * Hkv * ((N + kBlockRows - 1) / kBlockRows) > (int64_t)INT32_MAX) return fail(PCAST_ENOTSUP, "grid too large");
+  const int Np = (N + kKvBlock - 1) / kKvBlock * kKvBlock;
+  if ((int64_t)Np * d * 2 > (int64_t)INT32_MAX)
+    return fail(PCAST_ENOTSUP, "N = %d, d = %d: the backward addresses one head's rows with 32-bit byte offsets", N, d);
+  if ((rc = check_device()) != PCAST_OK) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (N % kKvBlock == 0)
+    return enqueue_bwd(Q, K, V, O, dO, lse, bias, B, Hq, Hkv, N, d, causal, dQ, dK, dV, workspace, st);
+  // a partial last key block: run on whole-block copies (pure data movement around the kernels)
+  const BwdPad l = bwd_pad_layout(B, Hq, Hkv, N, d);
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  const size_t rq = (size_t)B * Hq, rk = (size_t)B * Hkv;  // heads
+  // zeros everywhere (bf16 and fp32 zero are both all-zero bits), then the real rows
+  if ((rc = fill_u32(w + l.q, 0u, (int64_t)((l.bias - l.q) / 4), st)) != PCAST_OK) return rc;
+  const size_t rowq = (size_t)N * d, padq = (size_t)Np * d;  // elements per head
+  if ((rc = copy_rows(w + l.q, padq * 2, Q, rowq * 2, rowq * 2, rq, st)) != PCAST_OK) return rc;
+  if ((rc = copy_rows(w + l.k, padq * 2, K, rowq * 2, rowq * 2, rk, st)) != PCAST_OK) return rc;
+  if ((rc = copy_rows(w + l.v, padq * 2, V, rowq * 2, rowq * 2, rk, st)) != PCAST_OK) return rc;
+  if ((rc = copy_rows(w + l.o, padq * 4, O, rowq * 4, rowq * 4, rq, st)) != PCAST_OK) return rc;
+  if ((rc = copy_rows(w + l.dout, padq * 2, dO, rowq * 2, rowq * 2, rq, st)) != PCAST_OK) return rc;
+  if ((rc = copy_rows(w + l.lse, (size_t)Np * 4, lse, (size_t)N * 4, (size_t)N * 4, rq, st)) != PCAST_OK) return rc;
+  // bias: the caller's (or 0) on the first N keys, -inf on the keys past N
+  if ((rc = fill_u32(w + l.bias, 0xFF800000u, Np, st)) != PCAST_OK) return rc;
+  if (bias) {
+    if ((rc = copy_rows(w + l.bias, (size_t)N * 4, bias, (size_t)N * 4, (size_t)N * 4, 1, st)) != PCAST_OK) return rc;
+  } else if ((rc = fill_u32(w + l.bias, 0u, N, st)) != PCAST_OK) {
+    return rc;
+  }
+  rc = enqueue_bwd(w + l.q, w + l.k, w + l.v, reinterpret_cast<const float*>(w + l.o), w + l.dout,
+                   reinterpret_cast<const float*>(w + l.lse), reinterpret_cast<const float*>(w + l.bias), B, Hq, Hkv,
+                   Np, d, causal, reinterpret_cast<float*>(w + l.dq), reinterpret_cast<float*>(w + l.dk),
+                   reinterpret_cast<float*>(w + l.dv), workspace, st);
+  if (rc != PCAST_OK) return rc;
+  if ((rc = copy_rows(dQ, rowq * 4, w + l.dq, padq * 4, rowq * 4, rq, st)) != PCAST_OK) return rc;
+  if ((rc = copy_rows(dK, rowq * 4, w + l.dk, padq * 4, rowq * 4, rk, st)) != PCAST_OK) return rc;
+  return copy_rows(dV, rowq * 4, w + l.dv, padq * 4, rowq * 4, rk, st);
 }
 
 int attn_decode_pcast(const void* Q, const void* K, const void* vop, const float* bias, int B, int Hq,

@@ -226,6 +226,15 @@ def test_bwd_workspace_layout(lib):
     for B, Hq, Hkv, N, d in ((4, 32, 32, 8192, 128), (1, 3, 1, 64, 64)):
         want = 2 * up(4 * B * Hq * N)  # -D and -lse * sqrt(d) per row, fp32
         assert sna.bwd_workspace_bytes(B, Hq, Hkv, N, d) == want
+    # N not a multiple of 64: the row workspace of Np = whole blocks, then the padded copies of
+    # Q, K, V (bf16), O (fp32), dO (bf16), lse, the bias (Np floats) and dQ, dK, dV (fp32)
+    for B, Hq, Hkv, N, d in ((2, 4, 2, 100, 64), (1, 8, 1, 1000, 128)):
+        Np = -(-N // 64) * 64
+        nq, nk = B * Hq * Np * d, B * Hkv * Np * d
+        off = 2 * up(4 * B * Hq * Np)
+        for size in (2 * nq, 2 * nk, 2 * nk, 4 * nq, 2 * nq, 4 * B * Hq * Np, 4 * Np, 4 * nq, 4 * nk, 4 * nk):
+            off = up(off) + size
+        assert sna.bwd_workspace_bytes(B, Hq, Hkv, N, d) == up(off)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -235,9 +244,9 @@ def test_bwd_workspace_layout(lib):
     (dict(dV=0), sna.PCAST_EINVAL),
     (dict(causal=5), sna.PCAST_EINVAL),
     (dict(Hq=3, Hkv=2), sna.PCAST_EINVAL),
-    (dict(N=96), sna.PCAST_ENOTSUP),
     (dict(d=96), sna.PCAST_ENOTSUP),
     (dict(N=1 << 23), sna.PCAST_ENOTSUP),  # one head's rows reach 2 GiB
+    (dict(N=(1 << 23) - 5), sna.PCAST_ENOTSUP),  # the same with the rows padded to whole blocks
 ])
 def test_bwd_argument_errors(lib, kw, code):
     a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, lse=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128,
