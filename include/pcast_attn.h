@@ -60,8 +60,8 @@ extern "C" {
  * N      sequence length (queries and keys), N >= 1.  For S > 0 any N: when
  *        N % 64 != 0 the last key block is partial and its keys past N are
  *        masked (they take no probability), query rows past N are neither
- *        stored nor counted.  For S = 0 (and for the FP8-logit entry points
- *        below) N % 64 == 0, else PCAST_ENOTSUP.
+ *        stored nor counted.  For S = 0 (and for the rotated FP8-logit entry
+ *        points below) N % 64 == 0, else PCAST_ENOTSUP.
  * d      head size, 64 or 128.
  * causal 0 = every key visible; 1 = key j visible to query i iff j <= i.
  * S      > 0 and finite: P-cast scale (powers of two are exact in fp32; values
@@ -302,8 +302,8 @@ int attn_bwd_pcast(const void* Q, const void* K, const void* V, const float* O, 
  *        (the query heads of one kv head and their rows share one 32-column
  *        MFMA tile), else PCAST_ENOTSUP.
  * Nk     any length >= Nq: with Nk % 64 != 0 the last key block is partial
- *        (its keys past Nk do not exist; the V copy is zero-padded).  With
- *        FP8 logits (attn_decode_pcast_qk8) Nk must be a multiple of 64.
+ *        (its keys past Nk do not exist; the V copy and, with FP8 logits, the K
+ *        codes are zero-padded).
  * split_keys  keys per range, a positive multiple of 64 (PCAST_EINVAL
  *        otherwise); the last range may be shorter.  split_keys >= Nk gives
  *        the P-cast path itself.

@@ -64,20 +64,22 @@ def scale_exps(amax) -> np.ndarray:
 
 def quantize_blocks(bits: np.ndarray, rows: int):
     """Quantise a bf16 tensor [B, H, N, d] in blocks of `rows` consecutive rows
-    of one head (N % rows == 0).
+    of one head; a partial last block (N % rows != 0) holds the rows that exist,
+    so its scale is that of their max.
 
-    Returns (bf16 bits of E4M3_RNE(x / 2^e) * 2^e, exponents e [B, H, N / rows]).
+    Returns (bf16 bits of E4M3_RNE(x / 2^e) * 2^e, exponents e [B, H, ceil(N / rows)]).
     """
     x = _bf16_bits_to_f64(bits)
     B, H, N, d = x.shape
-    if N % rows:
-        raise ValueError("N must be a multiple of the block rows")
-    blocks = x.reshape(B, H, N // rows, rows * d)
+    nb = -(-N // rows)
+    xp = np.zeros((B, H, nb * rows, d))  # rows past N are zeros: they leave every block max unchanged
+    xp[:, :, :N] = x
+    blocks = xp.reshape(B, H, nb, rows * d)
     exps = scale_exps(np.max(np.abs(blocks), axis=3))
     e = exps[..., None]
     q = e4m3_rne(np.ldexp(blocks, -e))
     assert q.size == 0 or np.max(np.abs(q)) <= E4M3_MAX
-    out = np.ldexp(q, e).reshape(x.shape)
+    out = np.ldexp(q, e).reshape(xp.shape)[:, :, :N]
     return _f64_to_bf16_bits(out).reshape(np.shape(bits)), exps
 
 
@@ -87,7 +89,7 @@ def quantize_q(bits: np.ndarray):
 
 
 def quantize_k(bits: np.ndarray):
-    """K with one scale per 64-key block: (dequantised bf16 bits, exponents [B, H, N/64])."""
+    """K with one scale per 64-key block: (dequantised bf16 bits, exponents [B, H, ceil(N/64)])."""
     return quantize_blocks(bits, K_BLOCK_ROWS)
 
 

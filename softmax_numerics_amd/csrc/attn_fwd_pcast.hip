@@ -215,21 +215,26 @@ __device__ inline void codes8(const i32x4_t w, int e, int& lo, int& hi) {
 }
 
 // One key block of K per workgroup: the block's exponent e and the codes of
-// K * 2^-e, [B][Hkv][N][D] bytes, plus the V operand copy of the same block.
+// K * 2^-e, [B][Hkv][ceil(N/64)*64][D] bytes (the rows past N of a partial last block
+// are zeros, which leave its max unchanged), plus the V operand copy of the same block.
 template <int D>
 __global__ __launch_bounds__(256) void pcast_prep_kv8(const uint16_t* __restrict__ K,
                                                       const uint16_t* __restrict__ V,
                                                       uint8_t* __restrict__ vop, uint8_t* __restrict__ k8,
-                                                      int* __restrict__ kexp) {
+                                                      int* __restrict__ kexp, int N, int n_tiles) {
   constexpr int kChunks = kKvBlock * D / 8 / 256;  // 16-byte chunks per thread
   const int tid = threadIdx.x;
   const int64_t blk = blockIdx.x;  // flat (b, hkv, key block)
-  const uint16_t* src = K + blk * kKvBlock * D;
+  const int64_t bh = blk / n_tiles;
+  const int t = (int)(blk % n_tiles);
+  const int rows = min(kKvBlock, N - t * kKvBlock);  // keys of this block inside the sequence
+  const uint16_t* src = K + (bh * N + (int64_t)t * kKvBlock) * D;
   i32x4_t w[kChunks];
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < kChunks; ++i) {
-    w[i] = *reinterpret_cast<const i32x4_t*>(src + (i * 256 + tid) * 8);
+    const int e0 = (i * 256 + tid) * 8;  // first element of the chunk in the block
+    w[i] = e0 / D < rows ? *reinterpret_cast<const i32x4_t*>(src + e0) : i32x4_t{0, 0, 0, 0};
     m = max(m, absmax8(w[i]));
   }
 #pragma unroll
@@ -246,8 +251,7 @@ __global__ __launch_bounds__(256) void pcast_prep_kv8(const uint16_t* __restrict
     *reinterpret_cast<int2*>(dst + (i * 256 + tid) * 8) = make_int2(lo, hi);
   }
   if (tid == 0) kexp[blk] = e;
-  // N is a multiple of 64 here: the flat block index addresses V as one block per "head"
-  prep_v_block<D, true>(V, vop, blk, kKvBlock, 1);
+  prep_v_block<D, true>(V, vop, blk, N, n_tiles);
 }
 
 // Rotated FP8 logits: x -> x diag(sigma) H (H the Sylvester matrix of +-1, sigma the
@@ -957,7 +961,8 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_fp8(
     }
   }
 
-  const uint8_t* kbase = kQ8 ? p.k8 + ((int64_t)b * p.Hkv + hk) * p.N * D
+  // FP8 K codes are laid out in whole key blocks per head
+  const uint8_t* kbase = kQ8 ? p.k8 + ((int64_t)b * p.Hkv + hk) * n_tiles * kKTile
                              : reinterpret_cast<const uint8_t*>(p.k + ((int64_t)b * p.Hkv + hk) * p.N * D);
   const uint8_t* vbase = static_cast<const uint8_t*>(p.vop) + ((int64_t)b * p.Hkv + hk) * (int64_t)n_tiles * kVTile;
 
@@ -1547,7 +1552,8 @@ __global__ __launch_bounds__(64) void pcast_decode_split(const Params p) {
       qf[s] = row_ok ? *reinterpret_cast<const bf16x8_t*>(qrow + s * 16) : z;
     }
   }
-  const uint8_t* kbase = kQ8 ? p.k8 + ((int64_t)b * p.Hkv + hk) * p.Nk * D
+  // FP8 K codes are laid out in whole key blocks per head
+  const uint8_t* kbase = kQ8 ? p.k8 + ((int64_t)b * p.Hkv + hk) * n_blk * kKTile
                              : reinterpret_cast<const uint8_t*>(p.k + ((int64_t)b * p.Hkv + hk) * p.Nk * D);
   const int* kexp_head = kQ8 ? p.kexp + ((int64_t)b * p.Hkv + hk) * n_blk : nullptr;
   const uint8_t* vbase = static_cast<const uint8_t*>(p.vop) + ((int64_t)b * p.Hkv + hk) * (int64_t)n_blk * kVTile;
@@ -2506,11 +2512,12 @@ struct Qk8Layout {
 };
 Qk8Layout qk8_layout(int B, int Hkv, int N, int d, int Hq = 0) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t nkv = (size_t)B * Hkv * N * d;
+  const size_t n_tiles = (size_t)(N + kKvBlock - 1) / kKvBlock;
+  const size_t nkv = (size_t)B * Hkv * n_tiles * kKvBlock * d;  // whole key blocks
   Qk8Layout l;
   l.k8 = up(nkv);
   l.kexp = up(l.k8 + nkv);
-  l.total = up(l.kexp + (size_t)B * Hkv * (N / kKvBlock) * 4);
+  l.total = up(l.kexp + (size_t)B * Hkv * n_tiles * 4);
   l.q8 = l.total;
   l.qexp = up(l.q8 + (size_t)B * Hq * N * d);
   l.total_rot = up(l.qexp + (size_t)B * Hq * N * 4);
@@ -2630,14 +2637,17 @@ int enqueue_prep(const void* V, int B, int Hkv, int N, int d, float S, void* ws,
 int enqueue_prep_qk8(const void* K, const void* V, int B, int Hkv, int N, int d, void* ws, hipStream_t st) {
   const Qk8Layout l = qk8_layout(B, Hkv, N, d);
   uint8_t* base = static_cast<uint8_t*>(ws);
-  const int64_t n_blocks = (int64_t)B * Hkv * (N / kKvBlock);
+  const int n_tiles = (N + kKvBlock - 1) / kKvBlock;
+  const int64_t n_blocks = (int64_t)B * Hkv * n_tiles;
   const uint16_t* Kb = static_cast<const uint16_t*>(K);
   const uint16_t* Vb = static_cast<const uint16_t*>(V);
   int* kexp = reinterpret_cast<int*>(base + l.kexp);
   if (d == 64)
-    hipLaunchKernelGGL(pcast_prep_kv8<64>, dim3((unsigned)n_blocks), dim3(256), 0, st, Kb, Vb, base, base + l.k8, kexp);
+    hipLaunchKernelGGL(pcast_prep_kv8<64>, dim3((unsigned)n_blocks), dim3(256), 0, st, Kb, Vb, base, base + l.k8, kexp,
+                       N, n_tiles);
   else
-    hipLaunchKernelGGL(pcast_prep_kv8<128>, dim3((unsigned)n_blocks), dim3(256), 0, st, Kb, Vb, base, base + l.k8, kexp);
+    hipLaunchKernelGGL(pcast_prep_kv8<128>, dim3((unsigned)n_blocks), dim3(256), 0, st, Kb, Vb, base, base + l.k8,
+                       kexp, N, n_tiles);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? PCAST_OK : hip_fail(e, "K/V pre-pass launch");
 }
@@ -3080,7 +3090,7 @@ int attn_decode_pcast_qk8(const void* Q, const void* qk8_workspace, const float*
     return fail(PCAST_EINVAL, "Q, qk8_workspace, out and workspace must be non-null");
   if (!aligned(qk8_workspace, 16))
     return fail(PCAST_EINVAL, "Q, qk8_workspace, out and workspace must be 16-byte aligned");
-  const int rc = check_decode(Q, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out, stats, workspace, false);
+  const int rc = check_decode(Q, bias, B, Hq, Hkv, Nq, Nk, d, S, order, split_keys, out, stats, workspace, true);
   if (rc != PCAST_OK) return rc;
   const Qk8Layout l = qk8_layout(B, Hkv, Nk, d);
   const uint8_t* base = static_cast<const uint8_t*>(qk8_workspace);
@@ -3168,7 +3178,7 @@ int pcast_prepare_qk8(const void* K, const void* V, int B, int Hkv, int N, int d
   if (!K || !V || !workspace) return fail(PCAST_EINVAL, "K, V and workspace must be non-null");
   if (!aligned(K, 16) || !aligned(V, 16) || !aligned(workspace, 16))
     return fail(PCAST_EINVAL, "K, V and workspace must be 16-byte aligned");
-  int rc = check_shape(B, Hkv, Hkv, N, d, 1.0f);
+  int rc = check_shape(B, Hkv, Hkv, N, d, 1.0f, true);
   if (rc != PCAST_OK) return rc;
   if ((rc = check_device()) != PCAST_OK) return rc;
   return enqueue_prep_qk8(K, V, B, Hkv, N, d, workspace, static_cast<hipStream_t>(stream));
@@ -3182,7 +3192,7 @@ int attn_fwd_pcast_qk8_prepared(const void* Q, const void* workspace, const floa
   if (!aligned(workspace, 16)) return fail(PCAST_EINVAL, "workspace must be 16-byte aligned");
   int rc = check_attn_args(Q, workspace, bias, causal, order, out, stats);
   if (rc != PCAST_OK) return rc;
-  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S, true)) != PCAST_OK) return rc;
   if ((rc = check_qk8(S)) != PCAST_OK) return rc;
   if ((rc = check_device()) != PCAST_OK) return rc;
   return enqueue_attn(Q, nullptr, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,
@@ -3197,7 +3207,7 @@ int attn_fwd_pcast_qk8(const void* Q, const void* K, const void* V, const float*
   if (rc != PCAST_OK) return rc;
   if (!V) return fail(PCAST_EINVAL, "V must be non-null");
   if (!aligned(V, 16)) return fail(PCAST_EINVAL, "V must be 16-byte aligned");
-  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S, true)) != PCAST_OK) return rc;
   if ((rc = check_qk8(S)) != PCAST_OK) return rc;
   if ((rc = check_device()) != PCAST_OK) return rc;
 

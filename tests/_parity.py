@@ -111,7 +111,7 @@ def compare_qk8(out_gpu, stats_gpu, qd_bits, kd_bits, vb, bias, causal, S, order
     """
     B, Hq, N, d = qd_bits.shape
     if blocks is None:
-        blocks = [(b, h, r) for b in range(B) for h in range(Hq) for r in range(N // 64)]
+        blocks = [(b, h, r) for b in range(B) for h in range(Hq) for r in range((N + 63) // 64)]
     ids = block_rows(B, Hq, N, blocks)
     delta = 2.0 * np.log(2.0) * qk8_logit_err(qd_bits, kd_bits, ids)
     abs_v = np.asarray(vb, dtype=np.uint16) & np.uint16(0x7FFF)

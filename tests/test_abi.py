@@ -51,7 +51,8 @@ def test_sizes_for_any_sequence_length(lib):
         assert sna.stats_words(2, 5, N) == 2 * 5 * nb * 2
     rc = _call(N=100, S=0.0)
     assert rc == sna.PCAST_ENOTSUP and "bf16 reference path" in sna.strerror(rc)
-    rc = sna.attn_fwd_pcast_qk8(FAKE, FAKE, FAKE, 0, 1, 2, 1, 100, 128, 1, 256.0, 1, FAKE, 0, 0)
+    # the rotated FP8-logit path keeps whole key blocks
+    rc = sna.prepare_qk8_rot(FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 100, 128, FAKE, 0)
     assert rc == sna.PCAST_ENOTSUP and "multiple of 64" in sna.strerror(rc)
 
 
@@ -111,9 +112,10 @@ def test_prepare_argument_errors(lib, kw, code):
 def test_qk8_workspace_layout(lib):
     # V codes, K codes, one int32 exponent per key block, each 256-byte aligned
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    for B, Hkv, N, d in ((4, 32, 8192, 128), (1, 1, 64, 64), (2, 3, 192, 128)):
-        nkv = B * Hkv * N * d
-        assert sna.workspace_bytes_qk8(B, Hkv, N, d) == up(up(up(nkv) + nkv) + 4 * B * Hkv * (N // 64))
+    for B, Hkv, N, d in ((4, 32, 8192, 128), (1, 1, 64, 64), (2, 3, 192, 128), (2, 3, 100, 64)):
+        nb = -(-N // 64)  # whole key blocks: the codes and the V copy of a partial block are padded
+        nkv = B * Hkv * nb * 64 * d
+        assert sna.workspace_bytes_qk8(B, Hkv, N, d) == up(up(up(nkv) + nkv) + 4 * B * Hkv * nb)
     assert sna.workspace_bytes_qk8(0, 1, 64, 64) == 0
 
 
@@ -127,7 +129,6 @@ def test_qk8_workspace_layout(lib):
     (dict(Hq=3, Hkv=2), sna.PCAST_EINVAL),
     (dict(S=0.0), sna.PCAST_ENOTSUP),
     (dict(d=96), sna.PCAST_ENOTSUP),
-    (dict(N=100), sna.PCAST_ENOTSUP),
 ])
 def test_qk8_argument_errors(lib, kw, code):
     a = dict(Q=FAKE, K=FAKE, V=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128, causal=1, S=256.0,
@@ -146,7 +147,6 @@ def test_qk8_argument_errors(lib, kw, code):
     (dict(V=FAKE + 8), sna.PCAST_EINVAL),
     (dict(workspace=0), sna.PCAST_EINVAL),
     (dict(B=0), sna.PCAST_EINVAL),
-    (dict(N=65), sna.PCAST_ENOTSUP),
     (dict(d=32), sna.PCAST_ENOTSUP),
 ])
 def test_prepare_qk8_argument_errors(lib, kw, code):
@@ -212,7 +212,6 @@ def test_decode_argument_errors(lib, kw, code):
     (dict(S=0.0), sna.PCAST_ENOTSUP),
     (dict(Hq=32, Hkv=8, Nq=9), sna.PCAST_ENOTSUP),
     (dict(d=80), sna.PCAST_ENOTSUP),
-    (dict(Nk=1000), sna.PCAST_ENOTSUP),  # FP8 logits: whole key blocks (the bf16-logit decode takes any Nk)
 ])
 def test_decode_qk8_argument_errors(lib, kw, code):
     a = dict(Q=FAKE, qk8_workspace=FAKE, bias=0, B=1, Hq=8, Hkv=2, Nq=1, Nk=1024, d=128, S=256.0, order=1,

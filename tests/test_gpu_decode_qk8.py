@@ -115,6 +115,13 @@ def test_rows_and_groups(sna, Hq, Hkv, Nq):
           1, 256, 192)
 
 
+@pytest.mark.parametrize("Nk", [1000, 1025])
+@pytest.mark.parametrize("order", [0, 1])
+def test_ragged_cache(sna, Nk, order):
+    # a partial last key block: its codes padded with zeros, its scale from the keys that exist
+    _case(sna, f"ragged Nk={Nk}", 2, 4, 1, 6, Nk, 128, synthetic.sink_bias(Nk, 7.0), 256.0, order, 1024, 194)
+
+
 @pytest.mark.parametrize("bias_kind", ["none", "random"])
 def test_bias_kinds(sna, bias_kind):
     bias = None if bias_kind == "none" else synthetic.random_bias(768, 193)

@@ -41,11 +41,14 @@ def _prepare(sna, kb, vb):
     assert rc == sna.PCAST_OK, sna.strerror(rc)
     torch.cuda.synchronize()
     w = ws.cpu().numpy()
-    nkv = B * Hkv * N * d
+    nb = -(-N // 64)  # whole key blocks: a partial last block is padded
+    nkv = B * Hkv * nb * 64 * d
     off_k = _up(nkv)
     off_e = _up(off_k + nkv)
-    return {"k8": w[off_k:off_k + nkv].reshape(kb.shape),
-            "kexp": w[off_e:off_e + 4 * B * Hkv * (N // 64)].view(np.int32).reshape(B, Hkv, N // 64)}
+    k8 = w[off_k:off_k + nkv].reshape(B, Hkv, nb * 64, d)
+    assert not np.any(k8[:, :, N:]), "codes of the padding rows"
+    return {"k8": k8[:, :, :N],
+            "kexp": w[off_e:off_e + 4 * B * Hkv * nb].view(np.int32).reshape(B, Hkv, nb)}
 
 
 def _check_k_prepass(parts, bits):
@@ -53,7 +56,7 @@ def _check_k_prepass(parts, bits):
     _, exps = qk8.quantize_k(bits)
     assert np.array_equal(parts["kexp"], exps), "key block exponents"
     B, H, N, d = bits.shape
-    e = np.repeat(exps, 64, axis=2)[..., None]
+    e = np.repeat(exps, 64, axis=2)[:, :, :N, None]
     want = e4m3.e4m3_encode(np.ldexp(x, -e))
     got = parts["k8"]
     assert not np.any((got & 0x7F) == 0x7F), "NaN code"
@@ -151,6 +154,22 @@ def _case(sna, name, B, Hq, Hkv, N, d, causal, bias, S, order, seed, blocks=None
 def test_small_grid(sna, d, causal, order, S):
     # five key blocks, a half-empty last row block, grouped kv heads, sink bias 7
     _case(sna, "grid", 2, 4, 2, 320, d, causal, synthetic.sink_bias(320, 7.0), S, order, 43)
+
+
+def test_k_prepass_bit_exact_partial_block(sna):
+    # N = 200: the last key block holds 8 keys, its scale from their max (the padding is 0)
+    print("\n[case] qk8 K pre-pass: B=2 Hkv=4 N=200 d=128", flush=True)
+    kb = _scaled_heads(2, 4, 200, 128, 45, 1)
+    vb = synthetic.gaussian_bf16(45, 2, kb.shape)
+    _check_k_prepass(_prepare(sna, kb, vb), kb)
+
+
+@pytest.mark.parametrize("N", [100, 200])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S,order", [(256.0, 1), (1.0, 0)])
+def test_ragged_sequence(sna, N, causal, S, order):
+    _case(sna, f"ragged N={N}", 2, 4, 2, N, 64 if N == 100 else 128, causal, synthetic.sink_bias(N, 7.0), S, order,
+          46 + N)
 
 
 @pytest.mark.parametrize("order", [0, 1])

@@ -105,6 +105,19 @@ def test_blocks_are_independent(rows):
     assert np.array_equal(y1, y0)
 
 
+def test_partial_last_block_is_its_existing_rows():
+    """N = 100: the last 64-key block holds keys 64..99; its scale and values equal those of
+    that block quantised on its own (a plain 36-row block of the same rows), and the full
+    block before it is unchanged by the cut."""
+    k, _, _ = synthetic.qkv_bf16(1, 2, 2, 100, 64, 47)
+    got, e = qk8.quantize_blocks(k, 64)
+    assert e.shape == (1, 2, 2)
+    tail, et = qk8.quantize_blocks(np.ascontiguousarray(k[:, :, 64:]), 36)
+    assert np.array_equal(got[:, :, 64:], tail) and np.array_equal(e[..., 1], et[..., 0])
+    head, eh = qk8.quantize_blocks(np.ascontiguousarray(k[:, :, :64]), 64)
+    assert np.array_equal(got[:, :, :64], head) and np.array_equal(e[..., 0], eh[..., 0])
+
+
 def test_grid_inputs_unchanged():
     """Q, K drawn from the E4M3 grid with max |x| = 448 in every row: quantisation
     is the identity at both granularities."""
