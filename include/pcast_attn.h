@@ -60,8 +60,8 @@ extern "C" {
  * N      sequence length (queries and keys), N >= 1.  For S > 0 any N: when
  *        N % 64 != 0 the last key block is partial and its keys past N are
  *        masked (they take no probability), query rows past N are neither
- *        stored nor counted.  For S = 0 (and for the rotated FP8-logit entry
- *        points below) N % 64 == 0, else PCAST_ENOTSUP.
+ *        stored nor counted.  (The rotated FP8-logit entry points below need
+ *        N % 64 == 0, else PCAST_ENOTSUP.)
  * d      head size, 64 or 128.
  * causal 0 = every key visible; 1 = key j visible to query i iff j <= i.
  * S      > 0 and finite: P-cast scale (powers of two are exact in fp32; values

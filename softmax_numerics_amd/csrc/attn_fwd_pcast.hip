@@ -593,11 +593,13 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params 
   int b, h, rb;
   decode_block(blockIdx.x, n_rb * p.Hq * p.B, n_rb, p.Hq, kCausal, b, h, rb);
   const int hk = h / (p.Hq / p.Hkv);
-  const int n_tiles = p.N / kKvBlock;
+  // key blocks; with N not a multiple of 64 the last one is partial: its keys past N get
+  // a bias of -inf in LDS (probability 0, and not counted, as a sink would not be)
+  const int n_tiles = (p.N + kKvBlock - 1) / kKvBlock, n_full = p.N / kKvBlock;
   const int row0 = rb * kBlockRows;
   const int wrow0 = row0 + wave * kRowsPerWave;  // first row of this wave
   const int myrow = wrow0 + li;
-  const bool wave_active = wrow0 < p.N;
+  const bool wave_active = wrow0 < p.N;  // rows past N (last row block) are computed, never stored
   const int t_last = kCausal ? min((row0 + kBlockRows - 1) / kKvBlock, n_tiles - 1) : n_tiles - 1;
   const int n_it = t_last + 1;
   const float c = p.logit_scale;
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params 
   // Q operand (B of S^T = K Q^T): lane holds Q[myrow][s*16 + g*8 .. +8) for each step s.
   bf16x8_t qf[G::kQSteps];
   if (wave_active) {
-    const uint16_t* qrow = p.q + (((int64_t)b * p.Hq + h) * p.N + myrow) * D + g * 8;
+    const uint16_t* qrow = p.q + (((int64_t)b * p.Hq + h) * p.N + min(myrow, p.N - 1)) * D + g * 8;
 #pragma unroll
     for (int s = 0; s < G::kQSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + s * 16);
   }
@@ -632,15 +634,28 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params 
   };
   auto load_k = [&](int t, int buf) __attribute__((always_inline)) {
     const uint8_t* ks = kbase + t * kKTile;
+    if (t < n_full) {
 #pragma unroll
-    for (int i = 0; i < kKLoads; ++i) load_to_lds16(ks + ksrc[i], kbuf(buf) + (wave * kKLoads + i) * 1024);
+      for (int i = 0; i < kKLoads; ++i) load_to_lds16(ks + ksrc[i], kbuf(buf) + (wave * kKLoads + i) * 1024);
+    } else {
+      // partial last block: rows past N read row N - 1 instead (their bias is -inf)
+      const int last = (p.N - 1 - t * kKvBlock) * kKRow;  // byte offset of row N - 1 in the tile
+#pragma unroll
+      for (int i = 0; i < kKLoads; ++i)
+        load_to_lds16(ks + min(ksrc[i], last + (ksrc[i] & (kKRow - 1))), kbuf(buf) + (wave * kKLoads + i) * 1024);
+    }
   };
   // V of a block and its bias travel together
   auto load_v = [&](int t, int buf) __attribute__((always_inline)) {
     const uint8_t* vs = vbase + t * kVTile;
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) load_to_lds16(vs + vsrc[i], vbuf(buf) + (wave * kVLoads + i) * 1024);
-    if (with_bias && wave == 0) load_to_lds4(p.bias + t * kKvBlock + lane, bbuf(buf));
+    if (t < n_full) {
+      if (with_bias && wave == 0) load_to_lds4(p.bias + t * kKvBlock + lane, bbuf(buf));
+    } else if (wave == 0) {
+      const int key = t * kKvBlock + lane;
+      bbuf(buf)[lane] = key < p.N ? (with_bias ? p.bias[key] : 0.0f) : -INFINITY;
+    }
   };
   auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -726,7 +741,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params 
     if (vis) {
       const int key0 = t * kKvBlock;
       const bool diag = kCausal && (key0 + kKvBlock - 1 > wrow0);
-      const bool has_bias = with_bias && __builtin_amdgcn_ballot_w64(bbuf(cur)[lane] != 0.0f) != 0;
+      const bool has_bias = (with_bias || t >= n_full) && __builtin_amdgcn_ballot_w64(bbuf(cur)[lane] != 0.0f) != 0;
       const float alpha = softmax(sacc, key0, diag, has_bias, cur);
       uint32_t pw[16];
 #pragma unroll
@@ -773,7 +788,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params 
   }
 
   // ---- epilogue: O = A / l (S = 1 on this path) ----
-  if (wave_active) {
+  if (myrow < p.N) {
     const float inv = 1.0f / (p.S * halves_sum(l_run));
     float* orow = p.out + (((int64_t)b * p.Hq + h) * p.N + myrow) * D;
 #pragma unroll
@@ -789,7 +804,8 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params 
       }
   }
   if constexpr (kStats) {
-    const unsigned int a = wave_sum(cnt_tot), z = wave_sum(cnt_zero);
+    const bool counted = myrow < p.N;
+    const unsigned int a = wave_sum(counted ? cnt_tot : 0u), z = wave_sum(counted ? cnt_zero : 0u);
     if (lane == 0 && wave_active) {
       atomicAdd(&lds_cnt[wave / 2][0], a);
       atomicAdd(&lds_cnt[wave / 2][1], z);
@@ -798,7 +814,7 @@ __global__ __launch_bounds__(kThreads, 2) void pcast_attn_fwd_bf16(const Params 
     if (tid < 2) {
       const int r64 = row0 / kKvBlock + tid;  // 64-row block index
       if (r64 * kKvBlock < p.N) {
-        unsigned long long* st = p.stats + 2 * (((int64_t)b * p.Hq + h) * (p.N / kKvBlock) + r64);
+        unsigned long long* st = p.stats + 2 * (((int64_t)b * p.Hq + h) * n_tiles + r64);
         st[0] = lds_cnt[tid][0];
         st[1] = lds_cnt[tid][1];
       }
@@ -2580,17 +2596,16 @@ const char* pcast_strerror(int code) {
 namespace {
 
 // Shape and scalar checks shared by the entry points.  Nothing here touches the device.
-// any_n: the entry point takes any N >= 1 on the P-cast path (S > 0), a partial last
-// key block being masked past N; otherwise N must be a multiple of 64.
+// any_n: the entry point takes any N >= 1, a partial last key block being masked past
+// N; otherwise N must be a multiple of 64.
 int check_shape(int B, int Hq, int Hkv, int N, int d, float S, bool any_n = false) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0)
     return fail(PCAST_EINVAL, "B, Hq, Hkv, N, d must be positive");
   if (Hq % Hkv != 0) return fail(PCAST_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (!std::isfinite(S) || S < 0.0f) return fail(PCAST_EINVAL, "S must be finite and >= 0");
   if (d != 64 && d != 128) return fail(PCAST_ENOTSUP, "d = %d: supported head sizes are 64 and 128", d);
-  if (N % kKvBlock != 0 && !(any_n && S > 0.0f))
-    return fail(PCAST_ENOTSUP, "N = %d: must be a multiple of %d%s", N, kKvBlock,
-                any_n ? " on the bf16 reference path (S = 0)" : " for this entry point");
+  if (N % kKvBlock != 0 && !any_n)
+    return fail(PCAST_ENOTSUP, "N = %d: must be a multiple of %d for this entry point", N, kKvBlock);
   if ((int64_t)B * Hkv * ((N + kKvBlock - 1) / kKvBlock) > (int64_t)INT32_MAX ||
       (int64_t)B * Hq * ((N + kBlockRows - 1) / kBlockRows) > (int64_t)INT32_MAX)
     return fail(PCAST_ENOTSUP, "grid too large");

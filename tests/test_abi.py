@@ -49,8 +49,6 @@ def test_sizes_for_any_sequence_length(lib):
         assert sna.workspace_bytes(2, 3, N, 128, 256.0) == 2 * 3 * nb * 64 * 128
         assert sna.workspace_bytes(2, 3, N, 64, 0.0) == 2 * 2 * 3 * nb * 64 * 64
         assert sna.stats_words(2, 5, N) == 2 * 5 * nb * 2
-    rc = _call(N=100, S=0.0)
-    assert rc == sna.PCAST_ENOTSUP and "bf16 reference path" in sna.strerror(rc)
     # the rotated FP8-logit path keeps whole key blocks
     rc = sna.prepare_qk8_rot(FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 100, 128, FAKE, 0)
     assert rc == sna.PCAST_ENOTSUP and "multiple of 64" in sna.strerror(rc)
@@ -76,7 +74,6 @@ def _call(**kw):
     (dict(Q=FAKE + 8), sna.PCAST_EINVAL),
     (dict(stats=FAKE + 4), sna.PCAST_EINVAL),
     (dict(d=96), sna.PCAST_ENOTSUP),
-    (dict(N=100, S=0.0), sna.PCAST_ENOTSUP),  # any N only on the P-cast path
 ])
 def test_argument_errors(lib, kw, code):
     assert _call(**kw) == code
@@ -88,7 +85,6 @@ def test_argument_errors(lib, kw, code):
     (dict(workspace=FAKE + 4), sna.PCAST_EINVAL),
     (dict(Q=0), sna.PCAST_EINVAL),
     (dict(order=5), sna.PCAST_EINVAL),
-    (dict(N=96, S=0.0), sna.PCAST_ENOTSUP),
 ])
 def test_prepared_argument_errors(lib, kw, code):
     a = dict(Q=FAKE, K=FAKE, workspace=FAKE, bias=0, B=1, Hq=2, Hkv=1, N=128, d=128, causal=1,
