@@ -60,8 +60,7 @@ extern "C" {
  * N      sequence length (queries and keys), N >= 1.  For S > 0 any N: when
  *        N % 64 != 0 the last key block is partial and its keys past N are
  *        masked (they take no probability), query rows past N are neither
- *        stored nor counted.  (The rotated FP8-logit entry points below need
- *        N % 64 == 0, else PCAST_ENOTSUP.)
+ *        stored nor counted.
  * d      head size, 64 or 128.
  * causal 0 = every key visible; 1 = key j visible to query i iff j <= i.
  * S      > 0 and finite: P-cast scale (powers of two are exact in fp32; values
@@ -403,7 +402,9 @@ int attn_decode_pcast_qk8(const void* Q, const void* qk8_workspace, const float*
  * attn_fwd_pcast_qk8.
  *
  * pcast_workspace_bytes_qk8_rot -- bytes of the workspace: that of the
- * unrotated variant plus the codes of Q and one exponent per query row.
+ * unrotated variant plus the codes of Q and one exponent per query row.  Any N:
+ * K's codes take whole 64-key blocks (a zero row for each key past N, so a
+ * partial block's exponent is that of the keys that exist), Q's take N rows.
  * pcast_prepare_qk8_rot -- enqueue the V copy and the rotation pre-passes of K
  * and Q.  signs: device, int8 [d], 16-byte aligned, the signs sigma (a negative
  * entry is -1, any other +1; the caller draws them).  Other arguments as for

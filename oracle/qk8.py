@@ -121,19 +121,23 @@ def rotate(bits: np.ndarray, signs) -> np.ndarray:
 
 
 def quantize_values(x: np.ndarray, rows: int):
-    """quantize_blocks on fp64 values [B, H, N, d]: (E4M3_RNE(x / 2^e) * 2^e, e)."""
+    """quantize_blocks on fp64 values [B, H, N, d]: (E4M3_RNE(x / 2^e) * 2^e, e); a
+    partial last block holds the rows that exist."""
     B, H, N, d = x.shape
-    blocks = x.reshape(B, H, N // rows, rows * d)
+    nb = -(-N // rows)
+    xp = np.zeros((B, H, nb * rows, d))  # rows past N are zeros: they leave every block max unchanged
+    xp[:, :, :N] = x
+    blocks = xp.reshape(B, H, nb, rows * d)
     exps = scale_exps(np.max(np.abs(blocks), axis=3))
     q = e4m3_rne(np.ldexp(blocks, -exps[..., None]))
     assert q.size == 0 or np.max(np.abs(q)) <= E4M3_MAX
-    return np.ldexp(q, exps[..., None]).reshape(x.shape), exps
+    return np.ldexp(q, exps[..., None]).reshape(xp.shape)[:, :, :N], exps
 
 
 def quantize_rotated(q_bits: np.ndarray, k_bits: np.ndarray, signs):
     """Rotated, then quantised Q (per row) and K (per 64-key block), as bf16 bits whose
     plain dot products are those of the original logits' inputs: Q~ and K~ / d.
-    Returns (q bits, k bits, q exps [B, H, N], k exps [B, Hkv, N/64])."""
+    Returns (q bits, k bits, q exps [B, H, N], k exps [B, Hkv, ceil(N/64)])."""
     d = np.shape(q_bits)[-1]
     qv, eq = quantize_values(rotate(q_bits, signs), Q_BLOCK_ROWS)
     kv, ek = quantize_values(rotate(k_bits, signs), K_BLOCK_ROWS)

@@ -280,20 +280,28 @@ __device__ inline int scale_exp_f64(double amax) {
 template <int D, bool kPerRow>
 __global__ __launch_bounds__(256) void pcast_prep_rot8(const uint16_t* __restrict__ x,
                                                        const signed char* __restrict__ signs,
-                                                       uint8_t* __restrict__ codes, int* __restrict__ exps) {
+                                                       uint8_t* __restrict__ codes, int* __restrict__ exps, int N,
+                                                       int n_tiles) {
   // four lanes per row, each with V contiguous values: the transform's stages of
   // stride below V run in registers, the strides V and 2V across lanes (xor 1, 2)
   constexpr int V = D / 4;
   const int tid = threadIdx.x;
   const int r = tid / 4, part = tid % 4;
-  const int64_t row = (int64_t)blockIdx.x * kKvBlock + r;  // 64 rows per workgroup
+  // 64 rows of one head per workgroup; in a partial last block the rows past N are zeros
+  // (they leave the block max unchanged): K codes are written for them (K's codes take
+  // whole blocks per head), Q codes and exponents are not (Q keeps N rows per head)
+  const int64_t bh = blockIdx.x / n_tiles;
+  const int t = (int)(blockIdx.x % n_tiles);
+  const bool exists = t * kKvBlock + r < N;
+  const int64_t row = bh * N + (int64_t)t * kKvBlock + min(r, N - 1 - t * kKvBlock);  // source row
+  const int64_t orow = kPerRow ? row : (int64_t)blockIdx.x * kKvBlock + r;          // code row
   const uint16_t* src = x + row * D + part * V;
   // the lane's V signs (16-byte aligned, V a multiple of 16) and values, all loads first
   i32x4_t sw[V / 16], xw[V / 8];
 #pragma unroll
   for (int k = 0; k < V / 16; ++k) sw[k] = *reinterpret_cast<const i32x4_t*>(signs + part * V + k * 16);
 #pragma unroll
-  for (int k = 0; k < V / 8; ++k) xw[k] = *reinterpret_cast<const i32x4_t*>(src + k * 8);
+  for (int k = 0; k < V / 8; ++k) xw[k] = exists ? *reinterpret_cast<const i32x4_t*>(src + k * 8) : i32x4_t{0, 0, 0, 0};
   double v[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) {
@@ -330,7 +338,7 @@ __global__ __launch_bounds__(256) void pcast_prep_rot8(const uint16_t* __restric
   int e;
   if constexpr (kPerRow) {
     e = scale_exp_f64(mx);
-    if (part == 0) exps[row] = e;
+    if (part == 0 && exists) exps[row] = e;
   } else {
     // the block's exponent from the max over its 64 rows
     __shared__ double rmax[kKvBlock];
@@ -341,7 +349,8 @@ __global__ __launch_bounds__(256) void pcast_prep_rot8(const uint16_t* __restric
     e = scale_exp_f64(bm);
     if (tid == 0) exps[blockIdx.x] = e;
   }
-  uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * D + part * V);
+  if (kPerRow && !exists) return;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(codes + orow * D + part * V);
 #pragma unroll
   for (int k = 0; k < V / 4; ++k) {
     float f[4];
@@ -3149,7 +3158,7 @@ int pcast_prepare_qk8_rot(const void* Q, const void* K, const void* V, const sig
   if (!Q || !K || !V || !signs || !workspace) return fail(PCAST_EINVAL, "Q, K, V, signs and workspace must be non-null");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(signs, 16) || !aligned(workspace, 16))
     return fail(PCAST_EINVAL, "Q, K, V, signs and workspace must be 16-byte aligned");
-  int rc = check_shape(B, Hq, Hkv, N, d, 1.0f);
+  int rc = check_shape(B, Hq, Hkv, N, d, 1.0f, true);
   if (rc != PCAST_OK) return rc;
   if ((rc = check_device()) != PCAST_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -3157,16 +3166,21 @@ int pcast_prepare_qk8_rot(const void* Q, const void* K, const void* V, const sig
   uint8_t* base = static_cast<uint8_t*>(workspace);
   const uint16_t* Qb = static_cast<const uint16_t*>(Q);
   const uint16_t* Kb = static_cast<const uint16_t*>(K);
-  const int64_t qblk = (int64_t)B * Hq * (N / kKvBlock), kblk = (int64_t)B * Hkv * (N / kKvBlock);
+  const int n_tiles = (N + kKvBlock - 1) / kKvBlock;
+  const int64_t qblk = (int64_t)B * Hq * n_tiles, kblk = (int64_t)B * Hkv * n_tiles;
   if ((rc = enqueue_prep(V, B, Hkv, N, d, 1.0f, workspace, st)) != PCAST_OK) return rc;
   int* kexp = reinterpret_cast<int*>(base + l.kexp);
   int* qexp = reinterpret_cast<int*>(base + l.qexp);
   if (d == 64) {
-    hipLaunchKernelGGL((pcast_prep_rot8<64, false>), dim3((unsigned)kblk), dim3(256), 0, st, Kb, signs, base + l.k8, kexp);
-    hipLaunchKernelGGL((pcast_prep_rot8<64, true>), dim3((unsigned)qblk), dim3(256), 0, st, Qb, signs, base + l.q8, qexp);
+    hipLaunchKernelGGL((pcast_prep_rot8<64, false>), dim3((unsigned)kblk), dim3(256), 0, st, Kb, signs, base + l.k8, kexp,
+                       N, n_tiles);
+    hipLaunchKernelGGL((pcast_prep_rot8<64, true>), dim3((unsigned)qblk), dim3(256), 0, st, Qb, signs, base + l.q8, qexp,
+                       N, n_tiles);
   } else {
-    hipLaunchKernelGGL((pcast_prep_rot8<128, false>), dim3((unsigned)kblk), dim3(256), 0, st, Kb, signs, base + l.k8, kexp);
-    hipLaunchKernelGGL((pcast_prep_rot8<128, true>), dim3((unsigned)qblk), dim3(256), 0, st, Qb, signs, base + l.q8, qexp);
+    hipLaunchKernelGGL((pcast_prep_rot8<128, false>), dim3((unsigned)kblk), dim3(256), 0, st, Kb, signs, base + l.k8, kexp,
+                       N, n_tiles);
+    hipLaunchKernelGGL((pcast_prep_rot8<128, true>), dim3((unsigned)qblk), dim3(256), 0, st, Qb, signs, base + l.q8, qexp,
+                       N, n_tiles);
   }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? PCAST_OK : hip_fail(e, "rotation pre-pass launch");
@@ -3180,7 +3194,7 @@ int attn_fwd_pcast_qk8_rot_prepared(const void* workspace, const float* bias, in
   if (!aligned(workspace, 16)) return fail(PCAST_EINVAL, "workspace must be 16-byte aligned");
   int rc = check_attn_args(workspace, workspace, bias, causal, order, out, stats);
   if (rc != PCAST_OK) return rc;
-  if ((rc = check_shape(B, Hq, Hkv, N, d, S)) != PCAST_OK) return rc;
+  if ((rc = check_shape(B, Hq, Hkv, N, d, S, true)) != PCAST_OK) return rc;
   if ((rc = check_qk8(S)) != PCAST_OK) return rc;
   if ((rc = check_device()) != PCAST_OK) return rc;
   return enqueue_attn(nullptr, nullptr, workspace, bias, B, Hq, Hkv, N, d, causal, S, order, out, stats,

@@ -42,16 +42,17 @@ def test_version_and_sizes(lib):
 
 
 def test_sizes_for_any_sequence_length(lib):
-    # the V copy and the counters take whole 64-key blocks; the bf16 path and the
-    # FP8-logit path keep N a multiple of 64
+    # the V copy and the counters take whole 64-key blocks
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     for N in (1, 63, 65, 100, 4097):
         nb = (N + 63) // 64
         assert sna.workspace_bytes(2, 3, N, 128, 256.0) == 2 * 3 * nb * 64 * 128
         assert sna.workspace_bytes(2, 3, N, 64, 0.0) == 2 * 2 * 3 * nb * 64 * 64
         assert sna.stats_words(2, 5, N) == 2 * 5 * nb * 2
-    # the rotated FP8-logit path keeps whole key blocks
-    rc = sna.prepare_qk8_rot(FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 100, 128, FAKE, 0)
-    assert rc == sna.PCAST_ENOTSUP and "multiple of 64" in sna.strerror(rc)
+        # rotated FP8 logits: K codes in whole blocks, Q codes and exponents per row
+        nkv, nq = 2 * 3 * nb * 64 * 128, 2 * 6 * N * 128
+        base = up(up(up(nkv) + nkv) + 4 * 2 * 3 * nb)
+        assert sna.workspace_bytes_qk8_rot(2, 6, 3, N, 128) == up(up(base + nq) + 4 * 2 * 6 * N)
 
 
 def _call(**kw):

@@ -289,30 +289,33 @@ def _rot_run(sna, qb, kb, vb, bias, causal, S, order, signs):
     return out.cpu().numpy(), st.cpu().numpy().reshape(B, Hq, -1, 2)
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_rotation_prepass_bit_exact(sna, d):
-    print(f"\n[case] qk8 rotation pre-pass d={d}", flush=True)
-    B, Hq, Hkv, N = 2, 4, 2, 192
+@pytest.mark.parametrize("d,N", [(64, 192), (128, 192), (128, 200), (64, 37)])
+def test_rotation_prepass_bit_exact(sna, d, N):
+    print(f"\n[case] qk8 rotation pre-pass d={d} N={N}", flush=True)
+    B, Hq, Hkv = 2, 4, 2
+    nb = -(-N // 64)
     qb = _scaled_heads(B, Hq, N, d, 51, 0)
     kb = _scaled_heads(B, Hkv, N, d, 51, 1)
     vb = synthetic.gaussian_bf16(51, 2, kb.shape)
     signs = _signs(d, 51)
     w = _prepare_rot(sna, qb, kb, vb, signs).cpu().numpy()
-    nkv, nq = B * Hkv * N * d, B * Hq * N * d
+    nkv, nq = B * Hkv * nb * 64 * d, B * Hq * N * d  # K codes in whole key blocks, Q codes per row
     off_k = _up(nkv)
     off_ke = _up(off_k + nkv)
-    off_q = _up(off_ke + 4 * B * Hkv * (N // 64))
+    off_q = _up(off_ke + 4 * B * Hkv * nb)
     off_qe = _up(off_q + nq)
-    k8 = w[off_k:off_k + nkv].reshape(kb.shape)
-    ke = w[off_ke:off_ke + 4 * B * Hkv * (N // 64)].view(np.int32).reshape(B, Hkv, N // 64)
+    k8 = w[off_k:off_k + nkv].reshape(B, Hkv, nb * 64, d)
+    ke = w[off_ke:off_ke + 4 * B * Hkv * nb].view(np.int32).reshape(B, Hkv, nb)
     q8 = w[off_q:off_q + nq].reshape(qb.shape)
     qe = w[off_qe:off_qe + 4 * B * Hq * N].view(np.int32).reshape(B, Hq, N)
+    # rows past the sequence are zeros (of either sign: a sign flip makes -0, code 0x80)
+    assert not e4m3.DECODE_TABLE[k8[:, :, N:]].any(), "K rows past the sequence"
     sg = signs.astype(np.float64)
-    for codes, exps, bits, rows in ((q8, qe, qb, 1), (k8, ke, kb, 64)):
+    for codes, exps, bits, rows in ((q8, qe, qb, 1), (k8[:, :, :N], ke, kb, 64)):
         x = qk8.rotate(bits, sg)
         _, want_e = qk8.quantize_values(x, rows)
         assert np.array_equal(exps, want_e), "exponents"
-        e = np.repeat(want_e, rows, axis=2)[..., None]
+        e = np.repeat(want_e, rows, axis=2)[:, :, :N, None]
         want = e4m3.e4m3_encode(np.ldexp(x, -e))
         assert np.array_equal(e4m3.DECODE_TABLE[codes], e4m3.DECODE_TABLE[want]), "codes"
 
@@ -329,6 +332,21 @@ def test_rotation_parity(sna, d, causal, S, order):
     qd, kd, _, _ = qk8.quantize_rotated(qb, kb, signs.astype(np.float64))
     rep = _parity.compare_qk8(out, st, qd, kd, vb, bias, causal, S, order)
     print(f"[case] qk8 rotation parity: {rep}", flush=True)
+
+
+@pytest.mark.parametrize("N", [100, 200])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S,order", [(256.0, 1), (1.0, 0)])
+def test_rotation_parity_ragged(sna, N, causal, S, order):
+    d = 64 if N == 100 else 128
+    print(f"\n[case] qk8 rotation parity ragged N={N} d={d} causal={causal} S={S} order={order}", flush=True)
+    qb, kb, vb = synthetic.qkv_bf16(2, 4, 2, N, d, 54)
+    bias = synthetic.sink_bias(N, 7.0)
+    signs = _signs(d, 54)
+    out, st = _rot_run(sna, qb, kb, vb, bias, causal, S, order, signs)
+    qd, kd, _, _ = qk8.quantize_rotated(qb, kb, signs.astype(np.float64))
+    rep = _parity.compare_qk8(out, st, qd, kd, vb, bias, causal, S, order)
+    print(f"[case] qk8 rotation parity ragged: {rep}", flush=True)
 
 
 def _outlier_inputs(B, Hq, Hkv, N, d, seed, mult):

@@ -118,6 +118,18 @@ def test_partial_last_block_is_its_existing_rows():
     assert np.array_equal(got[:, :, :64], head) and np.array_equal(e[..., 0], eh[..., 0])
 
 
+def test_rotated_values_partial_last_block():
+    """quantize_values (the rotated path's quantiser) on N = 100 rows: the partial block equals
+    its 36 rows quantised on their own, the full block is unchanged by the cut."""
+    q, _, _ = synthetic.qkv_bf16(1, 2, 2, 100, 64, 48)
+    x = qk8.rotate(q, np.where(np.arange(64) % 3 == 0, -1.0, 1.0))
+    got, e = qk8.quantize_values(x, 64)
+    tail, et = qk8.quantize_values(np.ascontiguousarray(x[:, :, 64:]), 36)
+    head, eh = qk8.quantize_values(np.ascontiguousarray(x[:, :, :64]), 64)
+    assert np.array_equal(got[:, :, 64:], tail) and np.array_equal(e[..., 1], et[..., 0])
+    assert np.array_equal(got[:, :, :64], head) and np.array_equal(e[..., 0], eh[..., 0])
+
+
 def test_grid_inputs_unchanged():
     """Q, K drawn from the E4M3 grid with max |x| = 448 in every row: quantisation
     is the identity at both granularities."""
