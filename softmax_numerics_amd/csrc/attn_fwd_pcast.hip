@@ -262,8 +262,8 @@ __global__ __launch_bounds__(256) void pcast_prep_kv8(const uint16_t* __restrict
 // that no intermediate fp32 rounding can move a value onto a midpoint; the result is
 // on the grid, which the fp32 conversion then encodes exactly.
 __device__ inline double e4m3_rne_f64(double y) {
+  // no branch for zero: it falls on the subnormal grid and keeps its sign
   const double a = fabs(y);
-  if (a == 0.0) return y;
   int E;
   frexp(a, &E);                                   // a in [2^(E-1), 2^E)
   const int step = a < 0x1.0p-6 ? -9 : (E - 1) - 3;  // grid step 2^step (subnormal below 2^-6)
@@ -275,6 +275,21 @@ __device__ inline int scale_exp_f64(double amax) {
   int E;
   const double m = frexp(amax, &E);
   return m <= 0.875 ? E - 9 : E - 8;
+}
+
+// x from the lane whose index differs in bit m (m = 1 or 2) within its quad of four lanes,
+// by two DPP quad permutations of the halves (every lane of the quad is active)
+__device__ inline double quad_xor_f64(double x, int m) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+  if (m == 1) {  // quad_perm [1, 0, 3, 2]
+    lo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, true);
+    hi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, true);
+  } else {  // quad_perm [2, 3, 0, 1]
+    lo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, true);
+    hi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, true);
+  }
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
 template <int D, bool kPerRow>
@@ -321,20 +336,21 @@ __global__ __launch_bounds__(256) void pcast_prep_rot8(const uint16_t* __restric
         v[i + h] = a - c;
       }
   // cross-lane stages: the lower partner keeps the sum, the upper the difference
+  // (o - v as o + (-v), the same rounding); the partner's value comes by a quad DPP move
 #pragma unroll
   for (int m = 1; m <= 2; m *= 2) {
-    const bool upper = (part & m) != 0;
+    const uint64_t flip = (part & m) != 0 ? 1ull << 63 : 0ull;  // the upper partner negates its own
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      const double o = __shfl_xor(v[i], m);
-      v[i] = upper ? o - v[i] : v[i] + o;
+      const double o = quad_xor_f64(v[i], m);
+      v[i] = __builtin_bit_cast(double, __builtin_bit_cast(uint64_t, v[i]) ^ flip) + o;
     }
   }
   double mx = 0.0;
 #pragma unroll
   for (int i = 0; i < V; ++i) mx = fmax(mx, fabs(v[i]));
-  mx = fmax(mx, __shfl_xor(mx, 1));
-  mx = fmax(mx, __shfl_xor(mx, 2));
+  mx = fmax(mx, quad_xor_f64(mx, 1));
+  mx = fmax(mx, quad_xor_f64(mx, 2));
   int e;
   if constexpr (kPerRow) {
     e = scale_exp_f64(mx);
@@ -350,15 +366,20 @@ __global__ __launch_bounds__(256) void pcast_prep_rot8(const uint16_t* __restric
     if (tid == 0) exps[blockIdx.x] = e;
   }
   if (kPerRow && !exists) return;
-  uint32_t* dst = reinterpret_cast<uint32_t*>(codes + orow * D + part * V);
+  // the lane's V codes (16-byte aligned: the code buffer is, and D and V are multiples of 16)
+  i32x4_t* dst = reinterpret_cast<i32x4_t*>(codes + orow * D + part * V);
 #pragma unroll
-  for (int k = 0; k < V / 4; ++k) {
-    float f[4];
+  for (int c = 0; c < V / 16; ++c) {
+    i32x4_t w;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) f[t] = (float)e4m3_rne_f64(ldexp(v[4 * k + t], -e));
-    int word = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-    word = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], word, true);
-    dst[k] = (uint32_t)word;
+    for (int k = 0; k < 4; ++k) {
+      float f[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) f[t] = (float)e4m3_rne_f64(ldexp(v[16 * c + 4 * k + t], -e));
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      w[k] = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], word, true);
+    }
+    dst[c] = w;
   }
 }
 
