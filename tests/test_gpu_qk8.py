@@ -76,7 +76,7 @@ def _scaled_heads(B, H, N, d, seed, tensor_id):
         x[4, :, 5] *= 200.0                    # one outlier channel
     if B * H > 6:
         x[6] = np.clip(x[6], -3.0, 3.0)
-        x[6, 3, 7] = 448.0 * 2.0 ** -7       # amax exactly 448 * 2^-7 (= 3.5)
+        x[6, min(3, N - 1), 7] = 448.0 * 2.0 ** -7  # amax exactly 448 * 2^-7 (= 3.5)
     u = x.reshape(B, H, N, d).view(np.uint32).astype(np.uint64)
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)   # back to bf16, RNE
 
@@ -289,7 +289,7 @@ def _rot_run(sna, qb, kb, vb, bias, causal, S, order, signs):
     return out.cpu().numpy(), st.cpu().numpy().reshape(B, Hq, -1, 2)
 
 
-@pytest.mark.parametrize("d,N", [(64, 192), (128, 192), (128, 200), (64, 37)])
+@pytest.mark.parametrize("d,N", [(64, 192), (128, 192), (128, 200), (64, 37), (128, 1)])
 def test_rotation_prepass_bit_exact(sna, d, N):
     print(f"\n[case] qk8 rotation pre-pass d={d} N={N}", flush=True)
     B, Hq, Hkv = 2, 4, 2
@@ -334,7 +334,7 @@ def test_rotation_parity(sna, d, causal, S, order):
     print(f"[case] qk8 rotation parity: {rep}", flush=True)
 
 
-@pytest.mark.parametrize("N", [100, 200])
+@pytest.mark.parametrize("N", [1, 100, 200])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("S,order", [(256.0, 1), (1.0, 0)])
 def test_rotation_parity_ragged(sna, N, causal, S, order):
